@@ -1,0 +1,213 @@
+// C ABI of libhsla: argument validation, workspace sizing and launch order.
+// The operations and their definitions are documented in include/hsla.h.
+#include <math.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "hsla.h"
+#include "internal.h"
+
+namespace {
+
+using hsla::Problem;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Validates the configuration and resolves the problem description.
+hsla_status resolve(const hsla_config* cfg, int32_t batch, int32_t max_seq_len,
+                    int32_t max_blocks, Problem* out) {
+  if (!cfg) return HSLA_ERR_INVALID_ARG;
+  if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 || cfg->num_q_heads % cfg->num_kv_heads != 0)
+    return HSLA_ERR_INVALID_ARG;
+  if (cfg->top_k < 0 || cfg->num_sink < 0 || cfg->window < 1) return HSLA_ERR_INVALID_ARG;
+  if (cfg->linear_tail != 0 && cfg->linear_tail != 1) return HSLA_ERR_INVALID_ARG;
+  if (!(cfg->scale >= 0.0f) || !isfinite(cfg->scale)) return HSLA_ERR_INVALID_ARG;
+  if (batch < 1 || max_seq_len < 1) return HSLA_ERR_INVALID_ARG;
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return HSLA_ERR_UNSUPPORTED;
+  if (cfg->head_dim != 64 && cfg->head_dim != 128) return HSLA_ERR_UNSUPPORTED;
+  const int B = cfg->block_size;
+  if (B != 16 && B != 32 && B != 64 && B != 128 && B != 256) return HSLA_ERR_UNSUPPORTED;
+  if (cfg->kv_dtype != HSLA_F32 && cfg->kv_dtype != HSLA_BF16) return HSLA_ERR_UNSUPPORTED;
+  if (cfg->window < B) return HSLA_ERR_INVALID_ARG;  // candidates must be full blocks
+  const long nblk = (static_cast<long>(max_seq_len) + B - 1) / B;
+  if (nblk >= (1L << 20)) return HSLA_ERR_UNSUPPORTED;  // block index field of the union list
+  if (max_blocks >= 0 && max_blocks < nblk) return HSLA_ERR_INVALID_ARG;
+  Problem p{};
+  p.Hq = cfg->num_q_heads;
+  p.Hkv = cfg->num_kv_heads;
+  p.G = G;
+  p.D = cfg->head_dim;
+  p.B = B;
+  p.top_k = cfg->top_k;
+  p.ns = cfg->num_sink;
+  p.W = cfg->window;
+  p.linear_tail = cfg->linear_tail;
+  p.bf16 = cfg->kv_dtype == HSLA_BF16;
+  p.sigma = cfg->scale > 0.0f ? cfg->scale : 1.0f / sqrtf(static_cast<float>(cfg->head_dim));
+  p.batch = batch;
+  p.max_seq_len = max_seq_len;
+  p.max_blocks = max_blocks;
+  p.nblk_max = static_cast<int>(nblk);
+  p.nc_max = hsla::candidate_range(max_seq_len, B, p.ns, p.W).count;
+  // Per-head selection bitmaps of the select kernel live in LDS.
+  const size_t bitmap = static_cast<size_t>(G) * ((p.nc_max + 63) / 64) * 8;
+  if (bitmap > 64 * 1024) return HSLA_ERR_UNSUPPORTED;
+  *out = p;
+  return HSLA_OK;
+}
+
+hsla_status check_pool(const hsla_kv_pool* pool, bool need_stats) {
+  if (!pool || !pool->k_pages || !pool->v_pages || !pool->block_table) return HSLA_ERR_INVALID_ARG;
+  if (need_stats && (!pool->blk_mean || !pool->blk_var)) return HSLA_ERR_INVALID_ARG;
+  if (pool->num_pages < 1 || pool->max_blocks_per_seq < 1) return HSLA_ERR_INVALID_ARG;
+  if (!aligned(pool->k_pages, 16) || !aligned(pool->v_pages, 16) || !aligned(pool->block_table, 4))
+    return HSLA_ERR_INVALID_ARG;
+  if (need_stats && (!aligned(pool->blk_mean, 16) || !aligned(pool->blk_var, 16))) return HSLA_ERR_INVALID_ARG;
+  return HSLA_OK;
+}
+
+hsla_status check_state(const hsla_state* st) {
+  if (!st || !st->S || !st->z || !st->sv) return HSLA_ERR_INVALID_ARG;
+  if (!aligned(st->S, 16) || !aligned(st->z, 16) || !aligned(st->sv, 16)) return HSLA_ERR_INVALID_ARG;
+  return HSLA_OK;
+}
+
+struct ProfileCtx {
+  hsla_profile* prof;
+  hipStream_t stream;
+  bool failed;
+};
+
+void record_event(void* ctx, int idx, const char* name) {
+  ProfileCtx* c = static_cast<ProfileCtx*>(ctx);
+  if (!c->prof || idx >= c->prof->capacity || idx >= HSLA_MAX_PROFILE_EVENTS) return;
+  if (hipEventRecord(c->prof->events[idx], c->stream) != hipSuccess) c->failed = true;
+  c->prof->names[idx] = name;
+  c->prof->recorded = idx + 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hsla_status_string(hsla_status s) {
+  switch (s) {
+    case HSLA_OK: return "HSLA_OK: success";
+    case HSLA_ERR_INVALID_ARG: return "HSLA_ERR_INVALID_ARG: null, misaligned or out-of-range argument";
+    case HSLA_ERR_UNSUPPORTED: return "HSLA_ERR_UNSUPPORTED: head_dim, GQA group, block size, dtype or size not built";
+    case HSLA_ERR_WORKSPACE: return "HSLA_ERR_WORKSPACE: workspace missing or too small";
+    case HSLA_ERR_HIP: return "HSLA_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown hsla_status";
+}
+
+const char* hsla_version(void) { return "hsla 0.1.0 gfx950"; }
+
+size_t hsla_build_workspace_size(const hsla_config* cfg, int32_t batch, int32_t max_seq_len) {
+  Problem p;
+  if (resolve(cfg, batch, max_seq_len, -1, &p) != HSLA_OK) return 0;
+  return hsla::build_layout(p).total;
+}
+
+hsla_status hsla_build_state(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
+                             const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  Problem p;
+  hsla_status st = resolve(cfg, batch, max_seq_len, pool ? pool->max_blocks_per_seq : 0, &p);
+  if (st != HSLA_OK) return st;
+  if ((st = check_pool(pool, true)) != HSLA_OK) return st;
+  if ((st = check_state(state)) != HSLA_OK) return st;
+  if (!seq_lens || !aligned(seq_lens, 4)) return HSLA_ERR_INVALID_ARG;
+  const hsla::BuildLayout L = hsla::build_layout(p);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, 16)) return HSLA_ERR_WORKSPACE;
+  hsla::BuildArgs a{};
+  a.k_pages = pool->k_pages;
+  a.v_pages = pool->v_pages;
+  a.blk_mean = pool->blk_mean;
+  a.blk_var = pool->blk_var;
+  a.block_table = pool->block_table;
+  a.S = state->S;
+  a.z = state->z;
+  a.sv = state->sv;
+  a.seq_lens = seq_lens;
+  a.ws = static_cast<float*>(workspace);
+  (void)hipGetLastError();  // a stale error from another runtime user is not ours
+  return hsla::launch_build(p, L, a, stream) == hipSuccess ? HSLA_OK : HSLA_ERR_HIP;
+}
+
+hsla_status hsla_append_token(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
+                              const void* k_new, const void* v_new, const int32_t* seq_lens_before,
+                              int32_t* seq_lens_after, int32_t batch, int32_t max_seq_len,
+                              hipStream_t stream) {
+  Problem p;
+  hsla_status st = resolve(cfg, batch, max_seq_len, pool ? pool->max_blocks_per_seq : 0, &p);
+  if (st != HSLA_OK) return st;
+  if ((st = check_pool(pool, true)) != HSLA_OK) return st;
+  if ((st = check_state(state)) != HSLA_OK) return st;
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return HSLA_ERR_INVALID_ARG;
+  if (!seq_lens_before || !aligned(seq_lens_before, 4)) return HSLA_ERR_INVALID_ARG;
+  if (seq_lens_after && (!aligned(seq_lens_after, 4) || seq_lens_after == seq_lens_before))
+    return HSLA_ERR_INVALID_ARG;
+  hsla::AppendArgs a{};
+  a.k_pages = pool->k_pages;
+  a.v_pages = pool->v_pages;
+  a.blk_mean = pool->blk_mean;
+  a.blk_var = pool->blk_var;
+  a.block_table = pool->block_table;
+  a.S = state->S;
+  a.z = state->z;
+  a.sv = state->sv;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.seq_lens_before = seq_lens_before;
+  a.seq_lens_after = seq_lens_after;
+  (void)hipGetLastError();
+  return hsla::launch_append(p, a, stream) == hipSuccess ? HSLA_OK : HSLA_ERR_HIP;
+}
+
+size_t hsla_decode_workspace_size(const hsla_config* cfg, int32_t batch, int32_t max_seq_len) {
+  Problem p;
+  if (resolve(cfg, batch, max_seq_len, -1, &p) != HSLA_OK) return 0;
+  return hsla::decode_layout(p).total;
+}
+
+hsla_status hsla_decode(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
+                        const void* q, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                        float* out, int32_t* sel_idx, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, hsla_profile* prof) {
+  Problem p;
+  hsla_status st = resolve(cfg, batch, max_seq_len, pool ? pool->max_blocks_per_seq : 0, &p);
+  if (st != HSLA_OK) return st;
+  if ((st = check_pool(pool, true)) != HSLA_OK) return st;
+  if (p.linear_tail && (st = check_state(state)) != HSLA_OK) return st;
+  if (!q || !aligned(q, 16) || !out || !aligned(out, 16)) return HSLA_ERR_INVALID_ARG;
+  if (!seq_lens || !aligned(seq_lens, 4)) return HSLA_ERR_INVALID_ARG;
+  if (sel_idx && !aligned(sel_idx, 4)) return HSLA_ERR_INVALID_ARG;
+  if (prof && (prof->capacity < 0 || prof->capacity > HSLA_MAX_PROFILE_EVENTS)) return HSLA_ERR_INVALID_ARG;
+  const hsla::DecodeLayout L = hsla::decode_layout(p);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, 16)) return HSLA_ERR_WORKSPACE;
+  hsla::DecodeArgs a{};
+  a.k_pages = pool->k_pages;
+  a.v_pages = pool->v_pages;
+  a.blk_mean = pool->blk_mean;
+  a.blk_var = pool->blk_var;
+  a.block_table = pool->block_table;
+  a.S = p.linear_tail ? state->S : nullptr;
+  a.z = p.linear_tail ? state->z : nullptr;
+  a.sv = p.linear_tail ? state->sv : nullptr;
+  a.q = q;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.sel_idx = sel_idx;
+  a.ws = static_cast<char*>(workspace);
+  ProfileCtx ctx{prof, stream, false};
+  if (prof) prof->recorded = 0;
+  (void)hipGetLastError();
+  const hipError_t e = hsla::launch_decode(p, L, a, stream, prof ? record_event : nullptr, &ctx);
+  if (e != hipSuccess || ctx.failed) return HSLA_ERR_HIP;
+  return HSLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Host-side plumbing between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "hsla.h"
+
+namespace hsla {
+
+// Status of the launch just made; failures are reported on stderr with the
+// kernel's name and HIP's error string.
+inline hipError_t launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) fprintf(stderr, "libhsla: launch of %s failed: %s\n", what, hipGetErrorString(e));
+  return e;
+}
+
+// Resolved, validated problem description handed to the launchers.
+struct Problem {
+  int Hq, Hkv, G, D, B, top_k, ns, W, linear_tail, bf16;
+  float sigma;
+  int batch, max_seq_len;
+  int max_blocks;  // block table row stride
+  int nc_max;      // candidate blocks at max_seq_len
+  int nblk_max;    // blocks of a max_seq_len sequence
+};
+
+// ---------------------------------------------------------------- decode
+struct DecodeLayout {
+  int score_chunk;     // candidates per scoring workgroup
+  int score_wgs;       // scoring workgroups per (sequence, kv head)
+  int ro_wgs;          // readout workgroups per (sequence, kv head)
+  int ro_rows;         // rows of S per readout workgroup
+  int umax;            // union-list capacity per (sequence, kv head)
+  int bps;             // union blocks per attention split
+  int max_split;       // attention splits per (sequence, kv head)
+  int pstride;         // floats per (split, head) partial
+  size_t off_scores, off_ro, off_roz, off_union, off_ucount, off_part, total;
+};
+DecodeLayout decode_layout(const Problem& p);
+
+struct DecodeArgs {
+  const void* k_pages;
+  const void* v_pages;
+  const float* blk_mean;
+  const float* blk_var;
+  const int32_t* block_table;
+  const float* S;
+  const float* z;
+  const float* sv;
+  const void* q;
+  const int32_t* seq_lens;
+  float* out;
+  int32_t* sel_idx;
+  char* ws;
+};
+
+// Launches score+readout, select, attend, merge.  `record` is called with the
+// kernel index before each launch and with the kernel count after the last.
+typedef void (*RecordFn)(void* ctx, int idx, const char* name);
+hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeArgs& a,
+                         hipStream_t stream, RecordFn rec, void* rec_ctx);
+
+// ---------------------------------------------------------------- build
+struct BuildLayout {
+  int tile;      // tokens staged in LDS at a time (multiple of 64 and of B)
+  int chunk;     // tokens per workgroup
+  int nchunk;    // workgroups per (sequence, kv head)
+  size_t part_stride;  // floats per chunk partial (D*D + 2*D)
+  size_t total;
+};
+BuildLayout build_layout(const Problem& p);
+
+struct BuildArgs {
+  const void* k_pages;
+  const void* v_pages;
+  float* blk_mean;
+  float* blk_var;
+  const int32_t* block_table;
+  float* S;
+  float* z;
+  float* sv;
+  const int32_t* seq_lens;
+  float* ws;
+};
+hipError_t launch_build(const Problem& p, const BuildLayout& L, const BuildArgs& a,
+                        hipStream_t stream);
+
+// ---------------------------------------------------------------- append
+struct AppendArgs {
+  void* k_pages;
+  void* v_pages;
+  float* blk_mean;
+  float* blk_var;
+  const int32_t* block_table;
+  float* S;
+  float* z;
+  float* sv;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* seq_lens_before;
+  int32_t* seq_lens_after;
+};
+hipError_t launch_append(const Problem& p, const AppendArgs& a, hipStream_t stream);
+
+}  // namespace hsla

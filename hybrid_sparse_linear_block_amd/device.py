@@ -1,0 +1,101 @@
+"""Device-memory plumbing around the libhsla entry points.
+
+`DeviceCache` owns the torch tensors of one paged KV cache (pages, block
+statistics, linear state, block table, lengths, workspaces) and calls the
+C ABI through the binding.  torch is used for memory and streams only.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import (HSLA_BF16, HSLA_F32, Config, Pool, State, hsla_append_token, hsla_build_state,
+               hsla_build_workspace_size, hsla_decode, hsla_decode_workspace_size)
+
+
+def to_device(x: np.ndarray, device="cuda") -> torch.Tensor:
+    """numpy -> device tensor; uint16 arrays are taken as bfloat16 bit patterns."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(x).to(device)
+
+
+def to_host_bits(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> numpy; bfloat16 becomes uint16 bit patterns."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class DeviceCache:
+    def __init__(self, cfg: Config, k_pages: np.ndarray, v_pages: np.ndarray, block_table: np.ndarray,
+                 seq_lens: np.ndarray, capacity_len: Optional[int] = None, device="cuda"):
+        self.cfg = cfg
+        self.device = device
+        self.k_pages = to_device(k_pages, device)
+        self.v_pages = to_device(v_pages, device)
+        P, Hkv, B, d = self.k_pages.shape
+        assert Hkv == cfg.num_kv_heads and B == cfg.block_size and d == cfg.head_dim
+        assert (self.k_pages.dtype == torch.bfloat16) == (cfg.kv_dtype == HSLA_BF16)
+        self.batch = int(block_table.shape[0])
+        f32 = dict(dtype=torch.float32, device=device)
+        self.blk_mean = torch.zeros((P, Hkv, d), **f32)
+        self.blk_var = torch.zeros((P, Hkv, d), **f32)
+        self.S = torch.zeros((self.batch, Hkv, d, d), **f32)
+        self.z = torch.zeros((self.batch, Hkv, d), **f32)
+        self.sv = torch.zeros((self.batch, Hkv, d), **f32)
+        self.block_table = to_device(block_table.astype(np.int32), device)
+        self.host_lens = np.asarray(seq_lens, np.int64).copy()
+        self.lens = [to_device(self.host_lens.astype(np.int32), device),
+                     torch.zeros(self.batch, dtype=torch.int32, device=device)]
+        self.cur = 0
+        cap = int(capacity_len if capacity_len is not None else self.host_lens.max())
+        cap = min(cap, int(block_table.shape[1]) * B)
+        self.capacity_len = cap
+        self.pool = Pool(self.k_pages, self.v_pages, self.blk_mean, self.blk_var, self.block_table)
+        self.state = State(self.S, self.z, self.sv)
+        self.build_ws = torch.empty(max(16, hsla_build_workspace_size(cfg, self.batch, cap)),
+                                    dtype=torch.uint8, device=device)
+        self.decode_ws = torch.empty(max(16, hsla_decode_workspace_size(cfg, self.batch, cap)),
+                                     dtype=torch.uint8, device=device)
+
+    @property
+    def seq_lens(self) -> torch.Tensor:
+        return self.lens[self.cur]
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.host_lens.max())
+
+    def build(self, stream=None) -> None:
+        hsla_build_state(self.cfg, self.pool, self.state, self.seq_lens, self.batch, self.max_seq_len,
+                         self.build_ws, stream=stream)
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+        assert self.max_seq_len + 1 <= self.capacity_len, "no room mapped for the appended token"
+        nxt = 1 - self.cur
+        hsla_append_token(self.cfg, self.pool, self.state, k_new, v_new, self.lens[self.cur], self.lens[nxt],
+                          self.batch, self.max_seq_len + 1, stream=stream)
+        self.cur = nxt
+        self.host_lens += 1
+
+    def decode(self, q: torch.Tensor, out: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None,
+               want_sel: bool = True, stream=None, prof=None):
+        cfg = self.cfg
+        if out is None:
+            out = torch.empty((self.batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=self.device)
+        if sel is None and want_sel and cfg.top_k > 0:
+            sel = torch.empty((self.batch, cfg.num_q_heads, cfg.top_k), dtype=torch.int32, device=self.device)
+        hsla_decode(cfg, self.pool, self.state if cfg.linear_tail else None, q, self.seq_lens, self.batch,
+                    self.max_seq_len, out, sel, self.decode_ws, stream=stream, prof=prof)
+        return out, sel
+
+
+def config_for(num_q_heads, num_kv_heads, head_dim, block_size, top_k, num_sink, window, linear_tail,
+               kv_dtype: str, scale: float = 0.0) -> Config:
+    return Config(num_q_heads, num_kv_heads, head_dim, block_size, top_k, num_sink, window, linear_tail,
+                  HSLA_BF16 if kv_dtype == "bf16" else HSLA_F32, scale)

@@ -1,0 +1,207 @@
+/*
+ * hsla.h -- C ABI of libhsla, hybrid sparse-plus-linear decode attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages (title, then the part of the page):
+ *   [SPLA]  "SPLA: Block Sparse Plus Linear Attention for Long Context
+ *           Modeling" -- TL;DR, Abstract, sections "Page Attention and
+ *           Selection", "Principled Block Selection via Taylor Expansion",
+ *           "Residual Linear Attention (RLA)", "Recurrence",
+ *           "IO-Efficient Implementation", Figure 1.
+ *   [SALSA] "SALSA: Training-Consistent Sparse Caching with Sink
+ *           Preservation for Linearized LLMs" -- abstract (sliding window,
+ *           sparse global cache, linear hidden state, sink tokens).
+ *   [SLAKE] "SLAKE: Softmax-Approximated Training-Free Linear Attention with
+ *           KV-Cache Eviction for Long-Sequence LLMs" -- abstract (first-order
+ *           Taylor linearisation of softmax for low-importance tokens).
+ *
+ * Definitions used throughout (T = tokens of a sequence including the
+ * current one, B = block_size, d = head_dim, sigma = scale or 1/sqrt(d)):
+ *   - query head h reads kv head h / (num_q_heads / num_kv_heads);
+ *   - block j of a sequence holds tokens [jB, (j+1)B); it is "full" when
+ *     (j+1)B <= T.  Block statistics: mean_j = (1/B) sum k_t and the
+ *     population variance var_j,c = (1/B) sum (k_t,c - mean_j,c)^2;
+ *   - sinks are tokens [0, num_sink), the window is [T - window, T) (it holds
+ *     the current token); candidate blocks intersect [num_sink, T - window);
+ *   - block score = sigma q.mean_j + log1p(sigma^2/2 sum_c q_c^2 var_j,c)
+ *     (second-order Taylor expansion of exp(sigma q.k) around the block mean,
+ *     averaged over the block) [SPLA, "Principled Block Selection ..."];
+ *   - each query head keeps its top_k candidates by (score desc, index asc);
+ *     exact set E = sinks U window U selected blocks, residual U = rest;
+ *   - global linear state over all T tokens with phi(q).phi(k) = 1 + sigma q.k
+ *     [SLAKE]: S = sum_t k_t v_t^T (d x d, S[i][j] = sum k_t,i v_t,j),
+ *     z = sum k_t, sv = sum v_t, n = T;
+ *   - out = (sum_E e^{s_t} v_t + num_U) / (sum_E e^{s_t} + den_U), s_t =
+ *     sigma q.k_t, with num_U = sv + sigma S^T q - sum_E (1+s_t) v_t and
+ *     den_U = n + sigma q.z - sum_E (1+s_t) (global minus selected, so U is
+ *     never read) [SPLA Abstract]; num_U = den_U = 0 when U is empty or the
+ *     linear tail is off.
+ *
+ * Conventions for every entry point:
+ *   - Memory: every pointer is a device pointer unless stated otherwise and
+ *     is owned by the caller.  The library never allocates or frees memory,
+ *     keeps no pointer after returning and has no global mutable state.
+ *     Tensor pointers must be 16-byte aligned.
+ *   - Asynchrony: all work is enqueued on `stream`; results are valid once
+ *     the stream has synchronised.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; on a negative status nothing has been enqueued, except
+ *     HSLA_ERR_HIP, which reports a failed launch.  Device-side contents
+ *     (block tables, lengths) are trusted: a length above max_seq_len or a
+ *     page index outside [0, num_pages) is undefined behaviour.
+ */
+#ifndef HSLA_H
+#define HSLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hsla_status {
+  HSLA_OK = 0,
+  HSLA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer */
+  HSLA_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, group, block size, dtype */
+  HSLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  HSLA_ERR_HIP = -4          /* a kernel launch failed */
+} hsla_status;
+
+typedef enum hsla_dtype { HSLA_F32 = 0, HSLA_BF16 = 1 } hsla_dtype;
+
+/* The problem statement's parameters.
+ * num_q_heads, num_kv_heads: GQA heads; num_q_heads / num_kv_heads must be
+ *   1, 2, 4 or 8.
+ * head_dim: 64 or 128.
+ * block_size: tokens per block and per KV page: 16, 32, 64, 128 or 256
+ *   [SPLA, "Page Attention and Selection": selection at page granularity].
+ * top_k: selected blocks per query head, >= 0 [SPLA Abstract].
+ * num_sink: initial sink tokens, >= 0; window: sliding-window length
+ *   including the current token, >= block_size [SALSA abstract].
+ * linear_tail: 1 = residual linear attention over U [SPLA, "Residual Linear
+ *   Attention (RLA)"]; 0 = drop U (plain block-sparse attention, the
+ *   "discard" behaviour of SPLA Figure 1(c)).
+ * kv_dtype: hsla_dtype of keys, values, queries and appended tokens.
+ * scale: sigma; 0 selects 1/sqrt(head_dim). */
+typedef struct hsla_config {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t top_k;
+  int32_t num_sink;
+  int32_t window;
+  int32_t linear_tail;
+  int32_t kv_dtype;
+  float scale;
+} hsla_config;
+
+/* Paged KV cache [SPLA, "Page Attention and Selection"].
+ * k_pages, v_pages: [num_pages, num_kv_heads, block_size, head_dim] kv_dtype;
+ *   page p, kv head g holds one block of one sequence for that head.
+ * blk_mean, blk_var: [num_pages, num_kv_heads, head_dim] float32 statistics
+ *   of the block stored in that page (defined only for full blocks).
+ * block_table: [batch, max_blocks_per_seq] int32, row-major; entry (b, j) is
+ *   the page of block j of sequence b.  Only entries j < ceil(T_b / B) are
+ *   read (and entry T_b / B by an append). */
+typedef struct hsla_kv_pool {
+  void* k_pages;
+  void* v_pages;
+  float* blk_mean;
+  float* blk_var;
+  const int32_t* block_table;
+  int32_t max_blocks_per_seq;
+  int32_t num_pages;
+} hsla_kv_pool;
+
+/* Global linear state per (sequence, kv head) [SPLA, "Residual Linear
+ * Attention (RLA)", "Recurrence"]: S [batch, Hkv, d, d], z and sv
+ * [batch, Hkv, d], all float32.  n is the sequence length itself. */
+typedef struct hsla_state {
+  float* S;
+  float* z;
+  float* sv;
+} hsla_state;
+
+/* Optional timing hook.  The caller creates `capacity` HIP events; the
+ * library records events[i] on `stream` just before its i-th kernel launch and
+ * one more after the last, sets `recorded`, and names the kernels in
+ * `names[i]` (static strings).  Pass NULL to record nothing. */
+#define HSLA_MAX_PROFILE_EVENTS 8
+typedef struct hsla_profile {
+  hipEvent_t events[HSLA_MAX_PROFILE_EVENTS];
+  int32_t capacity;
+  int32_t recorded;
+  const char* names[HSLA_MAX_PROFILE_EVENTS];
+} hsla_profile;
+
+/* Static description of a status code (never NULL). */
+const char* hsla_status_string(hsla_status status);
+
+/* Library version string (static). */
+const char* hsla_version(void);
+
+/* Bytes of workspace hsla_build_state needs for this shape (0 on invalid
+ * arguments).  Pure host function. */
+size_t hsla_build_workspace_size(const hsla_config* cfg, int32_t batch, int32_t max_seq_len);
+
+/* Build the block statistics of every full block and the global linear state
+ * of every (sequence, kv head) from a prefilled paged cache [SPLA TL;DR,
+ * Abstract; "Recurrence"].
+ * seq_lens: device [batch] int32, T_b <= max_seq_len (host value, sizes the
+ *   launch; >= 1).
+ * Writes pool->blk_mean / blk_var for the pages of full blocks, and
+ * state->S, z, sv for every (b, g).  The sums are reduced in a fixed order,
+ * so repeated builds are bitwise identical.
+ * workspace: device scratch of at least hsla_build_workspace_size() bytes;
+ *   contents on entry are ignored. */
+hsla_status hsla_build_state(const hsla_config* cfg, const hsla_kv_pool* pool,
+                             const hsla_state* state, const int32_t* seq_lens,
+                             int32_t batch, int32_t max_seq_len, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Append one token per (sequence, kv head) [SPLA, "Recurrence"].
+ * k_new, v_new: device [batch, Hkv, head_dim] kv_dtype.
+ * seq_lens_before: device [batch]; the token goes to position T_b =
+ *   seq_lens_before[b], i.e. slot T_b % B of page block_table[b][T_b / B],
+ *   which the caller must have mapped.  T_b + 1 <= max_seq_len.
+ * seq_lens_after: device [batch] or NULL; receives T_b + 1.  Must not alias
+ *   seq_lens_before.
+ * Updates S += k v^T, z += k, sv += v and, when position T_b completes its
+ * block, that block's statistics. */
+hsla_status hsla_append_token(const hsla_config* cfg, const hsla_kv_pool* pool,
+                              const hsla_state* state, const void* k_new, const void* v_new,
+                              const int32_t* seq_lens_before, int32_t* seq_lens_after,
+                              int32_t batch, int32_t max_seq_len, hipStream_t stream);
+
+/* Bytes of workspace hsla_decode needs for this shape (0 on invalid
+ * arguments).  Pure host function. */
+size_t hsla_decode_workspace_size(const hsla_config* cfg, int32_t batch, int32_t max_seq_len);
+
+/* One decode step for every (sequence, query head): block scores from the
+ * statistics, top-k selection, exact softmax attention over E, residual
+ * linear readout over U by subtraction from the global state, merge
+ * [SPLA Abstract, Figure 1; SALSA abstract; SLAKE abstract].
+ * q: device [batch, Hq, head_dim] kv_dtype (the current token's queries).
+ * seq_lens: device [batch], T_b including the current token, 1 <= T_b <=
+ *   max_seq_len.  The current token must already be in the cache and the
+ *   statistics of every full block and the state must be up to date.
+ * out: device [batch, Hq, head_dim] float32.
+ * sel_idx: device [batch, Hq, top_k] int32 or NULL; receives each head's
+ *   selected block indices in ascending order, padded with -1.
+ * workspace: device scratch of at least hsla_decode_workspace_size() bytes;
+ *   contents on entry are ignored.
+ * prof: optional timing hook (NULL for none). */
+hsla_status hsla_decode(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
+                        const void* q, const int32_t* seq_lens, int32_t batch,
+                        int32_t max_seq_len, float* out, int32_t* sel_idx, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream, hsla_profile* prof);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSLA_H */

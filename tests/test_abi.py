@@ -1,0 +1,139 @@
+"""The C ABI library loads, exports every entry point include/hsla.h declares,
+and rejects invalid arguments on the host (no GPU needed: every call here
+fails validation before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_sparse_linear_block_amd as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hsla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hsla_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = H.load()
+    names = declared_functions()
+    assert set(names) == set(H.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        s = H.status_string(code)
+        assert s and "unknown" not in s
+    assert "unknown" in H.status_string(7)
+    assert "gfx950" in H.hsla_version()
+
+
+def cfg(**kw):
+    base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=64, top_k=16, num_sink=4,
+                window=512, linear_tail=1, kv_dtype=H.HSLA_BF16, scale=0.0)
+    base.update(kw)
+    return H.Config(**base)
+
+
+def test_workspace_sizes_are_host_only_and_grow():
+    a = H.hsla_decode_workspace_size(cfg(), 8, 32768)
+    b = H.hsla_decode_workspace_size(cfg(), 8, 131072)
+    assert 0 < a < b
+    assert H.hsla_build_workspace_size(cfg(), 1, 32768) > 0
+    assert H.hsla_decode_workspace_size(cfg(head_dim=96), 8, 32768) == 0
+    assert H.hsla_build_workspace_size(cfg(num_q_heads=30), 8, 32768) == 0
+
+
+BAD_CONFIGS = [
+    (dict(num_q_heads=30), H.HSLA_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), H.HSLA_ERR_INVALID_ARG),
+    (dict(num_q_heads=48, num_kv_heads=8), H.HSLA_ERR_UNSUPPORTED),   # group 6
+    (dict(head_dim=96), H.HSLA_ERR_UNSUPPORTED),
+    (dict(block_size=48), H.HSLA_ERR_UNSUPPORTED),
+    (dict(top_k=-1), H.HSLA_ERR_INVALID_ARG),
+    (dict(num_sink=-2), H.HSLA_ERR_INVALID_ARG),
+    (dict(window=32), H.HSLA_ERR_INVALID_ARG),                         # window < block
+    (dict(linear_tail=2), H.HSLA_ERR_INVALID_ARG),
+    (dict(kv_dtype=7), H.HSLA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), H.HSLA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), H.HSLA_ERR_INVALID_ARG),
+]
+
+FAKE = 1 << 20   # an aligned non-null address; never dereferenced because validation fails first
+
+
+def pool(**kw):
+    base = dict(k_pages=FAKE, v_pages=FAKE, blk_mean=FAKE, blk_var=FAKE, block_table=FAKE,
+                max_blocks_per_seq=1024, num_pages=4096)
+    base.update(kw)
+    return H.hsla_kv_pool(**base)
+
+
+def state(**kw):
+    base = dict(S=FAKE, z=FAKE, sv=FAKE)
+    base.update(kw)
+    return H.hsla_state(**base)
+
+
+def call_decode(c, p=None, st=None, q=FAKE, lens=FAKE, batch=8, max_len=32768, out=FAKE, sel=FAKE,
+                ws=FAKE, ws_bytes=1 << 40):
+    lib = H.load()
+    return lib.hsla_decode(ctypes.byref(c.c()), ctypes.byref(p or pool()), ctypes.byref(st or state()), q, lens,
+                           batch, max_len, out, sel, ws, ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("bad,code", BAD_CONFIGS)
+def test_decode_rejects_bad_configs(bad, code):
+    assert call_decode(cfg(**bad)) == code
+
+
+@pytest.mark.parametrize("bad,code", BAD_CONFIGS)
+def test_build_and_append_reject_bad_configs(bad, code):
+    lib = H.load()
+    c = cfg(**bad)
+    assert lib.hsla_build_state(ctypes.byref(c.c()), ctypes.byref(pool()), ctypes.byref(state()), FAKE, 8, 32768,
+                                FAKE, 1 << 40, None) == code
+    assert lib.hsla_append_token(ctypes.byref(c.c()), ctypes.byref(pool()), ctypes.byref(state()), FAKE, FAKE,
+                                 FAKE, FAKE + 256, 8, 32768, None) == code
+
+
+def test_decode_rejects_bad_pointers_and_sizes():
+    c = cfg()
+    E = H.HSLA_ERR_INVALID_ARG
+    assert call_decode(c, q=0) == E
+    assert call_decode(c, q=FAKE + 2) == E               # misaligned
+    assert call_decode(c, out=0) == E
+    assert call_decode(c, lens=0) == E
+    assert call_decode(c, sel=FAKE + 2) == E
+    assert call_decode(c, batch=0) == E
+    assert call_decode(c, max_len=0) == E
+    assert call_decode(c, p=pool(k_pages=0)) == E
+    assert call_decode(c, p=pool(blk_var=FAKE + 4)) == E
+    assert call_decode(c, p=pool(max_blocks_per_seq=100)) == E   # 100 blocks < 32768 / 64
+    assert call_decode(c, st=state(S=0)) == E
+    assert call_decode(c, ws=0) == H.HSLA_ERR_WORKSPACE
+    assert call_decode(c, ws_bytes=16) == H.HSLA_ERR_WORKSPACE
+    assert call_decode(c, max_len=(1 << 20) * 64) == H.HSLA_ERR_UNSUPPORTED
+
+
+def test_append_rejects_aliased_lengths():
+    lib = H.load()
+    c = cfg()
+    assert lib.hsla_append_token(ctypes.byref(c.c()), ctypes.byref(pool()), ctypes.byref(state()), FAKE, FAKE,
+                                 FAKE, FAKE, 8, 32768, None) == H.HSLA_ERR_INVALID_ARG
+    assert lib.hsla_append_token(ctypes.byref(c.c()), ctypes.byref(pool()), ctypes.byref(state()), 0, FAKE,
+                                 FAKE, None, 8, 32768, None) == H.HSLA_ERR_INVALID_ARG
+
+
+def test_build_rejects_small_workspace():
+    lib = H.load()
+    c = cfg()
+    assert lib.hsla_build_state(ctypes.byref(c.c()), ctypes.byref(pool()), ctypes.byref(state()), FAKE, 8, 32768,
+                                FAKE, 64, None) == H.HSLA_ERR_WORKSPACE

@@ -1,0 +1,295 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Every case prints its name, seed and shape before touching the GPU."""
+import dataclasses
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from parity import (OUT_TOL, assert_state_close, assert_stats_close, check_selection, gpu_selection,
+                    row_rel_err)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # collected on CPU hosts, skipped there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import hybrid_sparse_linear_block_amd as H  # noqa: E402
+from hybrid_sparse_linear_block_amd.device import DeviceCache, config_for, to_device  # noqa: E402
+
+
+def _announce(wl, extra=""):
+    print(f"[case] {wl.name} cid={wl.cid} batch={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
+          f"d={wl.head_dim} B={wl.block_size} k={wl.top_k} ns={wl.num_sink} W={wl.window} "
+          f"lin={wl.linear_tail} {wl.kv_dtype} T={list(wl.seq_lens)[:8]} {extra}", flush=True)
+    sys.stdout.flush()
+
+
+def cfg_of(wl):
+    return config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
+                      wl.window, wl.linear_tail, wl.kv_dtype, wl.scale)
+
+
+def params_of(wl):
+    return O.Params(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
+                    wl.window, wl.linear_tail, wl.scale)
+
+
+def run_gpu(wl, inp, capacity_len=None):
+    dc = DeviceCache(cfg_of(wl), inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"],
+                     capacity_len=capacity_len)
+    dc.build()
+    q = to_device(inp["q"])
+    out, sel = dc.decode(q)
+    torch.cuda.synchronize()
+    return dc, out.cpu().numpy(), (None if sel is None else sel.cpu().numpy())
+
+
+def state_depth(T):
+    return min(T, 4096) + math.ceil(T / 32) + 16
+
+
+def check_case(wl, inp, dc, out, sel, heads=None, check_build=True, pair_data=None):
+    """Compares statistics, state, selections and outputs with the oracle.
+    Returns (worst row error, number of near-tie flips)."""
+    p = params_of(wl)
+    B, G = wl.block_size, wl.group
+    q64 = O.to_f64(inp["q"], wl.kv_dtype)
+    table = inp["block_table"]
+    if heads is None:
+        heads = [(b, h) for b in range(wl.batch) for h in range(wl.num_q_heads)]
+    pairs = sorted({(b, h // G) for b, h in heads})
+    if check_build:
+        mean_g, var_g = dc.blk_mean.cpu().numpy(), dc.blk_var.cpu().numpy()
+        S_g, z_g, sv_g = dc.S.cpu().numpy(), dc.z.cpu().numpy(), dc.sv.cpu().numpy()
+    cache = {}
+    for b, g in pairs:
+        if pair_data is not None:
+            K, V = pair_data(b, g)
+        else:
+            K, V = inp["pairs"][(b, g)]
+        Kf, Vf = O.to_f64(K, wl.kv_dtype), O.to_f64(V, wl.kv_dtype)
+        stats = O.block_statistics(Kf, B)
+        state = O.global_state(Kf, Vf)
+        cache[(b, g)] = (Kf, Vf, stats, state)
+        if check_build:
+            T = Kf.shape[0]
+            nb = T // B
+            pages = table[b, :nb]
+            assert_stats_close(mean_g[pages, g], var_g[pages, g], stats[0], stats[1], Kf, B, f"pair {(b, g)}")
+            gs = O.LinearState(S_g[b, g].astype(np.float64), z_g[b, g].astype(np.float64),
+                               sv_g[b, g].astype(np.float64), T)
+            assert_state_close(gs, state, Kf, Vf, state_depth(T), f"pair {(b, g)}")
+    worst, flips = 0.0, 0
+    for b, h in heads:
+        Kf, Vf, stats, state = cache[(b, h // G)]
+        r = O.decode_head(q64[b, h], Kf, Vf, p, stats=stats, state=state)
+        if sel is not None:
+            gs = gpu_selection(sel[b, h])
+            ok, flip, msg = check_selection(r, gs, wl.top_k)
+            assert ok, f"(b={b}, h={h}) {msg}"
+            if flip:
+                flips += 1
+                r = O.decode_head(q64[b, h], Kf, Vf, p, stats=stats, state=state, selected=gs)
+        assert np.isfinite(out[b, h]).all(), f"(b={b}, h={h}) non-finite output"
+        err = row_rel_err(out[b, h], r.out)
+        assert err <= OUT_TOL[wl.kv_dtype], f"(b={b}, h={h}) row error {err:.3e}"
+        worst = max(worst, err)
+    return worst, flips
+
+
+# ----------------------------------------------------------------------------
+# Reduced workloads: every head against the oracle
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny_f32_2k", "llama8b_small", "needle_small", "ragged_small"])
+def test_small_workloads(name):
+    wl = W.small(name)
+    _announce(wl)
+    inp = W.make_inputs(wl)
+    dc, out, sel = run_gpu(wl, inp)
+    worst, flips = check_case(wl, inp, dc, out, sel)
+    print(f"  worst row error {worst:.3e}, near-tie flips {flips}")
+
+
+def test_hybrid_layers_small():
+    for wl in W.hybrid_small():
+        _announce(wl)
+        inp = W.make_inputs(wl)
+        dc, out, sel = run_gpu(wl, inp)
+        worst, _ = check_case(wl, inp, dc, out, sel)
+        print(f"  layer {wl.layer}: worst {worst:.3e}")
+
+
+def test_needles_recalled_on_gpu():
+    wl = W.small("needle_small")
+    _announce(wl)
+    inp = W.make_inputs(wl)
+    _, _, sel = run_gpu(wl, inp)
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            for blk, h in W.needle_plan(wl, b, g):
+                assert blk in sel[b, h].tolist(), (b, g, blk, h)
+
+
+# ----------------------------------------------------------------------------
+# Special cases and edge shapes
+# ----------------------------------------------------------------------------
+
+def _wl(name, cid, **kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=64, top_k=6, num_sink=4,
+                window=256, linear_tail=1, kv_dtype=W.BF16, seq_lens=(1500, 1203), shuffle_pages=True,
+                spare_pages=2)
+    base.update(kw)
+    return W.Workload(name, cid, **base)
+
+
+def test_dense_when_budget_covers_all_candidates():
+    wl = _wl("dense_k", 30, top_k=40)          # 40 >= every n_cand here
+    _announce(wl)
+    inp = W.make_inputs(wl)
+    dc, out, sel = run_gpu(wl, inp)
+    check_case(wl, inp, dc, out, sel)
+    p = params_of(wl)
+    for b in range(wl.batch):
+        for h in range(wl.num_q_heads):
+            K, V = inp["pairs"][(b, h // wl.group)]
+            ref = O.dense_attention(O.to_f64(inp["q"][b, h], wl.kv_dtype), O.to_f64(K, wl.kv_dtype),
+                                    O.to_f64(V, wl.kv_dtype), p.sigma)
+            assert row_rel_err(out[b, h], ref) <= OUT_TOL[wl.kv_dtype]
+
+
+def test_sinks_and_window_only():
+    wl = _wl("sink_window", 31, top_k=0, linear_tail=0)
+    _announce(wl)
+    inp = W.make_inputs(wl)
+    dc, out, sel = run_gpu(wl, inp)
+    check_case(wl, inp, dc, out, sel)
+
+
+@pytest.mark.parametrize("lens", [(1, 5), (64, 260), (300, 261), (255, 320)])
+def test_short_sequences_have_no_candidates(lens):
+    wl = _wl(f"short_{lens[0]}_{lens[1]}", 32, seq_lens=lens, window=256, num_sink=4)
+    _announce(wl)
+    inp = W.make_inputs(wl)
+    dc, out, sel = run_gpu(wl, inp)
+    check_case(wl, inp, dc, out, sel)
+
+
+SHAPES = [
+    # (G, d, B, dtype, ns, W, k, lin)
+    (1, 128, 64, W.BF16, 4, 512, 8, 1),
+    (8, 128, 64, W.BF16, 4, 512, 5, 1),
+    (2, 64, 32, W.BF16, 0, 100, 7, 1),
+    (4, 128, 16, W.BF16, 20, 48, 12, 1),
+    (4, 128, 128, W.F32, 4, 256, 3, 1),
+    (4, 64, 256, W.BF16, 300, 600, 2, 1),
+    (4, 128, 256, W.BF16, 4, 256, 3, 0),
+    (4, 64, 64, W.F32, 70, 130, 4, 1),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "G{}_d{}_B{}_{}_ns{}_W{}_k{}_lin{}".format(*s))
+def test_shapes(shape):
+    G, d, B, dt, ns, Wn, k, lin = shape
+    wl = _wl("shape", 40 + SHAPES.index(shape), num_q_heads=2 * G, num_kv_heads=2, head_dim=d, block_size=B,
+             kv_dtype=dt, num_sink=ns, window=Wn, top_k=k, linear_tail=lin, seq_lens=(2311, 1777))
+    _announce(wl)
+    inp = W.make_inputs(wl)
+    dc, out, sel = run_gpu(wl, inp)
+    check_case(wl, inp, dc, out, sel)
+
+
+def test_exact_ties_go_to_the_lower_block():
+    """Blocks 5, 9 and 20 are copies of block 2, which is made to score high
+    for the first query head of each group: with k = 3 the four-way tie at the
+    top straddles the cut and must resolve to blocks 2, 5, 9."""
+    wl = _wl("ties", 50, batch=1, seq_lens=(2048,), top_k=3, shuffle_pages=False)
+    _announce(wl)
+    inp = W.make_inputs(wl)
+    B = wl.block_size
+    rng = np.random.default_rng(7)
+    for g in range(wl.num_kv_heads):
+        K, V = inp["pairs"][(0, g)]
+        qh = W.bf16_to_f32(inp["q"][0, g * wl.group])
+        qhat = qh / np.sqrt((qh.astype(np.float64) ** 2).sum())
+        K[2 * B:3 * B] = W.bf16_round(3.0 * qhat[None, :] + rng.standard_normal((B, wl.head_dim)))
+        for dst in (5, 9, 20):
+            K[dst * B:(dst + 1) * B] = K[2 * B:3 * B]
+        W.scatter_pairs(wl, inp["block_table"], inp["k_pages"], 0, g, K)
+    dc, out, sel = run_gpu(wl, inp)
+    check_case(wl, inp, dc, out, sel)
+    for g in range(wl.num_kv_heads):
+        assert gpu_selection(sel[0, g * wl.group]) == [2, 5, 9]
+
+
+def test_page_order_does_not_change_results():
+    wl1 = _wl("pages_a", 51, shuffle_pages=False)
+    wl2 = dataclasses.replace(wl1, name="pages_b", shuffle_pages=True, spare_pages=7)
+    _announce(wl1)
+    inp1, inp2 = W.make_inputs(wl1), W.make_inputs(wl2)
+    _, o1, s1 = run_gpu(wl1, inp1)
+    _, o2, s2 = run_gpu(wl2, inp2)
+    assert np.array_equal(s1, s2)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
+def test_runs_are_bitwise_reproducible():
+    wl = W.small("llama8b_small")
+    _announce(wl)
+    inp = W.make_inputs(wl)
+    dc, o1, s1 = run_gpu(wl, inp)
+    S1 = dc.S.cpu().numpy().copy()
+    dc.build()
+    o2, s2 = dc.decode(to_device(inp["q"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(S1.view(np.uint32), dc.S.cpu().numpy().view(np.uint32))
+    assert np.array_equal(o1.view(np.uint32), o2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(s1, s2.cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_append_matches_rebuild(dtype):
+    """Decode after N appends (crossing block boundaries) equals the oracle on
+    the full sequence, and the appended state matches a rebuild."""
+    N = 70
+    full = _wl("append_full", 60, kv_dtype=dtype, seq_lens=(1400, 1250), append_room=3)
+    start = dataclasses.replace(full, name="append_start", seq_lens=tuple(t - N for t in full.seq_lens))
+    _announce(full, f"N={N}")
+    inp_full = W.make_inputs(full)
+    table = inp_full["block_table"]
+    # Start from the first T-N tokens of every pair, laid out in the same pages.
+    kp, vp = W.empty_pool(full), W.empty_pool(full)
+    for (b, g), (K, V) in inp_full["pairs"].items():
+        W.scatter_pairs(full, table, kp, b, g, K[:start.seq_lens[b]])
+        W.scatter_pairs(full, table, vp, b, g, V[:start.seq_lens[b]])
+    dc = DeviceCache(cfg_of(full), kp, vp, table, np.asarray(start.seq_lens, np.int32),
+                     capacity_len=max(full.seq_lens))
+    dc.build()
+    for i in range(N):
+        kn = np.stack([np.stack([inp_full["pairs"][(b, g)][0][start.seq_lens[b] + i]
+                                 for g in range(full.num_kv_heads)]) for b in range(full.batch)])
+        vn = np.stack([np.stack([inp_full["pairs"][(b, g)][1][start.seq_lens[b] + i]
+                                 for g in range(full.num_kv_heads)]) for b in range(full.batch)])
+        dc.append(to_device(kn), to_device(vn))
+    out, sel = dc.decode(to_device(inp_full["q"]))
+    torch.cuda.synchronize()
+    assert dc.seq_lens.cpu().numpy().tolist() == list(full.seq_lens)
+    inp_check = dict(inp_full)
+    worst, _ = check_case(full, inp_check, dc, out.cpu().numpy(), sel.cpu().numpy(), check_build=False)
+    # statistics and state after appends
+    mean_g, var_g = dc.blk_mean.cpu().numpy(), dc.blk_var.cpu().numpy()
+    for (b, g), (K, V) in inp_full["pairs"].items():
+        Kf, Vf = O.to_f64(K, dtype), O.to_f64(V, dtype)
+        st = O.global_state(Kf, Vf)
+        gs = O.LinearState(dc.S[b, g].cpu().numpy().astype(np.float64), dc.z[b, g].cpu().numpy().astype(np.float64),
+                           dc.sv[b, g].cpu().numpy().astype(np.float64), Kf.shape[0])
+        assert_state_close(gs, st, Kf, Vf, state_depth(Kf.shape[0]) + N)
+        m, v = O.block_statistics(Kf, full.block_size)
+        pages = table[b, :Kf.shape[0] // full.block_size]
+        assert_stats_close(mean_g[pages, g], var_g[pages, g], m, v, Kf, full.block_size)
