@@ -1,0 +1,326 @@
+"""Decode-step benchmark of hybrid sparse-plus-linear attention on one MI355X.
+
+A step is one pass of the decode hot path for every sequence of the batch:
+hsla_append_token (the new token's k/v into its page, rank-1 update of the
+linear state, statistics of a block that fills) followed by hsla_decode
+(block scores + state readout, top-k, split-K exact attention over sinks,
+window and selected blocks, merge with the subtracted linear residual).
+The state/statistics build runs once per cache before the timed region and
+is reported separately under "build".
+
+Default workload: Llama-3.1-8B-shaped layer, batch 8, 32 query / 8 kv heads,
+d 128, 32768-token bf16 context (per-channel scales), block 64, top-k 16,
+4 sinks, window 512.  To keep the Infinity Cache (MALL) from serving a
+step's ~190 MB working set, the timed steps rotate over `--replicas`
+independent caches (as successive layers of a model would), each with its
+own queries.
+
+Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode attention µs/step & tokens/s at 32K/128K ctx; % of HBM roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b_32k", choices=["llama8b_32k", "needle_128k", "ragged_paged"])
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def workload(name):
+    import workloads as W
+    return {"llama8b_32k": W.llama8b_32k, "needle_128k": W.needle_128k, "ragged_paged": W.ragged_paged}[name]()
+
+
+class Hip:
+    """hipEvent helpers on the HIP runtime torch loaded (same soname)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return out.value
+
+
+def n_cand(T, wl):
+    lo = wl.num_sink // wl.block_size
+    hi = T - wl.window
+    return 0 if hi <= wl.num_sink else -(-hi // wl.block_size) - lo
+
+
+def union_tokens(T, wl, sel_rows):
+    """Tokens of sinks U window U every selected block of the group's heads."""
+    B = wl.block_size
+    mask = np.zeros(T, bool)
+    mask[:min(wl.num_sink, T)] = True
+    mask[max(0, T - wl.window):] = True
+    for row in sel_rows:
+        for blk in row:
+            if blk >= 0:
+                mask[blk * B:(blk + 1) * B] = True
+    return int(mask.sum())
+
+
+def step_bytes(wl, lens, sel):
+    """Algorithmic bytes of one decode call (kernel-level split) for the given
+    lengths and selections [batch, Hq, k]."""
+    d, G, e = wl.head_dim, wl.group, wl.elem_bytes
+    stats = state = kv = qio = selb = 0
+    for b in range(wl.batch):
+        T = int(lens[b])
+        for g in range(wl.num_kv_heads):
+            stats += n_cand(T, wl) * 2 * d * 4
+            state += (d * d + 2 * d) * 4 if wl.linear_tail else 0
+            rows = sel[b, g * G:(g + 1) * G] if sel is not None else []
+            kv += union_tokens(T, wl, rows) * 2 * d * e
+            qio += G * d * (e + 4)
+            selb += G * wl.top_k * 4
+    return dict(stats=stats, state=state, kv=kv, q_out=qio, sel=selb,
+                attend=kv + G * d * e * wl.batch * wl.num_kv_heads,
+                score_readout=stats + state + G * d * e * wl.batch * wl.num_kv_heads,
+                decode=stats + state + kv + qio + selb)
+
+
+def append_bytes(wl):
+    d, e = wl.head_dim, wl.elem_bytes
+    per_pair = 2 * d * d * 4 + 2 * 2 * d * 4 + 2 * d * e + 2 * d * e
+    return per_pair * wl.batch * wl.num_kv_heads
+
+
+def source_sha():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "hybrid_sparse_linear_block_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_entry(workload_name):
+    """HBM traffic of k_attend from the committed rocprofv3 counter runs, if
+    they were taken on the current kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = t.get(workload_name)
+    if not ent or ent.get("source_sha") != source_sha():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp_q, gpu_out, gpu_sel, budget_s):
+    """The fp64 oracle on a bounded sample of the same decode step: heads of
+    the first sequences, with block statistics and the linear state
+    precomputed (as the GPU path has them), timed on this host's cores."""
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    p = O.Params(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
+                 wl.window, wl.linear_tail, wl.scale)
+    heads_done, t_heads, worst = 0, 0.0, 0.0
+    t_start = time.perf_counter()
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            K, V = W.gen_pair(wl, b, g, inp_q)
+            Kf, Vf = O.to_f64(K, wl.kv_dtype), O.to_f64(V, wl.kv_dtype)
+            stats = O.block_statistics(Kf, wl.block_size)
+            state = O.global_state(Kf, Vf)
+            for hh in range(wl.group):
+                h = g * wl.group + hh
+                q = O.to_f64(inp_q[b, h], wl.kv_dtype)
+                t0 = time.perf_counter()
+                r = O.decode_head(q, Kf, Vf, p, stats=stats, state=state)
+                t_heads += time.perf_counter() - t0
+                heads_done += 1
+                gsel = [int(x) for x in gpu_sel[b, h] if x >= 0]
+                if gsel != r.selected.tolist():   # near-tie: compare against the GPU's choice
+                    r = O.decode_head(q, Kf, Vf, p, stats=stats, state=state, selected=gsel)
+                worst = max(worst, float(np.abs(gpu_out[b, h] - r.out).max() / np.abs(r.out).max()))
+            if time.perf_counter() - t_start > budget_s:
+                break
+        if time.perf_counter() - t_start > budget_s:
+            break
+    per_head = t_heads / heads_done
+    step_s = per_head * wl.batch * wl.num_q_heads
+    return dict(value=wl.batch / step_s, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=(f"{heads_done} of {wl.batch * wl.num_q_heads} (sequence, query head) decodes of one "
+                        f"step at T={max(wl.seq_lens)}, fp64 subtraction form with statistics and state "
+                        f"precomputed; step time = mean per head x {wl.batch * wl.num_q_heads}; append "
+                        f"not included"),
+                seconds=round(t_heads, 3), ms_per_step=round(step_s * 1e3, 1)), worst
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus above 1 is not supported "
+              "(the path shards by (sequence, kv head) with no exchange, see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads as W
+    from hybrid_sparse_linear_block_amd import hsla_profile
+    from hybrid_sparse_linear_block_amd.device import DeviceCache, PreparedDecodeStep, config_for, to_device
+
+    torch.cuda.set_device(0)
+    wl = workload(args.workload)
+    steps, warm, R = args.steps, args.warmup, max(1, args.replicas)
+    appends_per_replica = -(-(steps + warm) // R) + 1
+    wl = W.dataclasses.replace(wl, append_room=1 + -(-appends_per_replica // wl.block_size))
+    t0 = time.perf_counter()
+    inp = W.make_inputs(wl, keep_pairs=False)
+    t_gen = time.perf_counter() - t0
+    print(f"[bench] {wl.name}: inputs generated in {t_gen:.1f}s", file=sys.stderr, flush=True)
+    cfg = config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
+                     wl.window, wl.linear_tail, wl.kv_dtype)
+    cap = max(wl.seq_lens) + appends_per_replica + 1
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    caches, preps, qs = [], [], []
+    base = DeviceCache(cfg, inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"], capacity_len=cap)
+    k_tok, v_tok = W.gen_token(wl, 0)
+    k_tok, v_tok = to_device(k_tok), to_device(v_tok)
+    build_ms = []
+    for r in range(R):
+        # independent caches with the same contents at other addresses
+        dc = base if r == 0 else DeviceCache(cfg, inp["k_pages"], inp["v_pages"], inp["block_table"],
+                                             inp["seq_lens"], capacity_len=cap)
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        dc.build()
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        build_ms.append(hip.ms(e0, e1))
+        q = to_device(W.gen_queries(wl, variant=r))
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+        sel = torch.empty((wl.batch, wl.num_q_heads, max(1, wl.top_k)), dtype=torch.int32, device="cuda")
+        caches.append(dc)
+        qs.append(q)
+        preps.append(PreparedDecodeStep(dc, q, k_tok, v_tok, out, sel))
+    print(f"[bench] {R} caches built; build {np.mean(build_ms) * 1e3:.1f} us each", file=sys.stderr, flush=True)
+
+    # Spot check before any append: replica 0's decode at the prefilled length.
+    out0, sel0 = caches[0].decode(qs[0])
+    torch.cuda.synchronize()
+    out0, sel0 = out0.cpu().numpy(), sel0.cpu().numpy()
+    bytes0 = step_bytes(wl, caches[0].host_lens, sel0)
+
+    for i in range(warm):
+        preps[i % R]()
+    torch.cuda.synchronize()
+
+    nev = 5
+    evs = [[hip.event() for _ in range(nev)] for _ in range(steps)]
+    ev_app = [hip.event() for _ in range(steps)]
+    profs = []
+    for i in range(steps):
+        pr = hsla_profile()
+        pr.capacity = nev
+        for j in range(nev):
+            pr.events[j] = evs[i][j]
+        profs.append(pr)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        hip.record(ev_app[i], stream)
+        preps[i % R](profs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = [profs[0].names[j].decode() for j in range(nev - 1)]
+    per_kernel = {n: float(np.mean([hip.ms(evs[i][j], evs[i][j + 1]) for i in range(steps)]) * 1e3)
+                  for j, n in enumerate(names)}
+    per_kernel["append"] = float(np.mean([hip.ms(ev_app[i], evs[i][0]) for i in range(steps)]) * 1e3)
+    gpu_step_us = float(np.mean([hip.ms(ev_app[i], evs[i][nev - 1]) for i in range(steps)]) * 1e3)
+
+    # Algorithmic bytes from each replica's selections at its final length.
+    per_rep = []
+    for r in range(R):
+        o, s = caches[r].decode(qs[r])
+        torch.cuda.synchronize()
+        per_rep.append(step_bytes(wl, caches[r].host_lens, s.cpu().numpy()))
+    avg = {k: float(np.mean([d[k] for d in per_rep])) for k in per_rep[0]}
+    app_b = append_bytes(wl)
+
+    attend_us = per_kernel["attend"]
+    ms_per_step = wall / steps * 1e3
+    tokens_s = wl.batch / (wall / steps)
+    traffic = traffic_entry(wl.name)
+    roofline = {"bound": "hbm", "kernel": "k_attend", "achieved": round(avg["attend"] / (attend_us * 1e-6) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(avg["attend"] / (attend_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "bytes_per_launch": int(avg["attend"]), "us_per_launch": round(attend_us, 2)}
+    step_bytes_total = avg["decode"] + app_b
+    res = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "accumulate": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "ctx": int(max(wl.seq_lens)), "q_heads": wl.num_q_heads,
+                   "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block": wl.block_size,
+                   "top_k": wl.top_k, "sinks": wl.num_sink, "window": wl.window, "replicas": R,
+                   "step": "append + decode"},
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "gpu_us_per_step": round(gpu_step_us, 2),
+        "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
+        "roofline": roofline,
+        "step_roofline": {"bytes": int(step_bytes_total), "achieved": round(step_bytes_total / (gpu_step_us * 1e-6) / 1e9, 1),
+                          "frac": round(step_bytes_total / (gpu_step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "unit": "GB/s"},
+        "bytes_split": {k: int(v) for k, v in avg.items()},
+        "build": {"us": round(float(np.mean(build_ms)) * 1e3, 1),
+                  "bytes": int(wl.batch * wl.num_kv_heads * (max(wl.seq_lens) * wl.head_dim * 2 * wl.elem_bytes
+                                                              + (wl.head_dim ** 2 + 2 * wl.head_dim) * 4
+                                                              + max(wl.seq_lens) // wl.block_size * 2 * wl.head_dim * 4)),
+                  "flop": int(wl.batch * wl.num_kv_heads * 2 * max(wl.seq_lens) * wl.head_dim ** 2)},
+    }
+    res["build"]["GB/s"] = round(res["build"]["bytes"] / (res["build"]["us"] * 1e-6) / 1e9, 1)
+    res["build"]["TFLOP/s"] = round(res["build"]["flop"] / (res["build"]["us"] * 1e-6) / 1e12, 1)
+    if not args.no_cpu_baseline:
+        cb, worst = cpu_baseline(wl, inp["q"], out0, sel0, args.cpu_seconds)
+        res["cpu_baseline"] = cb
+        res["spot_check_max_row_err"] = float(f"{worst:.3e}")
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

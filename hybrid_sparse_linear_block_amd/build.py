@@ -20,7 +20,7 @@ ARCH = os.environ.get("HSLA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
-    "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+    "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++20",
     # packed fp32 VALU forms stay disabled on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",

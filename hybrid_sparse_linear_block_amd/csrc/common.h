@@ -63,9 +63,42 @@ struct Row8<KvF32> {
 // primitives: quad xor 1, quad xor 2, half-row mirror, row mirror.  After
 // reduce_rowN every lane of its N-lane group holds the group's sum.
 // ---------------------------------------------------------------------------
+// Every pattern used here reads a lane of the same row, so bound_ctrl never
+// applies; with it set the compiler folds the move into the consuming VALU op.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// The values of lane l and lane l ^ OFF, as (a, b).  Which of the two is
+// lane l's own value is fixed per OFF but not exposed: callers combine a and
+// b symmetrically (sum, max, or a pairing that is the same for every
+// variable), so they do not depend on it.  OFF 8 uses DPP row_ror:8; 16 and
+// 32 use the gfx950 permlane swaps; no LDS traffic.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
+  if constexpr (OFF == 8) {
+    a = x;
+    b = dpp_f<0x128>(x);
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else if constexpr (OFF == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    a = x;
+    b = __shfl_xor(x, OFF);
+  }
+}
+
+template <int OFF>
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  lane_pair<OFF>(x, a, b);
+  return a + b;
 }
 
 template <int N>
@@ -75,8 +108,27 @@ __device__ __forceinline__ float reduce_sum_lanes(float v) {
   if constexpr (N >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
   if constexpr (N >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
   if constexpr (N >= 16) v += dpp_f<0x140>(v); // row_mirror
-  if constexpr (N >= 32) v += __shfl_xor(v, 16);
+  if constexpr (N >= 32) v = pair_sum<16>(v);
   return v;
+}
+
+// Wavefront-wide reductions without LDS: DPP within rows, permlane swaps
+// across rows.  Every lane ends with the result.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = reduce_sum_lanes<16>(v);
+  v = pair_sum<16>(v);
+  return pair_sum<32>(v);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  float a, b;
+  lane_pair<16>(v, a, b);
+  v = fmaxf(a, b);
+  lane_pair<32>(v, a, b);
+  return fmaxf(a, b);
 }
 
 __device__ __forceinline__ float fast_exp(float x) {

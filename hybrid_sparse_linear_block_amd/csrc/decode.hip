@@ -22,6 +22,11 @@
 //      residual linear part into the normalised output.
 #include <math.h>
 
+#include <algorithm>
+
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 #include "internal.h"
 
@@ -31,6 +36,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr float kNegInf = -INFINITY;
+constexpr int kScoreChunk = 64;  // candidates per scoring workgroup
+constexpr int kRoRows = 16;      // rows of S per readout workgroup
+constexpr int kUnit = 64;        // tokens per attention work unit
+constexpr int kUnitsPerWg = 8;   // attention work units per workgroup
 
 struct DecodeParams {
   const void* k_pages;
@@ -49,12 +58,14 @@ struct DecodeParams {
   float* ro;
   float* roz;
   int32_t* ulist;
+  int32_t* upage;
   int32_t* ucount;
   float* part;
   int Hq, Hkv, B, top_k, ns, W, linear_tail;
   int max_blocks, max_seq_len, nc_max, nblk_max;
-  int score_chunk, score_wgs, ro_wgs, ro_rows;
+  int score_wgs, ro_wgs;
   int umax, bps, max_split, pstride;
+  int keys_staged;
   float sigma;
 };
 
@@ -119,97 +130,124 @@ __device__ __forceinline__ float q_elem(const void* q, size_t idx) {
 // 1. Block scores + global-state readout
 // ---------------------------------------------------------------------------
 template <typename KV, int D, int G>
-__device__ void score_part(const DecodeParams& P, int b, int g, int T, int chunk) {
-  constexpr int LPT = D / 8;           // lanes per candidate (8 channels each)
-  constexpr int CPP = kThreads / LPT;  // candidates per pass
+__device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, int T, int chunk) {
+  constexpr int LPT = D / 8;            // lanes per candidate (8 channels each)
+  constexpr int CPP = kThreads / LPT;   // candidates per pass
+  constexpr int NIT = kScoreChunk / CPP;
   static_assert(G <= LPT, "one writer lane per head");
   const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
   const int nc = min(cr.count, P.nc_max);
-  const int c_begin = chunk * P.score_chunk;
-  const int c_end = min(c_begin + P.score_chunk, nc);
-  if (c_begin >= c_end) return;
+  const int c_begin = chunk * kScoreChunk;
+  if (c_begin >= nc) return;
   const int tid = threadIdx.x;
   const int lig = tid % LPT;
   const int slot = tid / LPT;
+  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
 
-  float qf[G][8];
+  // Issue every load of the chunk before any arithmetic: page ids, then the
+  // statistics rows, then the queries.
+  int page[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int c = c_begin + slot + it * CPP;
+    const int pg = bt[cr.lo + min(c, nc - 1)];
+    page[it] = (c < nc) ? pg : -1;
+  }
+  float4 m0[NIT], m1[NIT], v0[NIT], v1[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {   // unconditional loads; unused slots read page 0
+    const size_t off = (static_cast<size_t>(max(page[it], 0)) * P.Hkv + g) * D + lig * 8;
+    m0[it] = *reinterpret_cast<const float4*>(P.blk_mean + off);
+    m1[it] = *reinterpret_cast<const float4*>(P.blk_mean + off + 4);
+    v0[it] = *reinterpret_cast<const float4*>(P.blk_var + off);
+    v1[it] = *reinterpret_cast<const float4*>(P.blk_var + off + 4);
+  }
+  // sigma q and (sigma^2 / 2) q^2: the score is then two plain dot products.
+  float qs[G][8], qq[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     QReg<KV> qr;
     qr.load(reinterpret_cast<const char*>(P.q) +
             ((static_cast<size_t>(b) * P.Hq + g * G + h) * D + lig * 8) * KV::kBytes);
-    qr.to_f32(qf[h]);
+    float qf[8];
+    qr.to_f32(qf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qs[h][i] = P.sigma * qf[i];
+      qq[h][i] = 0.5f * qs[h][i] * qs[h][i];
+    }
   }
-  const float sig = P.sigma;
-  const float half_s2 = 0.5f * sig * sig;
-  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
-
-  for (int c = c_begin + slot; c < c_end; c += CPP) {
-    const int page = bt[cr.lo + c];
-    const size_t off = (static_cast<size_t>(page) * P.Hkv + g) * D + lig * 8;
-    const float4 m0 = *reinterpret_cast<const float4*>(P.blk_mean + off);
-    const float4 m1 = *reinterpret_cast<const float4*>(P.blk_mean + off + 4);
-    const float4 v0 = *reinterpret_cast<const float4*>(P.blk_var + off);
-    const float4 v1 = *reinterpret_cast<const float4*>(P.blk_var + off + 4);
-    const float mu[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    const float va[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  const int hsel = lig % G;   // the head whose score this lane finishes
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const float mu[8] = {m0[it].x, m0[it].y, m0[it].z, m0[it].w, m1[it].x, m1[it].y, m1[it].z, m1[it].w};
+    const float va[8] = {v0[it].x, v0[it].y, v0[it].z, v0[it].w, v1[it].x, v1[it].y, v1[it].z, v1[it].w};
+    float d1 = 0.f, d2 = 0.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float d1 = 0.f, d2 = 0.f;
+      float a = 0.f, c = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        d1 = fmaf(qf[h][i], mu[i], d1);
-        d2 = fmaf(qf[h][i] * va[i], qf[h][i], d2);
+        a = fmaf(qs[h][i], mu[i], a);
+        c = fmaf(qq[h][i], va[i], c);
       }
-      d1 = reduce_sum_lanes<LPT>(d1);
-      d2 = reduce_sum_lanes<LPT>(d2);
-      if (lig == h) {
-        const float sc = sig * d1 + log1pf(half_s2 * d2);
-        P.scores[(static_cast<size_t>(b) * P.Hq + g * G + h) * P.nc_max + c] = sc;
-      }
+      a = reduce_sum_lanes<LPT>(a);
+      c = reduce_sum_lanes<LPT>(c);
+      d1 = (h == hsel) ? a : d1;
+      d2 = (h == hsel) ? c : d2;
+    }
+    const int cidx = c_begin + slot + it * CPP;
+    if (lig < G && page[it] >= 0) {
+      // log(1 + x) via the hardware logarithm: x >= 0, absolute error ~1e-7.
+      P.scores[(static_cast<size_t>(b) * P.Hq + g * G + lig) * P.nc_max + cidx] = d1 + __logf(1.f + d2);
     }
   }
 }
 
 template <typename KV, int D, int G>
-__device__ void readout_part(const DecodeParams& P, int b, int g, int rc) {
-  constexpr int C4 = D / 4;           // float4 columns per row
-  constexpr int RG = kThreads / C4;   // row groups
-  constexpr int RGW = kWave / C4;     // row groups per wavefront
+__device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g, int rc) {
+  constexpr int C4 = D / 4;            // float4 columns per row
+  constexpr int RG = kThreads / C4;    // row groups
+  constexpr int NR = kRoRows / RG;     // rows per thread
+  static_assert(kRoRows % RG == 0, "rows per readout workgroup");
   __shared__ float red[kThreads / kWave][C4][G][4];
   const int tid = threadIdx.x;
   const int col4 = tid % C4;
   const int rg = tid / C4;
   const int pair = b * P.Hkv + g;
-  const int r0 = rc * P.ro_rows;
-  const int r1 = min(r0 + P.ro_rows, D);
+  const int r0 = rc * kRoRows;
   const float* Sp = P.S + static_cast<size_t>(pair) * D * D;
   const size_t qbase = (static_cast<size_t>(b) * P.Hq + g * G) * D;
 
+  float4 srow[NR];
+  float qv[NR][G];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int r = r0 + rg + i * RG;
+    srow[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(r) * D + col4 * 4);
+#pragma unroll
+    for (int h = 0; h < G; ++h) qv[i][h] = q_elem<KV>(P.q, qbase + static_cast<size_t>(h) * D + r);
+  }
   float acc[G][4];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h) {
+    acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[h][j] = 0.f;
-
-  for (int r = r0 + rg; r < r1; r += RG) {
-    const float4 s = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(r) * D + col4 * 4);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float qv = q_elem<KV>(P.q, qbase + static_cast<size_t>(h) * D + r);
-      acc[h][0] = fmaf(qv, s.x, acc[h][0]);
-      acc[h][1] = fmaf(qv, s.y, acc[h][1]);
-      acc[h][2] = fmaf(qv, s.z, acc[h][2]);
-      acc[h][3] = fmaf(qv, s.w, acc[h][3]);
+    for (int i = 0; i < NR; ++i) {
+      acc[h][0] = fmaf(qv[i][h], srow[i].x, acc[h][0]);
+      acc[h][1] = fmaf(qv[i][h], srow[i].y, acc[h][1]);
+      acc[h][2] = fmaf(qv[i][h], srow[i].z, acc[h][2]);
+      acc[h][3] = fmaf(qv[i][h], srow[i].w, acc[h][3]);
     }
   }
   // Row groups inside a wavefront sit C4 lanes apart.
 #pragma unroll
-  for (int off = C4; off < kWave; off <<= 1)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[h][j] += __shfl_xor(acc[h][j], off);
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (C4 <= 16) acc[h][j] = pair_sum<16>(acc[h][j]);
+      acc[h][j] = pair_sum<32>(acc[h][j]);
+    }
   const int wave = tid / kWave;
   const int lane = tid % kWave;
   if (lane < C4) {
@@ -218,23 +256,29 @@ __device__ void readout_part(const DecodeParams& P, int b, int g, int rc) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) red[wave][lane][h][j] = acc[h][j];
   }
-  (void)RGW;
   __syncthreads();
   float* ro = P.ro + (static_cast<size_t>(pair) * P.ro_wgs + rc) * G * D;
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int h = idx / D;
     const int c = idx % D;
-    float s = 0.f;
+    float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kThreads / kWave; ++w) s += red[w][c / 4][h][c % 4];
-    ro[idx] = s;
+    for (int w = 0; w < kThreads / kWave; ++w) v += red[w][c / 4][h][c % 4];
+    ro[idx] = v;
   }
   if (tid < G) {
     const int h = tid;
-    const float* zp = P.z + static_cast<size_t>(pair) * D;
-    float s = 0.f;
-    for (int r = r0; r < r1; ++r) s = fmaf(q_elem<KV>(P.q, qbase + static_cast<size_t>(h) * D + r), zp[r], s);
-    P.roz[(static_cast<size_t>(pair) * P.ro_wgs + rc) * G + h] = s;
+    const float* zp = P.z + static_cast<size_t>(pair) * D + r0;
+    float zr[kRoRows], qr[kRoRows];
+#pragma unroll
+    for (int r = 0; r < kRoRows; ++r) {
+      zr[r] = zp[r];
+      qr[r] = q_elem<KV>(P.q, qbase + static_cast<size_t>(h) * D + r0 + r);
+    }
+    float v = 0.f;
+#pragma unroll
+    for (int r = 0; r < kRoRows; ++r) v = fmaf(qr[r], zr[r], v);
+    P.roz[(static_cast<size_t>(pair) * P.ro_wgs + rc) * G + h] = v;
   }
 }
 
@@ -269,9 +313,52 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Union of the group's exact blocks, ascending: blocks below the candidates
+// (sinks), candidates that some head selected or that hold sink or window
+// tokens, and blocks past the candidates (window).  Entry = block index |
+// (mask of the heads that selected it) << 20; the block's page goes to upage.
 template <int G>
-__global__ __launch_bounds__(kWave * G) void k_select(DecodeParams P) {
-  extern __shared__ uint64_t sel_bits[];     // [G][nwords]
+__device__ __forceinline__ void build_union(const DecodeParams& P, int pair, int b, int T, const CandRange& cr,
+                                            int nc, int nwords, const uint64_t* sel_bits, int lane, int hh) {
+  if (hh != 0) return;
+  const int nb = min(ceil_div(T, P.B), P.nblk_max);
+  const int win0 = T - P.W;
+  int cnt = 0;
+  int32_t* ul = P.ulist + static_cast<size_t>(pair) * P.umax;
+  int32_t* up = P.upage + static_cast<size_t>(pair) * P.umax;
+  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  for (int base = 0; base < nb; base += kWave) {
+    const int j = base + lane;
+    bool inc = false;
+    int hm = 0;
+    if (j < nb) {
+      if (nc == 0 || j < cr.lo || j >= cr.lo + nc) {
+        inc = true;
+      } else {
+        const int c = j - cr.lo;
+#pragma unroll
+        for (int x = 0; x < G; ++x)
+          hm |= static_cast<int>((sel_bits[static_cast<size_t>(x) * nwords + (c >> 6)] >> (c & 63)) & 1ull) << x;
+        const bool overlap = (j * P.B < P.ns) || ((j + 1) * P.B > win0);
+        inc = hm != 0 || overlap;
+      }
+    }
+    const uint64_t im = __ballot(inc);
+    const int pos = cnt + __popcll(im & lanes_below(lane));
+    if (inc && pos < P.umax) {
+      ul[pos] = j | (hm << 20);
+      up[pos] = bt[j];
+    }
+    cnt += __popcll(im);
+  }
+  if (lane == 0) P.ucount[pair] = min(cnt, P.umax);
+}
+
+template <int G>
+__global__ __launch_bounds__(kWave * G) void k_select_generic(DecodeParams P) {
+  // Dynamic LDS: per-head selection bitmaps [G][nwords] (uint64), then, when
+  // they fit, the per-head order keys [G][nc_max] (uint32).
+  extern __shared__ uint64_t dyn_lds[];
   __shared__ uint32_t hist[G][256];
   const int pair = blockIdx.x;
   const int b = pair / P.Hkv;
@@ -285,35 +372,43 @@ __global__ __launch_bounds__(kWave * G) void k_select(DecodeParams P) {
   const int h = g * G + hh;
   const int k = P.top_k;
   const float* sc = P.scores + (static_cast<size_t>(b) * P.Hq + h) * P.nc_max;
-  uint64_t* bits = sel_bits + static_cast<size_t>(hh) * nwords;
+  uint64_t* bits = dyn_lds + static_cast<size_t>(hh) * nwords;
+  const bool staged = P.keys_staged != 0;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(dyn_lds + static_cast<size_t>(G) * nwords) +
+                   static_cast<size_t>(hh) * P.nc_max;
+  if (staged) {
+#pragma unroll 4
+    for (int i = lane; i < nc; i += kWave) keys[i] = f32_order_key(sc[i]);
+  }
+  __syncthreads();
+  auto key_at = [&](int i) -> uint32_t { return staged ? keys[i] : f32_order_key(sc[i]); };
 
   const bool take_all = k >= nc;
   const bool take_none = (k <= 0) || (nc == 0);
-  // Threshold key (32-bit order key of the k-th best score) and how many of
-  // the candidates equal to it are taken (lowest indices first).
+  // Threshold key (order key of the k-th best score) and how many of the
+  // candidates equal to it are taken (lowest indices first).
   uint32_t prefix = 0, mask = 0;
   int rem = k;
   int shift = 0;
   if (!take_all && !take_none) {
     uint32_t kmin = 0xffffffffu, kmax = 0u;
     for (int i = lane; i < nc; i += kWave) {
-      const uint32_t key = f32_order_key(sc[i]);
+      const uint32_t key = key_at(i);
       kmin = min(kmin, key);
       kmax = max(kmax, key);
     }
     kmin = wave_min_u32(kmin);
     kmax = wave_max_u32(kmax);
     const uint32_t diff = kmin ^ kmax;
-    shift = diff ? 32 - __clz(diff) : 0;          // low bits that still vary
+    shift = diff ? 32 - __clz(static_cast<int>(diff)) : 0;   // low bits that still vary
     mask = (shift == 32) ? 0u : ~((1u << shift) - 1u);
     prefix = kmax & mask;
   }
   for (int pass = 0; pass < 4; ++pass) {
     const bool active = shift > 0;
-    int nb = 0;
     uint32_t dmask = 0;
     if (active) {
-      nb = min(8, shift);
+      const int nb = min(8, shift);
       shift -= nb;
       dmask = (1u << nb) - 1u;
     }
@@ -323,7 +418,7 @@ __global__ __launch_bounds__(kWave * G) void k_select(DecodeParams P) {
     __syncthreads();
     if (active) {
       for (int i = lane; i < nc; i += kWave) {
-        const uint32_t key = f32_order_key(sc[i]);
+        const uint32_t key = key_at(i);
         if ((key & mask) == prefix) atomicAdd(&hist[hh][(key >> shift) & dmask], 1u);
       }
     }
@@ -369,22 +464,18 @@ __global__ __launch_bounds__(kWave * G) void k_select(DecodeParams P) {
   for (int base = 0; base < nwords * 64; base += 64) {
     const int i = base + lane;
     const bool valid = i < nc;
-    bool sel = false;
-    if (valid && !take_none) {
-      if (take_all) {
-        sel = true;
-      } else {
-        const uint32_t key = f32_order_key(sc[i]);
-        const bool eq = key == thr;
-        const uint64_t eqm = __ballot(eq);
-        const int eqrank = neq + __popcll(eqm & lanes_below(lane));
-        sel = key > thr || (eq && eqrank < rem);
-      }
-    }
-    if (!take_all && !take_none) {
-      // Keep the tie count in step across lanes (ballot from every lane).
-      const uint32_t key = valid ? f32_order_key(sc[i]) : 0u;
-      neq += __popcll(__ballot(valid && key == thr));
+    const uint32_t key = valid ? key_at(i) : 0u;
+    bool sel;
+    if (take_none) {
+      sel = false;
+    } else if (take_all) {
+      sel = valid;
+    } else {
+      const bool eq = valid && key == thr;
+      const uint64_t eqm = __ballot(eq);
+      const int eqrank = neq + __popcll(eqm & lanes_below(lane));
+      sel = valid && (key > thr || (eq && eqrank < rem));
+      neq += __popcll(eqm);
     }
     const uint64_t sm = __ballot(sel);
     const int pos = nsel + __popcll(sm & lanes_below(lane));
@@ -396,65 +487,210 @@ __global__ __launch_bounds__(kWave * G) void k_select(DecodeParams P) {
     for (int j = nsel + lane; j < k; j += kWave) out[j] = -1;
   __syncthreads();
 
-  // Union of the group's exact blocks, ascending: blocks below the
-  // candidates (sinks), candidates that some head selected or that hold sink
-  // or window tokens, and blocks past the candidates (window).
-  if (hh == 0) {
-    const int nb = min(ceil_div(T, P.B), P.nblk_max);
-    const int win0 = T - P.W;
-    int cnt = 0;
-    int32_t* ul = P.ulist + static_cast<size_t>(pair) * P.umax;
-    for (int base = 0; base < nb; base += kWave) {
-      const int j = base + lane;
-      bool inc = false;
-      int hm = 0;
-      if (j < nb) {
-        if (nc == 0 || j < cr.lo || j >= cr.lo + nc) {
-          inc = true;
-        } else {
-          const int c = j - cr.lo;
+  build_union<G>(P, pair, b, T, cr, nc, nwords, dyn_lds, lane, hh);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront (DPP row shifts,
+// then row broadcasts 15 and 31 across rows).
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
+  auto add = [](uint32_t x, int y) { return x + static_cast<uint32_t>(y); };
+  v = add(v, __builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, true));   // row_shr:1
+  v = add(v, __builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, true));   // row_shr:2
+  v = add(v, __builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, true));   // row_shr:4
+  v = add(v, __builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, true));   // row_shr:8
+  v = add(v, __builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = add(v, __builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return v;
+}
+
+// Top-k with the order keys of one head held in registers: lane l holds
+// candidates l, l + 64, ..., l + 64 (KPL - 1).  A radix select over the
+// 32-bit order keys (8-bit digits, skipping the bits every key shares) finds
+// the k-th largest key with a histogram private to the wavefront, so no
+// workgroup barrier is needed until the union step.
+template <int G, int KPL>
+__global__ __launch_bounds__(kWave * G) void k_select(DecodeParams P) {
+  extern __shared__ uint64_t dyn_lds[];   // [G][nwords] selection bitmaps
+  __shared__ __attribute__((aligned(16))) uint32_t hist[G][256];
+  const int pair = blockIdx.x;
+  const int b = pair / P.Hkv;
+  const int g = pair % P.Hkv;
+  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
+  const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
+  const int nc = min(cr.count, P.nc_max);
+  const int nwords = (P.nc_max + 63) / 64;
+  const int hh = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int h = g * G + hh;
+  const int k = P.top_k;
+  const float* sc = P.scores + (static_cast<size_t>(b) * P.Hq + h) * P.nc_max;
+  uint64_t* bits = dyn_lds + static_cast<size_t>(hh) * nwords;
+
+  uint32_t key[KPL];
+  uint32_t valid = 0;   // bit j: slot j holds a candidate
 #pragma unroll
-          for (int x = 0; x < G; ++x)
-            hm |= static_cast<int>((sel_bits[static_cast<size_t>(x) * nwords + (c >> 6)] >> (c & 63)) & 1ull) << x;
-          const bool overlap = (j * P.B < P.ns) || ((j + 1) * P.B > win0);
-          inc = hm != 0 || overlap;
+  for (int j = 0; j < KPL; ++j) {
+    const int c = lane + kWave * j;
+    const float v = sc[min(c, max(nc - 1, 0))];
+    key[j] = f32_order_key(v);
+    valid |= (c < nc ? 1u : 0u) << j;
+  }
+  const bool take_all = k >= nc;
+  const bool take_none = (k <= 0) || (nc == 0);
+  uint32_t thr = 0;
+  int rem = k;
+  if (!take_all && !take_none) {
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      if ((valid >> j) & 1) {
+        kmin = min(kmin, key[j]);
+        kmax = max(kmax, key[j]);
+      }
+    }
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    const uint32_t diff = kmin ^ kmax;
+    int shift = diff ? 32 - __clz(static_cast<int>(diff)) : 0;   // low bits that still vary
+    uint32_t mask = (shift == 32) ? 0u : ~((1u << shift) - 1u);
+    uint32_t prefix = kmax & mask;
+    uint4* hrow = reinterpret_cast<uint4*>(&hist[hh][4 * lane]);
+    while (shift > 0) {
+      const int nb = min(8, shift);
+      shift -= nb;
+      const uint32_t dmask = (1u << nb) - 1u;
+      *hrow = make_uint4(0, 0, 0, 0);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+      for (int j = 0; j < KPL; ++j)
+        if (((valid >> j) & 1) && (key[j] & mask) == prefix) atomicAdd(&hist[hh][(key[j] >> shift) & dmask], 1u);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const uint4 c4 = *hrow;
+      const uint32_t mine = c4.x + c4.y + c4.z + c4.w;
+      const uint32_t incl = wave_scan_incl(mine);
+      const uint32_t total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1));
+      const uint32_t suffix = total - incl + mine;   // keys whose digit >= 4 * lane
+      const uint32_t above = suffix - mine;          // keys whose digit > 4 * lane + 3
+      const bool here = above < static_cast<uint32_t>(rem) && static_cast<uint32_t>(rem) <= suffix;
+      int digit = 0, rem_here = rem;
+      if (here) {   // the crossing bin is one of this lane's four, scanned from the top
+        uint32_t acc = above;
+        bool found = false;
+        const uint32_t cs[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (!found && acc + cs[j] >= static_cast<uint32_t>(rem)) {
+            digit = 4 * lane + j;
+            rem_here = rem - static_cast<int>(acc);
+            found = true;
+          }
+          acc += cs[j];
         }
       }
-      const uint64_t im = __ballot(inc);
-      const int pos = cnt + __popcll(im & lanes_below(lane));
-      if (inc && pos < P.umax) ul[pos] = j | (hm << 20);
-      cnt += __popcll(im);
+      const uint64_t hm = __ballot(here);
+      const int src = __ffsll(static_cast<unsigned long long>(hm)) - 1;
+      digit = __builtin_amdgcn_readlane(digit, src);
+      rem = __builtin_amdgcn_readlane(rem_here, src);
+      prefix |= static_cast<uint32_t>(digit) << shift;
+      mask |= dmask << shift;
     }
-    if (lane == 0) P.ucount[pair] = min(cnt, P.umax);
+    thr = prefix;
   }
+
+  // Ascending output and per-head selection bitmap.
+  int nsel = 0, neq = 0;
+  int32_t* out = P.sel_idx ? P.sel_idx + (static_cast<size_t>(b) * P.Hq + h) * k : nullptr;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const bool vj = (valid >> j) & 1;
+    bool sel;
+    if (take_none) {
+      sel = false;
+    } else if (take_all) {
+      sel = vj;
+    } else {
+      const bool eq = vj && key[j] == thr;
+      const uint64_t eqm = __ballot(eq);
+      const int eqrank = neq + __popcll(eqm & lanes_below(lane));
+      sel = vj && (key[j] > thr || (eq && eqrank < rem));
+      neq += __popcll(eqm);
+    }
+    const uint64_t sm = __ballot(sel);
+    const int pos = nsel + __popcll(sm & lanes_below(lane));
+    if (sel && out && pos < k) out[pos] = cr.lo + lane + kWave * j;
+    nsel += __popcll(sm);
+    if (lane == 0 && j < nwords) bits[j] = sm;
+  }
+  if (out)
+    for (int j = nsel + lane; j < k; j += kWave) out[j] = -1;
+  __syncthreads();
+  build_union<G>(P, pair, b, T, cr, nc, nwords, dyn_lds, lane, hh);
 }
 
 // ---------------------------------------------------------------------------
 // 3. Split-K exact attention over the union + exact tokens' linear sums
 // ---------------------------------------------------------------------------
-template <typename KV, int D, int G>
-__global__ __launch_bounds__(kThreads) void k_attend(DecodeParams P) {
+// A workgroup walks its split in units of 64 token rows (one block when B is
+// 64, a slice of one when B is larger, several blocks when B is smaller).
+// Each unit takes three passes:
+//   dot      lanes form groups of D/8 lanes, each lane holding 8 channels of
+//            one row (a 16-byte load for bf16); the group's dot product with
+//            every active query head goes to LDS;
+//   softmax  one wavefront per head takes the 64 scores at once (one row per
+//            lane): running maximum, exponentials and the first-order weights
+//            (1 + s) are computed once per row and published in LDS;
+//   fma      every lane accumulates its 8 channels of p v and (1 + s) v.
+// All lanes share one running maximum per head, so the final combine is a
+// plain sum.  The next unit's rows are loaded into a second register buffer
+// before the current unit's barriers, so they are in flight while it is
+// processed.  For B >= 64 a unit lies in one page: its page, first token and
+// selection mask are wavefront-uniform and each lane's row offset is fixed.
+template <typename KV, int D, int G, bool BIG>
+__global__ __launch_bounds__(kThreads, (G <= 4 ? 3 : 1)) void k_attend(DecodeParams P) {
   constexpr int LPT = D / 8;             // lanes per token row
   constexpr int NGRP = kThreads / LPT;   // token groups per workgroup
-  constexpr int U = 4;                   // tokens per group per step
-  __shared__ float red[kThreads / kWave][G][2 * D + 4];
+  constexpr int U = kUnit / NGRP;        // rows per group per unit
+  constexpr int NW = kThreads / kWave;
+  constexpr int kAll = (1 << G) - 1;
+  static_assert(kUnit == kWave, "softmax pass maps one row to one lane");
+  __shared__ float s_lds[G][kUnit];
+  __shared__ float2 pw_lds[G][kUnit];
+  __shared__ float scale_lds[G];
+  __shared__ float red[NW][G][2 * D];
+  __shared__ float mll[G][4];
 
+  // Split s of a (sequence, kv head) takes union entries s, s + S, s + 2S, ...
+  // (S = max_split), so window and sink blocks, which every head of the
+  // group needs, spread over the splits instead of piling into the last one.
+  // The count and the candidate entries are fetched in one round trip.
   const int pair = blockIdx.x / P.max_split;
   const int split = blockIdx.x % P.max_split;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int ent_at = split + lane * P.max_split;   // this lane's candidate entry
+  const bool ent_in = lane < P.bps && ent_at < P.umax;
+  const size_t ent_off = static_cast<size_t>(pair) * P.umax + (ent_in ? ent_at : 0);
   const int count = min(P.ucount[pair], P.umax);
-  const int e0 = split * P.bps;
-  if (e0 >= count) return;
-  const int e1 = min(e0 + P.bps, count);
+  int my_ent = P.ulist[ent_off];
+  int my_page = P.upage[ent_off];
+  if (split >= count) return;
+  const int ne = min(P.bps, ceil_div(count - split, P.max_split));
+  if (!(ent_in && lane < ne)) {
+    my_ent = 0;
+    my_page = -1;
+  }
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
   const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
   const int B = P.B;
   const int ns = P.ns;
   const int win0 = T - P.W;
-  const float sig = P.sigma;
-  const int tid = threadIdx.x;
   const int lig = tid % LPT;
   const int grp = tid / LPT;
+  const int upb = BIG ? B / kUnit : 1;   // units per block
+  const int epu = BIG ? 1 : kUnit / B;   // blocks per unit
+  const int nu = BIG ? ne * upb : ceil_div(ne, epu);
 
   QReg<KV> qr[G];
 #pragma unroll
@@ -462,195 +698,305 @@ __global__ __launch_bounds__(kThreads) void k_attend(DecodeParams P) {
     qr[h].load(reinterpret_cast<const char*>(P.q) +
                ((static_cast<size_t>(b) * P.Hq + g * G + h) * D + lig * 8) * KV::kBytes);
 
-  float m[G], l[G], ld[G], acc[G][8], lacc[G][8];
+  float acc[G][8], lacc[G][8];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-    ld[h] = 0.f;
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc[h][i] = 0.f;
-      lacc[h][i] = 0.f;
-    }
+    for (int i = 0; i < 8; ++i) acc[h][i] = lacc[h][i] = 0.f;
+  // Softmax state of the heads this wavefront owns (h % NW == wave): the
+  // running maximum (uniform) and per-lane partial sums of p and 1 + s.
+  constexpr int OWN = (G + NW - 1) / NW;   // heads owned per wavefront
+  float m_run[OWN], l_lane[OWN], ld_lane[OWN];
+#pragma unroll
+  for (int o = 0; o < OWN; ++o) {
+    m_run[o] = kNegInf;
+    l_lane[o] = 0.f;
+    ld_lane[o] = 0.f;
   }
 
   const char* kp = reinterpret_cast<const char*>(P.k_pages);
   const char* vp = reinterpret_cast<const char*>(P.v_pages);
-  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
-  const int32_t* ul = P.ulist + static_cast<size_t>(pair) * P.umax;
-  constexpr int kAll = (1 << G) - 1;
-  const int nblk = ceil_div(T, B);
+  const size_t head_tile = static_cast<size_t>(B) * D * KV::kBytes;   // bytes of one (page, head) tile
+  int lane_off[U];   // byte offset of this lane's row i inside a 64-row slice
+#pragma unroll
+  for (int i = 0; i < U; ++i) lane_off[i] = ((grp + NGRP * i) * D + lig * 8) * KV::kBytes;
 
-  for (int e = e0; e < e1; ++e) {
-    const int ent = ul[e];
-    const int blk = ent & 0xFFFFF;
-    if (blk >= nblk) continue;
-    const int fmask = (ent >> 20) & kAll;
-    const int t0 = blk * B;
-    const bool sw = (t0 < ns) || (t0 + B > win0);
-    const int active = fmask | (sw ? kAll : 0);
-    const int page = bt[blk];
-    const size_t row0 = (static_cast<size_t>(page) * P.Hkv + g) * B;
-    for (int tt = 0; tt < B; tt += NGRP * U) {
-      Row8<KV> kr[U], vr[U];
-      int tok[U];
-      bool valid[U];
+  struct Unit {
+    Row8<KV> k[U], v[U];
+    int tok[U];    // token position of row i, or -1 when absent
+    int fm;        // B >= 64: heads that selected the unit's block (uniform)
+    int fmr[U];    // B < 64: heads that selected row i's block
+    int active;    // heads any row of the unit needs (uniform)
+  };
+  // Issues the loads of unit u (any u: past the end it reads valid rows of
+  // the split's first page and marks every row absent).
+  auto fetch = [&](int u, Unit& x) __attribute__((always_inline)) {
+    const bool live = u < nu;
+    if constexpr (BIG) {
+      const int e = live ? u / upb : 0;
+      const int sub = live ? u - e * upb : 0;
+      const int ent = __builtin_amdgcn_readlane(my_ent, e);
+      const int page = max(__builtin_amdgcn_readlane(my_page, e), 0);
+      const int t0 = (ent & 0xFFFFF) * B + sub * kUnit;
+      const size_t base = (static_cast<size_t>(page) * P.Hkv + g) * head_tile +
+                          static_cast<size_t>(sub) * kUnit * D * KV::kBytes;
+      const bool ok = live && __builtin_amdgcn_readlane(my_page, e) >= 0;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int r = tt + grp + NGRP * u;
-        tok[u] = t0 + r;
-        valid[u] = (r < B) && (tok[u] < T);
-        if (valid[u]) {
-          const size_t off = ((row0 + r) * D + lig * 8) * KV::kBytes;
-          kr[u].load(kp + off);
-          vr[u].load(vp + off);
-        } else {
-          kr[u].zero();
-          vr[u].zero();
-        }
+      for (int i = 0; i < U; ++i) {
+        const int t = t0 + grp + NGRP * i;
+        x.tok[i] = (ok && t < T) ? t : -1;
+        x.k[i].load(kp + base + lane_off[i]);
+        x.v[i].load(vp + base + lane_off[i]);
       }
-      float vf[U][8];
+      x.fm = (ent >> 20) & kAll;
+      const bool sw = t0 < ns || t0 + kUnit > win0;
+      x.active = ok ? (x.fm | (sw ? kAll : 0)) : 0;
+    } else {
+      int active = 0;
 #pragma unroll
-      for (int u = 0; u < U; ++u) vr[u].to_f32(vf[u]);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        if (!((active >> h) & 1)) continue;
-        const bool full = (fmask >> h) & 1;
-        float s[U];
-        bool inc[U];
-        float mx = kNegInf;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          s[u] = sig * reduce_sum_lanes<LPT>(qr[h].dot(kr[u]));
-          inc[u] = valid[u] && (full || tok[u] < ns || tok[u] >= win0);
-          if (inc[u]) mx = fmaxf(mx, s[u]);
-        }
-        const float mnew = fmaxf(m[h], mx);
-        if (mnew > m[h]) {
-          const float c = (m[h] == kNegInf) ? 0.f : fast_exp(m[h] - mnew);
-          l[h] *= c;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][i] *= c;
-          m[h] = mnew;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float p = inc[u] ? fast_exp(s[u] - m[h]) : 0.f;
-          const float w = inc[u] ? 1.f + s[u] : 0.f;
-          l[h] += p;
-          ld[h] += w;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            acc[h][i] = fmaf(p, vf[u][i], acc[h][i]);
-            lacc[h][i] = fmaf(w, vf[u][i], lacc[h][i]);
+      for (int i = 0; i < U; ++i) {
+        const int r = grp + NGRP * i;
+        const int e = live ? u * epu + r / B : 0;
+        const int row = r % B;
+        const int ent = __shfl(my_ent, e & (kWave - 1));
+        const int page = __shfl(my_page, e & (kWave - 1));
+        const int t = (ent & 0xFFFFF) * B + row;
+        const bool ok = live && e < ne && page >= 0 && t < T;
+        x.tok[i] = ok ? t : -1;
+        x.fmr[i] = (ent >> 20) & kAll;
+        const size_t off = (((static_cast<size_t>(max(page, 0)) * P.Hkv + g) * B + row) * D + lig * 8) * KV::kBytes;
+        x.k[i].load(kp + off);
+        x.v[i].load(vp + off);
+      }
+      // Per-row selection masks differ across the unit; the unit's active set
+      // is the union over its blocks.
+      if (live) {
+        for (int xx = 0; xx < epu; ++xx) {
+          const int e = u * epu + xx;
+          if (e < ne) {
+            const int ent = __builtin_amdgcn_readlane(my_ent, e);
+            const int t0 = (ent & 0xFFFFF) * B;
+            const bool sw = t0 < ns || t0 + B > win0;
+            active |= ((ent >> 20) & kAll) | (sw ? kAll : 0);
           }
         }
       }
+      x.fm = 0;
+      x.active = active;
     }
-  }
+  };
 
-  // Combine the token groups of each wavefront (they sit LPT lanes apart).
+  auto process = [&](Unit& x) __attribute__((always_inline)) {
+    const int active = x.active;
+    bool valid[U], vsw[U];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int off = LPT; off < kWave; off <<= 1) {
-      const float mo = __shfl_xor(m[h], off);
-      const float mn = fmaxf(m[h], mo);
-      const float ca = (m[h] == kNegInf) ? 0.f : fast_exp(m[h] - mn);
-      const float cb = (mo == kNegInf) ? 0.f : fast_exp(mo - mn);
-      l[h] = l[h] * ca + __shfl_xor(l[h], off) * cb;
-      ld[h] += __shfl_xor(ld[h], off);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acc[h][i] = acc[h][i] * ca + __shfl_xor(acc[h][i], off) * cb;
-        lacc[h][i] += __shfl_xor(lacc[h][i], off);
-      }
-      m[h] = mn;
+    for (int i = 0; i < U; ++i) {
+      valid[i] = x.tok[i] >= 0;
+      vsw[i] = valid[i] && (x.tok[i] < ns || x.tok[i] >= win0);
     }
-  }
-  const int wave = tid / kWave;
-  const int lane = tid % kWave;
-  if (lane < LPT) {
+    // ---- dot pass: raw dot products (scaled in the softmax pass)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      if (!((active >> h) & 1)) continue;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        red[wave][h][lane * 8 + i] = acc[h][i];
-        red[wave][h][D + lane * 8 + i] = lacc[h][i];
+      for (int i = 0; i < U; ++i) {
+        const float d = reduce_sum_lanes<LPT>(qr[h].dot(x.k[i]));
+        bool inc;
+        if constexpr (BIG) {
+          inc = ((x.fm >> h) & 1) ? valid[i] : vsw[i];
+        } else {
+          inc = vsw[i] || (valid[i] && ((x.fmr[i] >> h) & 1));
+        }
+        if (lig == 0) s_lds[h][grp + NGRP * i] = inc ? d : kNegInf;
       }
+    }
+    __syncthreads();
+    // ---- softmax pass: wavefront w owns heads w, w + NW, ...
+#pragma unroll
+    for (int o = 0; o < OWN; ++o) {
+      const int h = wave + o * NW;
+      if (h >= G || !((active >> h) & 1)) continue;
+      const float sv = P.sigma * s_lds[h][lane];
+      const bool inc = sv != kNegInf;
+      const float mnew = fmaxf(m_run[o], wave_max(sv));
+      const float c = (m_run[o] == kNegInf) ? 0.f : (mnew == m_run[o] ? 1.f : fast_exp(m_run[o] - mnew));
+      const float pv = inc ? fast_exp(sv - mnew) : 0.f;
+      const float wv = inc ? 1.f + sv : 0.f;
+      pw_lds[h][lane] = make_float2(pv, wv);
+      l_lane[o] = fmaf(l_lane[o], c, pv);
+      ld_lane[o] += wv;
+      m_run[o] = mnew;
+      if (lane == 0) scale_lds[h] = c;
+    }
+    __syncthreads();
+    // ---- fma pass
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+      if (!valid[i]) x.v[i].zero();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (!((active >> h) & 1)) continue;
+      const float c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(scale_lds[h])));
+      if (c != 1.f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[h][j] *= c;
+      }
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const float2 pw = pw_lds[h][grp + NGRP * i];
+        float vf[8];
+        x.v[i].to_f32(vf);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          acc[h][j] = fmaf(pw.x, vf[j], acc[h][j]);
+          lacc[h][j] = fmaf(pw.y, vf[j], lacc[h][j]);
+        }
+      }
+    }
+  };
+
+  Unit ua, ub;
+  fetch(0, ua);
+  for (int u = 0; u < nu; u += 2) {
+    fetch(u + 1, ub);
+    process(ua);
+    if (u + 1 >= nu) break;
+    fetch(u + 2, ua);
+    process(ub);
+  }
+
+  // ---- combine: plain sums over the groups of a wavefront, then over waves.
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (LPT <= 8) {
+        acc[h][j] = pair_sum<8>(acc[h][j]);
+        lacc[h][j] = pair_sum<8>(lacc[h][j]);
+      }
+      acc[h][j] = pair_sum<32>(pair_sum<16>(acc[h][j]));
+      lacc[h][j] = pair_sum<32>(pair_sum<16>(lacc[h][j]));
+    }
+  if (lane < LPT) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        red[wave][h][lane * 8 + j] = acc[h][j];
+        red[wave][h][D + lane * 8 + j] = lacc[h][j];
+      }
+  }
+#pragma unroll
+  for (int o = 0; o < OWN; ++o) {
+    const int h = wave + o * NW;
+    if (h < G) {
+      const float lsum = wave_sum(l_lane[o]);
+      const float ldsum = wave_sum(ld_lane[o]);
       if (lane == 0) {
-        red[wave][h][2 * D] = m[h];
-        red[wave][h][2 * D + 1] = l[h];
-        red[wave][h][2 * D + 2] = ld[h];
+        mll[h][0] = m_run[o];
+        mll[h][1] = lsum;
+        mll[h][2] = ldsum;
       }
     }
   }
   __syncthreads();
-  constexpr int NW = kThreads / kWave;
   float* outp = P.part + (static_cast<size_t>(pair) * P.max_split + split) * G * P.pstride;
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int h = idx / D;
-    const int c = idx % D;
-    float M = kNegInf;
+  for (int idx = tid; idx < G * 2 * D; idx += kThreads) {
+    const int h = idx / (2 * D);
+    const int c = idx % (2 * D);
+    float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, red[w][h][2 * D]);
-    float a = 0.f, la = 0.f, ls = 0.f, lds = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = red[w][h][2 * D];
-      const float f = (mw == kNegInf) ? 0.f : fast_exp(mw - M);
-      a = fmaf(f, red[w][h][c], a);
-      la += red[w][h][D + c];
-      ls = fmaf(f, red[w][h][2 * D + 1], ls);
-      lds += red[w][h][2 * D + 2];
-    }
-    float* o = outp + static_cast<size_t>(h) * P.pstride;
-    o[4 + c] = a;
-    o[4 + D + c] = la;
-    if (c == 0) {
-      o[0] = M;
-      o[1] = ls;
-      o[2] = lds;
-      o[3] = 0.f;
-    }
+    for (int w = 0; w < NW; ++w) v += red[w][h][c];
+    outp[static_cast<size_t>(h) * P.pstride + 4 + c] = v;
+  }
+  if (tid < G) {
+    float* o = outp + static_cast<size_t>(tid) * P.pstride;
+    o[0] = mll[tid][0];
+    o[1] = mll[tid][1];
+    o[2] = mll[tid][2];
+    o[3] = 0.f;
   }
 }
 
 // ---------------------------------------------------------------------------
 // 4. Merge of the splits and the residual linear part
 // ---------------------------------------------------------------------------
+// One workgroup per (sequence, query head); NP = 256 / D lanes share a
+// channel and walk the splits with a running maximum, then combine.
 template <int D, int G>
-__global__ __launch_bounds__(128) void k_merge(DecodeParams P) {
+__global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
+  constexpr int NP = kThreads / D;
+  __shared__ float part_m[NP][D], part_num[NP][D], part_den[NP][D], part_lnum[NP][D], part_lden[NP][D];
   const int bh = blockIdx.x;
   const int b = bh / P.Hq;
   const int h = bh % P.Hq;
   const int g = h / G;
   const int hh = h % G;
   const int pair = b * P.Hkv + g;
-  const int c = threadIdx.x;
-  if (c >= D) return;
+  const int tid = threadIdx.x;
+  const int c = tid % D;
+  const int pp = tid / D;
   const int count = min(P.ucount[pair], P.umax);
-  const int nsplit = ceil_div(count, P.bps);
-  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
+  const int nsplit = min(count, P.max_split);   // split s holds entries s, s + max_split, ...
   const size_t sstride = static_cast<size_t>(G) * P.pstride;
   const float* pb = P.part + (static_cast<size_t>(pair) * P.max_split * G + hh) * P.pstride;
 
   float M = 0.f;   // the linear part is in unshifted units (log-scale 0)
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pb[s * sstride]);
   float num = 0.f, den = 0.f, lnum = 0.f, lden = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* ps = pb + s * sstride;
-    const float ms = ps[0];
-    const float f = (ms == kNegInf) ? 0.f : __expf(ms - M);
-    num = fmaf(f, ps[4 + c], num);
-    den = fmaf(f, ps[1], den);
-    lnum += ps[4 + D + c];
-    lden += ps[2];
+  constexpr int NPC = 8;   // splits per lane whose loads are issued together
+  for (int s0 = pp; s0 < nsplit; s0 += NP * NPC) {
+    float ms[NPC], ls[NPC], lds[NPC], a[NPC], la[NPC];
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      const int sidx = min(s0 + i * NP, nsplit - 1);
+      const float* ps = pb + sidx * sstride;
+      ms[i] = ps[0];
+      ls[i] = ps[1];
+      lds[i] = ps[2];
+      a[i] = ps[4 + c];
+      la[i] = ps[4 + D + c];
+    }
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      if (s0 + i * NP >= nsplit) break;
+      lnum += la[i];
+      lden += lds[i];
+      if (ms[i] != kNegInf) {
+        if (ms[i] > M) {
+          const float r = __expf(M - ms[i]);
+          num *= r;
+          den *= r;
+          M = ms[i];
+        }
+        const float f = __expf(ms[i] - M);
+        num = fmaf(f, a[i], num);
+        den = fmaf(f, ls[i], den);
+      }
+    }
   }
+  part_m[pp][c] = M;
+  part_num[pp][c] = num;
+  part_den[pp][c] = den;
+  part_lnum[pp][c] = lnum;
+  part_lden[pp][c] = lden;
+  __syncthreads();
+  if (pp != 0) return;
+#pragma unroll
+  for (int x = 1; x < NP; ++x) M = fmaxf(M, part_m[x][c]);
+  num = den = lnum = lden = 0.f;
+#pragma unroll
+  for (int x = 0; x < NP; ++x) {
+    const float f = __expf(part_m[x][c] - M);
+    num = fmaf(f, part_num[x][c], num);
+    den = fmaf(f, part_den[x][c], den);
+    lnum += part_lnum[x][c];
+    lden += part_lden[x][c];
+  }
+  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
   const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
   if (P.linear_tail && P.top_k < min(cr.count, P.nc_max)) {
     float ro = 0.f, rz = 0.f;
+#pragma unroll 8
     for (int rc = 0; rc < P.ro_wgs; ++rc) {
       ro += P.ro[((static_cast<size_t>(pair) * P.ro_wgs + rc) * G + hh) * D + c];
       rz += P.roz[(static_cast<size_t>(pair) * P.ro_wgs + rc) * G + hh];
@@ -678,25 +1024,38 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
   if (rec) rec(ctx, 1, "select");
   {
     const int nwords = (p.nc_max + 63) / 64;
-    const size_t lds = static_cast<size_t>(G) * nwords * sizeof(uint64_t);
-    if (lds > 32 * 1024) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select<G>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((k_select<G>), dim3(pairs), dim3(kWave * G), lds, stream, P);
-    hipError_t e = launch_status("k_select");
+    const size_t bits = static_cast<size_t>(G) * nwords * sizeof(uint64_t);
+    const int kpl = ceil_div(std::max(p.nc_max, 1), kWave);
+    auto go = [&](auto kernel, size_t lds) -> hipError_t {
+      if (lds > 32 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(kernel, dim3(pairs), dim3(kWave * G), lds, stream, P);
+      return launch_status("k_select");
+    };
+    hipError_t e;
+    if (kpl <= 2) e = go(k_select<G, 2>, bits);
+    else if (kpl <= 4) e = go(k_select<G, 4>, bits);
+    else if (kpl <= 8) e = go(k_select<G, 8>, bits);
+    else if (kpl <= 16) e = go(k_select<G, 16>, bits);
+    else if (kpl <= 32) e = go(k_select<G, 32>, bits);
+    else e = go(k_select_generic<G>, bits + (L.keys_staged ? static_cast<size_t>(G) * p.nc_max * sizeof(uint32_t) : 0));
     if (e != hipSuccess) return e;
   }
   if (rec) rec(ctx, 2, "attend");
   {
-    hipLaunchKernelGGL((k_attend<KV, D, G>), dim3(pairs * L.max_split), dim3(kThreads), 0, stream, P);
+    if (p.B >= kUnit)
+      hipLaunchKernelGGL((k_attend<KV, D, G, true>), dim3(pairs * L.max_split), dim3(kThreads), 0, stream, P);
+    else
+      hipLaunchKernelGGL((k_attend<KV, D, G, false>), dim3(pairs * L.max_split), dim3(kThreads), 0, stream, P);
     hipError_t e = launch_status("k_attend");
     if (e != hipSuccess) return e;
   }
   if (rec) rec(ctx, 3, "merge");
   {
-    hipLaunchKernelGGL((k_merge<D, G>), dim3(p.batch * p.Hq), dim3(128), 0, stream, P);
+    hipLaunchKernelGGL((k_merge<D, G>), dim3(p.batch * p.Hq), dim3(kThreads), 0, stream, P);
     hipError_t e = launch_status("k_merge");
     if (e != hipSuccess) return e;
   }
@@ -723,15 +1082,20 @@ static size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 DecodeLayout decode_layout(const Problem& p) {
   DecodeLayout L{};
   const int pairs = p.batch * p.Hkv;
-  L.score_chunk = 64;
+  L.score_chunk = kScoreChunk;
   L.score_wgs = p.nc_max > 0 ? ceil_div(p.nc_max, L.score_chunk) : 0;
-  L.ro_rows = 16;
+  L.ro_rows = kRoRows;
   L.ro_wgs = p.linear_tail ? p.D / L.ro_rows : 0;
+  {
+    const size_t bits = static_cast<size_t>(p.G) * ((p.nc_max + 63) / 64) * sizeof(uint64_t);
+    const size_t keys = static_cast<size_t>(p.G) * p.nc_max * sizeof(uint32_t);
+    L.keys_staged = (bits + keys) <= 96 * 1024 ? 1 : 0;
+  }
   const int sink_blocks = p.ns / p.B;
   const long sel_blocks = std::min<long>(static_cast<long>(p.G) * p.top_k, p.nc_max);
   const long bound = static_cast<long>(sink_blocks) + sel_blocks + 2 + p.W / p.B + 1;
   L.umax = static_cast<int>(std::max<long>(1, std::min<long>(bound, p.nblk_max)));
-  L.bps = std::max(1, 256 / p.B);
+  L.bps = std::max(1, kUnitsPerWg * kUnit / p.B);
   L.max_split = ceil_div(L.umax, L.bps);
   L.pstride = 2 * p.D + 4;
   size_t off = 0;
@@ -742,6 +1106,8 @@ DecodeLayout decode_layout(const Problem& p) {
   L.off_roz = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(pairs) * std::max(1, L.ro_wgs) * p.G);
   L.off_union = off;
+  off = align_up(off + sizeof(int32_t) * static_cast<size_t>(pairs) * L.umax);
+  L.off_upage = off;
   off = align_up(off + sizeof(int32_t) * static_cast<size_t>(pairs) * L.umax);
   L.off_ucount = off;
   off = align_up(off + sizeof(int32_t) * static_cast<size_t>(pairs));
@@ -770,6 +1136,7 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.ro = reinterpret_cast<float*>(a.ws + L.off_ro);
   P.roz = reinterpret_cast<float*>(a.ws + L.off_roz);
   P.ulist = reinterpret_cast<int32_t*>(a.ws + L.off_union);
+  P.upage = reinterpret_cast<int32_t*>(a.ws + L.off_upage);
   P.ucount = reinterpret_cast<int32_t*>(a.ws + L.off_ucount);
   P.part = reinterpret_cast<float*>(a.ws + L.off_part);
   P.Hq = p.Hq;
@@ -783,10 +1150,9 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.max_seq_len = p.max_seq_len;
   P.nc_max = p.nc_max;
   P.nblk_max = p.nblk_max;
-  P.score_chunk = L.score_chunk;
   P.score_wgs = L.score_wgs;
   P.ro_wgs = L.ro_wgs;
-  P.ro_rows = L.ro_rows;
+  P.keys_staged = L.keys_staged;
   P.umax = L.umax;
   P.bps = L.bps;
   P.max_split = L.max_split;

@@ -38,7 +38,8 @@ struct DecodeLayout {
   int bps;             // union blocks per attention split
   int max_split;       // attention splits per (sequence, kv head)
   int pstride;         // floats per (split, head) partial
-  size_t off_scores, off_ro, off_roz, off_union, off_ucount, off_part, total;
+  int keys_staged;     // select kernel keeps the order keys in LDS
+  size_t off_scores, off_ro, off_roz, off_union, off_upage, off_ucount, off_part, total;
 };
 DecodeLayout decode_layout(const Problem& p);
 

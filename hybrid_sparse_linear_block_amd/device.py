@@ -99,3 +99,48 @@ def config_for(num_q_heads, num_kv_heads, head_dim, block_size, top_k, num_sink,
                kv_dtype: str, scale: float = 0.0) -> Config:
     return Config(num_q_heads, num_kv_heads, head_dim, block_size, top_k, num_sink, window, linear_tail,
                   HSLA_BF16 if kv_dtype == "bf16" else HSLA_F32, scale)
+
+
+class PreparedDecodeStep:
+    """One decode step (append + decode) of a DeviceCache with every C
+    argument marshalled once, so that repeated calls cost one ctypes call per
+    entry point.  Lengths ping-pong between the cache's two length buffers;
+    each call advances the cache by one token."""
+
+    def __init__(self, dc: DeviceCache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                 out: torch.Tensor, sel: Optional[torch.Tensor], stream=None):
+        import ctypes
+
+        from . import hsla_profile, load
+        self.lib = load()
+        self.dc = dc
+        self.keep = (q, k_new, v_new, out, sel)
+        self.cfg = dc.cfg.c()
+        self.pool = dc.pool.c()
+        self.state = dc.state.c()
+        self.stream = (torch.cuda.current_stream() if stream is None else stream).cuda_stream
+        self.q, self.k, self.v = q.data_ptr(), k_new.data_ptr(), v_new.data_ptr()
+        self.out = out.data_ptr()
+        self.sel = sel.data_ptr() if sel is not None else None
+        self.ws = dc.decode_ws.data_ptr()
+        self.ws_bytes = dc.decode_ws.numel()
+        self.lens = [dc.lens[0].data_ptr(), dc.lens[1].data_ptr()]
+        self.byref = ctypes.byref
+        self.prof_type = hsla_profile
+
+    def __call__(self, prof=None) -> None:
+        dc = self.dc
+        assert dc.max_seq_len + 1 <= dc.capacity_len
+        cur, nxt = dc.cur, 1 - dc.cur
+        br = self.byref
+        st = self.lib.hsla_append_token(br(self.cfg), br(self.pool), br(self.state), self.k, self.v,
+                                        self.lens[cur], self.lens[nxt], dc.batch, dc.max_seq_len + 1, self.stream)
+        if st != 0:
+            raise RuntimeError(f"hsla_append_token failed: {st}")
+        dc.cur = nxt
+        dc.host_lens += 1
+        st = self.lib.hsla_decode(br(self.cfg), br(self.pool), br(self.state), self.q, self.lens[nxt], dc.batch,
+                                  dc.max_seq_len, self.out, self.sel, self.ws, self.ws_bytes, self.stream,
+                                  br(prof) if prof is not None else None)
+        if st != 0:
+            raise RuntimeError(f"hsla_decode failed: {st}")
