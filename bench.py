@@ -267,11 +267,12 @@ def main():
         preps[i % R](profs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = [profs[0].names[j].decode() for j in range(nev - 1)]
+    nrec = profs[0].recorded
+    names = [profs[0].names[j].decode() for j in range(nrec - 1)]
     per_kernel = {n: float(np.mean([hip.ms(evs[i][j], evs[i][j + 1]) for i in range(steps)]) * 1e3)
                   for j, n in enumerate(names)}
     per_kernel["append"] = float(np.mean([hip.ms(ev_app[i], evs[i][0]) for i in range(steps)]) * 1e3)
-    gpu_step_us = float(np.mean([hip.ms(ev_app[i], evs[i][nev - 1]) for i in range(steps)]) * 1e3)
+    gpu_step_us = float(np.mean([hip.ms(ev_app[i], evs[i][nrec - 1]) for i in range(steps)]) * 1e3)
 
     # Algorithmic bytes from each replica's selections at its final length.
     per_rep = []

@@ -39,7 +39,11 @@ constexpr float kNegInf = -INFINITY;
 constexpr int kScoreChunk = 64;  // candidates per scoring workgroup
 constexpr int kRoRows = 16;      // rows of S per readout workgroup
 constexpr int kUnit = 64;        // tokens per attention work unit
-constexpr int kUnitsPerWg = 8;   // attention work units per workgroup
+// Attention workgroups per launch: two per compute unit of MI355X (256
+// CUs), so that every CU carries the same number of splits.
+constexpr int kAttendWgsTarget = 2 * 256;
+constexpr size_t kKeysStageBytes = 16 * 1024;   // order keys staged in LDS up to this size
+constexpr size_t kBtStageBytes = 8 * 1024;      // block-table row staged in LDS up to this size
 
 struct DecodeParams {
   const void* k_pages;
@@ -54,18 +58,19 @@ struct DecodeParams {
   const int32_t* seq_lens;
   float* out;
   int32_t* sel_idx;
-  float* scores;
+  uint32_t* keys;   // block-score order keys [batch, Hq, sstride]
   float* ro;
   float* roz;
-  int32_t* ulist;
-  int32_t* upage;
+  int32_t* ulist;   // union entries [pairs, umax]: block | head mask << 20
+  int32_t* upage;   // their pages [pairs, umax]
   int32_t* ucount;
   float* part;
   int Hq, Hkv, B, top_k, ns, W, linear_tail;
   int max_blocks, max_seq_len, nc_max, nblk_max;
   int score_wgs, ro_wgs;
   int umax, bps, max_split, pstride;
-  int keys_staged;
+  int sstride, nwords, keys_staged, bt_staged;
+  SelLayout sl;
   float sigma;
 };
 
@@ -199,7 +204,7 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
     const int cidx = c_begin + slot + it * CPP;
     if (lig < G && page[it] >= 0) {
       // log(1 + x) via the hardware logarithm: x >= 0, absolute error ~1e-7.
-      P.scores[(static_cast<size_t>(b) * P.Hq + g * G + lig) * P.nc_max + cidx] = d1 + __logf(1.f + d2);
+      P.keys[(static_cast<size_t>(b) * P.Hq + g * G + lig) * P.sstride + cidx] = f32_order_key(d1 + __logf(1.f + d2));
     }
   }
 }
@@ -297,197 +302,37 @@ __global__ __launch_bounds__(kThreads) void k_score_readout(DecodeParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. Top-k selection and union of the group's exact blocks
+// 2. Top-k selection and the union of the group's exact blocks
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off)));
-  return v;
+// Every attention workgroup of a (sequence, kv head) recomputes the selection
+// from the block scores (a few KB, cache resident) before it touches K/V:
+// the G heads' top-k blocks (score desc, index asc), the union of the
+// group's exact blocks in ascending block order (SPLA Figure 1(a)), and its
+// own share of that union.  A separate selection kernel would leave every
+// attention workgroup a dependent round trip for the union at its start,
+// which queues behind the K/V loads the first workgroups have already
+// issued; recomputing it costs a few microseconds of arithmetic instead.
+// Wavefront-wide min / max of uint32 without LDS: DPP permutations inside
+// each row of 16 lanes, then the permlane swaps across rows.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  auto dpp = [](uint32_t x, auto ctrl) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), decltype(ctrl)::value, 0xf, 0xf, true));
+  };
+  v = op(v, dpp(v, std::integral_constant<int, 0xB1>{}));    // quad_perm [1,0,3,2]
+  v = op(v, dpp(v, std::integral_constant<int, 0x4E>{}));    // quad_perm [2,3,0,1]
+  v = op(v, dpp(v, std::integral_constant<int, 0x141>{}));   // row_half_mirror
+  v = op(v, dpp(v, std::integral_constant<int, 0x140>{}));   // row_mirror
+  auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r16[0], r16[1]);
+  auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(r32[0], r32[1]);
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off)));
-  return v;
-}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_minmax_u32<false>(v); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_minmax_u32<true>(v); }
 __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-}
-
-// Union of the group's exact blocks, ascending: blocks below the candidates
-// (sinks), candidates that some head selected or that hold sink or window
-// tokens, and blocks past the candidates (window).  Entry = block index |
-// (mask of the heads that selected it) << 20; the block's page goes to upage.
-template <int G>
-__device__ __forceinline__ void build_union(const DecodeParams& P, int pair, int b, int T, const CandRange& cr,
-                                            int nc, int nwords, const uint64_t* sel_bits, int lane, int hh) {
-  if (hh != 0) return;
-  const int nb = min(ceil_div(T, P.B), P.nblk_max);
-  const int win0 = T - P.W;
-  int cnt = 0;
-  int32_t* ul = P.ulist + static_cast<size_t>(pair) * P.umax;
-  int32_t* up = P.upage + static_cast<size_t>(pair) * P.umax;
-  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
-  for (int base = 0; base < nb; base += kWave) {
-    const int j = base + lane;
-    bool inc = false;
-    int hm = 0;
-    if (j < nb) {
-      if (nc == 0 || j < cr.lo || j >= cr.lo + nc) {
-        inc = true;
-      } else {
-        const int c = j - cr.lo;
-#pragma unroll
-        for (int x = 0; x < G; ++x)
-          hm |= static_cast<int>((sel_bits[static_cast<size_t>(x) * nwords + (c >> 6)] >> (c & 63)) & 1ull) << x;
-        const bool overlap = (j * P.B < P.ns) || ((j + 1) * P.B > win0);
-        inc = hm != 0 || overlap;
-      }
-    }
-    const uint64_t im = __ballot(inc);
-    const int pos = cnt + __popcll(im & lanes_below(lane));
-    if (inc && pos < P.umax) {
-      ul[pos] = j | (hm << 20);
-      up[pos] = bt[j];
-    }
-    cnt += __popcll(im);
-  }
-  if (lane == 0) P.ucount[pair] = min(cnt, P.umax);
-}
-
-template <int G>
-__global__ __launch_bounds__(kWave * G) void k_select_generic(DecodeParams P) {
-  // Dynamic LDS: per-head selection bitmaps [G][nwords] (uint64), then, when
-  // they fit, the per-head order keys [G][nc_max] (uint32).
-  extern __shared__ uint64_t dyn_lds[];
-  __shared__ uint32_t hist[G][256];
-  const int pair = blockIdx.x;
-  const int b = pair / P.Hkv;
-  const int g = pair % P.Hkv;
-  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
-  const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
-  const int nc = min(cr.count, P.nc_max);
-  const int nwords = (P.nc_max + 63) / 64;
-  const int hh = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  const int h = g * G + hh;
-  const int k = P.top_k;
-  const float* sc = P.scores + (static_cast<size_t>(b) * P.Hq + h) * P.nc_max;
-  uint64_t* bits = dyn_lds + static_cast<size_t>(hh) * nwords;
-  const bool staged = P.keys_staged != 0;
-  uint32_t* keys = reinterpret_cast<uint32_t*>(dyn_lds + static_cast<size_t>(G) * nwords) +
-                   static_cast<size_t>(hh) * P.nc_max;
-  if (staged) {
-#pragma unroll 4
-    for (int i = lane; i < nc; i += kWave) keys[i] = f32_order_key(sc[i]);
-  }
-  __syncthreads();
-  auto key_at = [&](int i) -> uint32_t { return staged ? keys[i] : f32_order_key(sc[i]); };
-
-  const bool take_all = k >= nc;
-  const bool take_none = (k <= 0) || (nc == 0);
-  // Threshold key (order key of the k-th best score) and how many of the
-  // candidates equal to it are taken (lowest indices first).
-  uint32_t prefix = 0, mask = 0;
-  int rem = k;
-  int shift = 0;
-  if (!take_all && !take_none) {
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
-    for (int i = lane; i < nc; i += kWave) {
-      const uint32_t key = key_at(i);
-      kmin = min(kmin, key);
-      kmax = max(kmax, key);
-    }
-    kmin = wave_min_u32(kmin);
-    kmax = wave_max_u32(kmax);
-    const uint32_t diff = kmin ^ kmax;
-    shift = diff ? 32 - __clz(static_cast<int>(diff)) : 0;   // low bits that still vary
-    mask = (shift == 32) ? 0u : ~((1u << shift) - 1u);
-    prefix = kmax & mask;
-  }
-  for (int pass = 0; pass < 4; ++pass) {
-    const bool active = shift > 0;
-    uint32_t dmask = 0;
-    if (active) {
-      const int nb = min(8, shift);
-      shift -= nb;
-      dmask = (1u << nb) - 1u;
-    }
-    __syncthreads();
-    if (active)
-      for (int j = lane; j < 256; j += kWave) hist[hh][j] = 0u;
-    __syncthreads();
-    if (active) {
-      for (int i = lane; i < nc; i += kWave) {
-        const uint32_t key = key_at(i);
-        if ((key & mask) == prefix) atomicAdd(&hist[hh][(key >> shift) & dmask], 1u);
-      }
-    }
-    __syncthreads();
-    if (active) {
-      const uint32_t c0 = hist[hh][4 * lane], c1 = hist[hh][4 * lane + 1];
-      const uint32_t c2 = hist[hh][4 * lane + 2], c3 = hist[hh][4 * lane + 3];
-      const uint32_t mine = c0 + c1 + c2 + c3;
-      uint32_t suffix = mine;   // keys whose digit >= 4*lane
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t t = static_cast<uint32_t>(__shfl_down(static_cast<int>(suffix), off));
-        if (lane + off < kWave) suffix += t;
-      }
-      const uint32_t above = suffix - mine;   // keys whose digit > 4*lane + 3
-      const bool here = above < static_cast<uint32_t>(rem) && static_cast<uint32_t>(rem) <= suffix;
-      int digit = 0, rem_here = rem;
-      if (here) {
-        uint32_t acc = above;
-        const uint32_t cs[4] = {c0, c1, c2, c3};
-        for (int j = 3; j >= 0; --j) {
-          if (acc + cs[j] >= static_cast<uint32_t>(rem)) {
-            digit = 4 * lane + j;
-            rem_here = rem - static_cast<int>(acc);
-            break;
-          }
-          acc += cs[j];
-        }
-      }
-      const uint64_t hm = __ballot(here);
-      const int src = __ffsll(static_cast<unsigned long long>(hm)) - 1;
-      digit = __shfl(digit, src);
-      rem = __shfl(rem_here, src);
-      prefix |= static_cast<uint32_t>(digit) << shift;
-      mask |= dmask << shift;
-    }
-  }
-  const uint32_t thr = prefix;
-
-  // Ascending output and per-head selection bitmap.
-  int nsel = 0, neq = 0;
-  int32_t* out = P.sel_idx ? P.sel_idx + (static_cast<size_t>(b) * P.Hq + h) * k : nullptr;
-  for (int base = 0; base < nwords * 64; base += 64) {
-    const int i = base + lane;
-    const bool valid = i < nc;
-    const uint32_t key = valid ? key_at(i) : 0u;
-    bool sel;
-    if (take_none) {
-      sel = false;
-    } else if (take_all) {
-      sel = valid;
-    } else {
-      const bool eq = valid && key == thr;
-      const uint64_t eqm = __ballot(eq);
-      const int eqrank = neq + __popcll(eqm & lanes_below(lane));
-      sel = valid && (key > thr || (eq && eqrank < rem));
-      neq += __popcll(eqm);
-    }
-    const uint64_t sm = __ballot(sel);
-    const int pos = nsel + __popcll(sm & lanes_below(lane));
-    if (sel && out && pos < k) out[pos] = cr.lo + i;
-    nsel += __popcll(sm);
-    if (lane == 0) bits[base / 64] = sm;
-  }
-  if (out)
-    for (int j = nsel + lane; j < k; j += kWave) out[j] = -1;
-  __syncthreads();
-
-  build_union<G>(P, pair, b, T, cr, nc, nwords, dyn_lds, lane, hh);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wavefront (DPP row shifts,
@@ -503,128 +348,301 @@ __device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
   return v;
 }
 
-// Top-k with the order keys of one head held in registers: lane l holds
-// candidates l, l + 64, ..., l + 64 (KPL - 1).  A radix select over the
-// 32-bit order keys (8-bit digits, skipping the bits every key shares) finds
-// the k-th largest key with a histogram private to the wavefront, so no
-// workgroup barrier is needed until the union step.
-template <int G, int KPL>
-__global__ __launch_bounds__(kWave * G) void k_select(DecodeParams P) {
-  extern __shared__ uint64_t dyn_lds[];   // [G][nwords] selection bitmaps
-  __shared__ __attribute__((aligned(16))) uint32_t hist[G][256];
-  const int pair = blockIdx.x;
-  const int b = pair / P.Hkv;
-  const int g = pair % P.Hkv;
-  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
-  const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
-  const int nc = min(cr.count, P.nc_max);
-  const int nwords = (P.nc_max + 63) / 64;
-  const int hh = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  const int h = g * G + hh;
-  const int k = P.top_k;
-  const float* sc = P.scores + (static_cast<size_t>(b) * P.Hq + h) * P.nc_max;
-  uint64_t* bits = dyn_lds + static_cast<size_t>(hh) * nwords;
-
-  uint32_t key[KPL];
-  uint32_t valid = 0;   // bit j: slot j holds a candidate
+// One radix pass step shared by the two threshold searches below: given the
+// wavefront's histogram row (4 bins per lane, digit 4 lane + j), find the
+// digit holding the rem-th largest key and how many of that digit's keys are
+// still to take.
+__device__ __forceinline__ void radix_pick(const uint4 c4, int lane, int& digit, int& rem) {
+  const uint32_t mine = c4.x + c4.y + c4.z + c4.w;
+  const uint32_t incl = wave_scan_incl(mine);
+  const uint32_t total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1));
+  const uint32_t suffix = total - incl + mine;   // keys whose digit >= 4 * lane
+  const uint32_t above = suffix - mine;          // keys whose digit > 4 * lane + 3
+  const bool here = above < static_cast<uint32_t>(rem) && static_cast<uint32_t>(rem) <= suffix;
+  int d = 0, rem_here = rem;
+  if (here) {   // the crossing bin is one of this lane's four, scanned from the top
+    uint32_t acc = above;
+    bool found = false;
+    const uint32_t cs[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int c = lane + kWave * j;
-    const float v = sc[min(c, max(nc - 1, 0))];
-    key[j] = f32_order_key(v);
-    valid |= (c < nc ? 1u : 0u) << j;
+    for (int j = 3; j >= 0; --j) {
+      if (!found && acc + cs[j] >= static_cast<uint32_t>(rem)) {
+        d = 4 * lane + j;
+        rem_here = rem - static_cast<int>(acc);
+        found = true;
+      }
+      acc += cs[j];
+    }
+  }
+  const uint64_t hm = __ballot(here);
+  const int src = __ffsll(static_cast<unsigned long long>(hm)) - 1;
+  digit = __builtin_amdgcn_readlane(d, src);
+  rem = __builtin_amdgcn_readlane(rem_here, src);
+}
+
+// k-th largest of n order keys for one wavefront: `thr` is that key and
+// `rem` how many keys equal to it are taken (the lowest indices first).
+// Radix select over 8-bit digits, skipping the high bits every key shares,
+// with a 256-bin histogram private to the wavefront (no workgroup barrier).
+// KPL > 0: lane l holds keys l, l + 64, ... in registers; KPL == 0: keys
+// are read through key_at on every pass.
+template <int KPL, typename KeyAt>
+__device__ __forceinline__ void wave_topk_threshold(const uint32_t* key, KeyAt key_at, int n, int k, int lane,
+                                                    uint32_t* hist, uint32_t& thr, int& rem) {
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  if constexpr (KPL > 0) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      if (lane + kWave * j < n) {
+        kmin = min(kmin, key[j]);
+        kmax = max(kmax, key[j]);
+      }
+  } else {
+    for (int i = lane; i < n; i += kWave) {
+      const uint32_t x = key_at(i);
+      kmin = min(kmin, x);
+      kmax = max(kmax, x);
+    }
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  const uint32_t diff = kmin ^ kmax;
+  int shift = diff ? 32 - __clz(static_cast<int>(diff)) : 0;   // low bits that still vary
+  uint32_t mask = (shift == 32) ? 0u : ~((1u << shift) - 1u);
+  uint32_t prefix = kmax & mask;
+  rem = k;
+  uint4* hrow = reinterpret_cast<uint4*>(hist + 4 * lane);
+  while (shift > 0) {
+    const int nb = min(8, shift);
+    shift -= nb;
+    const uint32_t dmask = (1u << nb) - 1u;
+    *hrow = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if constexpr (KPL > 0) {
+#pragma unroll
+      for (int j = 0; j < KPL; ++j)
+        if (lane + kWave * j < n && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+    } else {
+      for (int i = lane; i < n; i += kWave) {
+        const uint32_t x = key_at(i);
+        if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & dmask], 1u);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    int digit;
+    radix_pick(*hrow, lane, digit, rem);
+    prefix |= static_cast<uint32_t>(digit) << shift;
+    mask |= dmask << shift;
+  }
+  thr = prefix;
+}
+
+// One head's selection: threshold, then the bitmap of selected candidates
+// (word w, bit i: candidate 64 w + i) and, when `out` is set, the selected
+// block indices in ascending order padded with -1.
+template <int KPL, typename KeyAt>
+__device__ __forceinline__ void head_select(KeyAt key_at, int nc, int k, int nwords, int lane, uint32_t* hist,
+                                            uint64_t* bits_row, int32_t* out, int lo) {
+  uint32_t key[KPL > 0 ? KPL : 1];
+  if constexpr (KPL > 0) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) key[j] = key_at(min(lane + kWave * j, max(nc - 1, 0)));
   }
   const bool take_all = k >= nc;
   const bool take_none = (k <= 0) || (nc == 0);
   uint32_t thr = 0;
   int rem = k;
-  if (!take_all && !take_none) {
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      if ((valid >> j) & 1) {
-        kmin = min(kmin, key[j]);
-        kmax = max(kmax, key[j]);
-      }
-    }
-    kmin = wave_min_u32(kmin);
-    kmax = wave_max_u32(kmax);
-    const uint32_t diff = kmin ^ kmax;
-    int shift = diff ? 32 - __clz(static_cast<int>(diff)) : 0;   // low bits that still vary
-    uint32_t mask = (shift == 32) ? 0u : ~((1u << shift) - 1u);
-    uint32_t prefix = kmax & mask;
-    uint4* hrow = reinterpret_cast<uint4*>(&hist[hh][4 * lane]);
-    while (shift > 0) {
-      const int nb = min(8, shift);
-      shift -= nb;
-      const uint32_t dmask = (1u << nb) - 1u;
-      *hrow = make_uint4(0, 0, 0, 0);
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-      for (int j = 0; j < KPL; ++j)
-        if (((valid >> j) & 1) && (key[j] & mask) == prefix) atomicAdd(&hist[hh][(key[j] >> shift) & dmask], 1u);
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      const uint4 c4 = *hrow;
-      const uint32_t mine = c4.x + c4.y + c4.z + c4.w;
-      const uint32_t incl = wave_scan_incl(mine);
-      const uint32_t total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1));
-      const uint32_t suffix = total - incl + mine;   // keys whose digit >= 4 * lane
-      const uint32_t above = suffix - mine;          // keys whose digit > 4 * lane + 3
-      const bool here = above < static_cast<uint32_t>(rem) && static_cast<uint32_t>(rem) <= suffix;
-      int digit = 0, rem_here = rem;
-      if (here) {   // the crossing bin is one of this lane's four, scanned from the top
-        uint32_t acc = above;
-        bool found = false;
-        const uint32_t cs[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {
-          if (!found && acc + cs[j] >= static_cast<uint32_t>(rem)) {
-            digit = 4 * lane + j;
-            rem_here = rem - static_cast<int>(acc);
-            found = true;
-          }
-          acc += cs[j];
-        }
-      }
-      const uint64_t hm = __ballot(here);
-      const int src = __ffsll(static_cast<unsigned long long>(hm)) - 1;
-      digit = __builtin_amdgcn_readlane(digit, src);
-      rem = __builtin_amdgcn_readlane(rem_here, src);
-      prefix |= static_cast<uint32_t>(digit) << shift;
-      mask |= dmask << shift;
-    }
-    thr = prefix;
-  }
-
-  // Ascending output and per-head selection bitmap.
+  if (!take_all && !take_none) wave_topk_threshold<KPL>(key, key_at, nc, k, lane, hist, thr, rem);
   int nsel = 0, neq = 0;
-  int32_t* out = P.sel_idx ? P.sel_idx + (static_cast<size_t>(b) * P.Hq + h) * k : nullptr;
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const bool vj = (valid >> j) & 1;
+  auto word = [&](int w, uint32_t x) {
+    const int i = w * kWave + lane;
+    const bool valid = i < nc;
     bool sel;
     if (take_none) {
       sel = false;
     } else if (take_all) {
-      sel = vj;
+      sel = valid;
     } else {
-      const bool eq = vj && key[j] == thr;
+      const bool eq = valid && x == thr;
       const uint64_t eqm = __ballot(eq);
       const int eqrank = neq + __popcll(eqm & lanes_below(lane));
-      sel = vj && (key[j] > thr || (eq && eqrank < rem));
+      sel = valid && (x > thr || (eq && eqrank < rem));
       neq += __popcll(eqm);
     }
     const uint64_t sm = __ballot(sel);
     const int pos = nsel + __popcll(sm & lanes_below(lane));
-    if (sel && out && pos < k) out[pos] = cr.lo + lane + kWave * j;
+    if (sel && out && pos < k) out[pos] = lo + i;
     nsel += __popcll(sm);
-    if (lane == 0 && j < nwords) bits[j] = sm;
+    if (lane == 0) bits_row[w] = sm;
+  };
+  if constexpr (KPL > 0) {
+#pragma unroll
+    for (int w = 0; w < KPL; ++w)
+      if (w < nwords) word(w, key[w]);
+  } else {
+    for (int w = 0; w < nwords; ++w) {
+      const int i = w * kWave + lane;
+      word(w, i < nc ? key_at(i) : 0u);
+    }
   }
   if (out)
     for (int j = nsel + lane; j < k; j += kWave) out[j] = -1;
+}
+
+// Selection of one (sequence, kv head), one workgroup: stage the G heads'
+// order keys and the block-table row in LDS (every load of a round issued
+// before any store), top-k per head (wavefront w takes heads w, w + 4, ...),
+// then the union in ascending block order -- blocks below the candidates
+// (sinks), candidates selected by some head or holding sink or window
+// tokens, blocks past the candidates (window) -- written as entries
+// block | (mask of the heads that selected it) << 20 with their pages.
+template <int G>
+__global__ __launch_bounds__(kThreads) void k_select(DecodeParams P) {
+  constexpr int NW = kThreads / kWave;
+  extern __shared__ uint64_t dyn_lds[];
+  char* smem = reinterpret_cast<char*>(dyn_lds);
+  const int pair = blockIdx.x;
+  const int b = pair / P.Hkv;
+  const int g = pair % P.Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
+  uint64_t* bits = reinterpret_cast<uint64_t*>(smem + P.sl.bits);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + P.sl.hist) + wave * 256;
+  uint64_t* umask = reinterpret_cast<uint64_t*>(smem + P.sl.umask);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(smem + P.sl.keys);
+  int32_t* btrow = reinterpret_cast<int32_t*>(smem + P.sl.btrow);
+
+  const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
+  const int nc = min(cr.count, P.nc_max);
+  const int nwords = P.nwords;
+  const int nb = min(ceil_div(T, P.B), P.nblk_max);
+  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  const uint32_t* key0 = P.keys + (static_cast<size_t>(b) * P.Hq + g * G) * P.sstride;
+
+  if (P.keys_staged) {
+    const uint4* src = reinterpret_cast<const uint4*>(key0);
+    uint4* dst = reinterpret_cast<uint4*>(keys);
+    const int n4 = G * P.sstride / 4;
+    for (int base = 0; base < n4; base += 4 * kThreads) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = src[min(base + tid + u * kThreads, n4 - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (base + tid + u * kThreads < n4) dst[base + tid + u * kThreads] = v[u];
+    }
+  }
+  if (P.bt_staged) {
+    for (int base = 0; base < nb; base += 4 * kThreads) {
+      int v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = bt[min(base + tid + u * kThreads, nb - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (base + tid + u * kThreads < nb) btrow[base + tid + u * kThreads] = v[u];
+    }
+  }
   __syncthreads();
-  build_union<G>(P, pair, b, T, cr, nc, nwords, dyn_lds, lane, hh);
+
+  for (int hh = wave; hh < G; hh += NW) {
+    int32_t* out = P.sel_idx ? P.sel_idx + (static_cast<size_t>(b) * P.Hq + g * G + hh) * P.top_k : nullptr;
+    uint64_t* brow = bits + hh * nwords;
+    if (P.keys_staged) {
+      const uint32_t* kh = keys + hh * P.sstride;
+      auto key_at = [&](int i) -> uint32_t { return kh[i]; };
+      if (nc <= 4 * kWave)
+        head_select<4>(key_at, nc, P.top_k, nwords, lane, hist, brow, out, cr.lo);
+      else if (nc <= 8 * kWave)
+        head_select<8>(key_at, nc, P.top_k, nwords, lane, hist, brow, out, cr.lo);
+      else if (nc <= 16 * kWave)
+        head_select<16>(key_at, nc, P.top_k, nwords, lane, hist, brow, out, cr.lo);
+      else
+        head_select<0>(key_at, nc, P.top_k, nwords, lane, hist, brow, out, cr.lo);
+    } else {
+      const uint32_t* kh = key0 + static_cast<size_t>(hh) * P.sstride;
+      auto key_at = [&](int i) -> uint32_t { return kh[i]; };
+      head_select<0>(key_at, nc, P.top_k, nwords, lane, hist, brow, out, cr.lo);
+    }
+  }
+  __syncthreads();
+
+  const int win0 = T - P.W;
+  auto in_union = [&](int j, int& hm) -> bool {
+    hm = 0;
+    if (j >= nb) return false;
+    if (nc == 0 || j < cr.lo || j >= cr.lo + nc) return true;
+    const int c = j - cr.lo;
+#pragma unroll
+    for (int x = 0; x < G; ++x) hm |= static_cast<int>((bits[x * nwords + (c >> 6)] >> (c & 63)) & 1ull) << x;
+    const bool overlap = (j * P.B < P.ns) || ((j + 1) * P.B > win0);
+    return hm != 0 || overlap;
+  };
+  int32_t* ul = P.ulist + static_cast<size_t>(pair) * P.umax;
+  int32_t* up = P.upage + static_cast<size_t>(pair) * P.umax;
+  const int nch = ceil_div(nb, kWave);
+  // Chunk c = blocks 64 c .. 64 c + 63: inclusion masks (LDS, up to 64
+  // chunks per round), prefix counts by one scan, then every lane writes its
+  // block's entry at its position.
+  int done = 0;   // union entries of the chunks before this round
+  for (int c0 = 0; c0 < nch; c0 += kWave) {
+    const int ncr = min(kWave, nch - c0);
+    for (int c = wave; c < ncr; c += NW) {
+      int hm;
+      const uint64_t m = __ballot(in_union((c0 + c) * kWave + lane, hm));
+      if (lane == 0) umask[c] = m;
+    }
+    __syncthreads();
+    const uint64_t mymask = lane < ncr ? umask[lane] : 0ull;
+    const uint32_t cnt_c = static_cast<uint32_t>(__popcll(mymask));
+    const uint32_t incl = wave_scan_incl(cnt_c);
+    const int total = __builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1);
+    for (int c = wave; c < ncr; c += NW) {
+      const int base = done + __builtin_amdgcn_readlane(static_cast<int>(incl - cnt_c), c);
+      const uint64_t m = umask[c];
+      const int j = (c0 + c) * kWave + lane;
+      if ((m >> lane) & 1ull) {
+        const int pos = base + __popcll(m & lanes_below(lane));
+        if (pos < P.umax) {
+          int hm;
+          in_union(j, hm);
+          ul[pos] = j | (hm << 20);
+          up[pos] = P.bt_staged ? btrow[j] : bt[j];
+        }
+      }
+    }
+    done += total;
+    __syncthreads();   // umask is reused by the next round
+  }
+  if (tid == 0) P.ucount[pair] = min(done, P.umax);
+}
+
+// The split's share of the union: split s takes entries s, s + S, s + 2S,
+// ... (S = max_split), so window and sink blocks, which every head of the
+// group needs, spread over the splits instead of piling into the last one.
+// Lane e < ne holds entry e and its page; the count and the entries come in
+// one round trip.
+struct SplitShare {
+  int ent;
+  int page;    // -1 on lanes past ne
+  int count;   // union size (uniform)
+  int ne;      // entries of this split (uniform)
+};
+__device__ __forceinline__ SplitShare load_share(const DecodeParams& P, int pair, int split, int lane) {
+  const int ent_at = split + lane * P.max_split;
+  const bool ent_in = lane < P.bps && ent_at < P.umax;
+  const size_t off = static_cast<size_t>(pair) * P.umax + (ent_in ? ent_at : 0);
+  SplitShare r;
+  r.count = __builtin_amdgcn_readfirstlane(min(P.ucount[pair], P.umax));
+  r.ent = P.ulist[off];
+  r.page = P.upage[off];
+  r.ne = split < r.count ? min(P.bps, ceil_div(r.count - split, P.max_split)) : 0;
+  if (!(ent_in && lane < r.ne)) {
+    r.ent = 0;
+    r.page = -1;
+  }
+  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -646,7 +664,7 @@ __global__ __launch_bounds__(kWave * G) void k_select(DecodeParams P) {
 // processed.  For B >= 64 a unit lies in one page: its page, first token and
 // selection mask are wavefront-uniform and each lane's row offset is fixed.
 template <typename KV, int D, int G, bool BIG>
-__global__ __launch_bounds__(kThreads, (G <= 4 ? 3 : 1)) void k_attend(DecodeParams P) {
+__global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
   constexpr int LPT = D / 8;             // lanes per token row
   constexpr int NGRP = kThreads / LPT;   // token groups per workgroup
   constexpr int U = kUnit / NGRP;        // rows per group per unit
@@ -659,30 +677,19 @@ __global__ __launch_bounds__(kThreads, (G <= 4 ? 3 : 1)) void k_attend(DecodePar
   __shared__ float red[NW][G][2 * D];
   __shared__ float mll[G][4];
 
-  // Split s of a (sequence, kv head) takes union entries s, s + S, s + 2S, ...
-  // (S = max_split), so window and sink blocks, which every head of the
-  // group needs, spread over the splits instead of piling into the last one.
-  // The count and the candidate entries are fetched in one round trip.
   const int pair = blockIdx.x / P.max_split;
   const int split = blockIdx.x % P.max_split;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
-  const int ent_at = split + lane * P.max_split;   // this lane's candidate entry
-  const bool ent_in = lane < P.bps && ent_at < P.umax;
-  const size_t ent_off = static_cast<size_t>(pair) * P.umax + (ent_in ? ent_at : 0);
-  const int count = min(P.ucount[pair], P.umax);
-  int my_ent = P.ulist[ent_off];
-  int my_page = P.upage[ent_off];
-  if (split >= count) return;
-  const int ne = min(P.bps, ceil_div(count - split, P.max_split));
-  if (!(ent_in && lane < ne)) {
-    my_ent = 0;
-    my_page = -1;
-  }
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
-  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
+  const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
+  const SplitShare share = load_share(P, pair, split, lane);
+  if (split >= share.count) return;
+  const int ne = share.ne;
+  const int my_ent = share.ent;
+  const int my_page = share.page;
   const int B = P.B;
   const int ns = P.ns;
   const int win0 = T - P.W;
@@ -919,6 +926,340 @@ __global__ __launch_bounds__(kThreads, (G <= 4 ? 3 : 1)) void k_attend(DecodePar
 }
 
 // ---------------------------------------------------------------------------
+// 3b. Split-K exact attention for bf16 keys/values on the matrix cores
+// ---------------------------------------------------------------------------
+// Per union token the exact part costs G dot products of length D and 2G
+// multiply-adds per channel (p v for the softmax, (1 + s) v for the linear
+// sums that are subtracted from the global state): about 3 fp32 MACs per
+// byte of K/V at G = 4, more than the vector ALUs sustain at HBM rate.  The
+// two contractions run on MFMA instead:
+//   scores  S[h][t]  = sum_c Q[h][c] K[t][c]       v_mfma_f32_16x16x32_bf16,
+//           rows = query heads (G of 16 used), columns = 16 tokens;
+//   values  O[r][c] += sum_t A[r][t] V[t][c]       v_mfma_f32_16x16x16_bf16,
+//           rows r = (p_hi, p_lo, w_hi, w_lo) x G heads, columns = channels.
+// p = exp(s - m) and w = 1 + s are fp32; each is split into a bf16 pair
+// hi + lo (hi = bf16(x), lo = bf16(x - hi)) that carries ~16 mantissa bits,
+// so the products match the fp32 vector path to ~2^-17 relative while keys,
+// values and queries enter exactly (they are bf16 already).
+//
+// Work: the split's union blocks are cut into slices of 16 rows of one page;
+// wavefront w of the workgroup takes slices w, w + 4, ...  Each wavefront
+// keeps its own running maximum per head, so the slice loop has no
+// workgroup barrier; the four wavefronts are combined once at the end.
+// Lane l = 16 q + n: in the score MFMA it carries token n (channels
+// q D/4 .. q D/4 + D/4 of its K row); in the value MFMA it carries tokens
+// 4q .. 4q + 3 of the slice at channels (D/16) n .. (D/16) n + D/16, and its
+// value tile t column n is channel (D/16) n + t.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  return fmaxf(v, dpp_f<0x140>(v));
+}
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)));
+}
+
+template <int NT>
+struct VSlice;
+template <>
+struct VSlice<8> {   // D = 128: 8 channels of a row per lane
+  uint4 r;
+  __device__ __forceinline__ void load(const char* p) { r = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ uint32_t word(int i) const { return i == 0 ? r.x : i == 1 ? r.y : i == 2 ? r.z : r.w; }
+  __device__ __forceinline__ void zero() { r = make_uint4(0, 0, 0, 0); }
+};
+template <>
+struct VSlice<4> {   // D = 64: 4 channels of a row per lane
+  uint2 r;
+  __device__ __forceinline__ void load(const char* p) { r = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ uint32_t word(int i) const { return i == 0 ? r.x : r.y; }
+  __device__ __forceinline__ void zero() { r = make_uint2(0, 0); }
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
+  constexpr int NW = kThreads / kWave;
+  constexpr int KS = D / 32;            // score MFMAs per slice (32 channels each)
+  constexpr int NT = D / 16;            // value tiles (16 channels each)
+  constexpr int MT = G <= 4 ? 1 : 2;    // value M-tiles of 16 rows
+  constexpr int R = 4 * G;              // value rows used: p_hi, p_lo, w_hi, w_lo per head
+  constexpr int kAll = (1 << G) - 1;
+  constexpr int SL = 16;                // rows per slice
+  __shared__ float s_pub[NW][G][SL];    // scores of a wavefront's current slice
+  __shared__ float m_pub[NW][G];        // running maximum per head
+  __shared__ float c_pub[NW][G];        // rescale factor of the last slice
+  __shared__ float red[NW][2][G][D];    // per-wavefront sums of p v and w v
+  __shared__ float wst[NW][G][3];       // per-wavefront m, sum p, sum w
+  __shared__ uint4 q_lds[16][D / 8 + 1];
+
+  const int pair = blockIdx.x / P.max_split;
+  const int split = blockIdx.x % P.max_split;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: keeps the loop scalar
+  const int lane = tid % kWave;
+  const int q4 = lane / 16;
+  const int n16 = lane % 16;
+  const int b = pair / P.Hkv;
+  const int g = pair % P.Hkv;
+  const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
+  const SplitShare share = load_share(P, pair, split, lane);   // issued with the query loads below
+  const int B = P.B;
+  const int ns = P.ns;
+  const int win0 = T - P.W;
+  const int spb = B / SL;               // slices per block
+
+  // Query operand rows (heads; rows G..15 zero) staged in LDS, 16 bytes of
+  // padding per row so that the 16 rows fall on distinct banks.
+  for (int idx = tid; idx < 16 * (D / 8); idx += kThreads) {
+    const int row = idx / (D / 8);
+    const int col = idx % (D / 8);
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (row < G)
+      w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(P.q) +
+                                          (static_cast<size_t>(b) * P.Hq + g * G + row) * D + col * 8);
+    q_lds[row][col] = w;
+  }
+  if (lane < G) {
+    m_pub[wave][lane] = kNegInf;
+    c_pub[wave][lane] = 1.f;
+  }
+  if (split >= share.count) return;
+  __syncthreads();   // q_lds
+  const int ne = share.ne;
+  const int my_ent = share.ent;
+  const int my_page = share.page;
+  const int nsl = ne * spb;             // slices of the split
+  const int nk = nsl > wave ? ceil_div(nsl - wave, NW) : 0;   // slices of this wavefront
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[4];                        // running max of heads 4 q4 + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m_run[i] = kNegInf;
+  float l_acc[MT];                       // sum of this lane's value-operand row (fp32)
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) l_acc[mt] = 0.f;
+
+  const char* kp = reinterpret_cast<const char*>(P.k_pages);
+  const char* vp = reinterpret_cast<const char*>(P.v_pages);
+  const size_t k_lane = (static_cast<size_t>(n16) * D + q4 * (D / 4)) * 2;
+  const size_t v_lane = (static_cast<size_t>(4 * q4) * D + NT * n16) * 2;
+
+  struct Slice {
+    uint4 k[KS];
+    VSlice<NT> v[4];
+    int t0;   // first token (uniform); T for a slice without a page (no row valid)
+    int fm;   // heads that selected the block (uniform)
+  };
+  // A fetch past the wavefront's last slice re-reads that slice (an L2 hit)
+  // and marks every row invalid.
+  auto fetch = [&](int kk, Slice& x) __attribute__((always_inline)) {
+    const bool live = kk < nk;
+    const int sl = wave + NW * (live ? kk : max(nk - 1, 0));
+    const int e = sl / spb;
+    const int sub = sl - e * spb;
+    const int ent = __builtin_amdgcn_readlane(my_ent, e);
+    const int pg = __builtin_amdgcn_readlane(my_page, e);
+    const size_t base = ((static_cast<size_t>(max(pg, 0)) * P.Hkv + g) * B + sub * SL) * D * 2;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) x.k[s] = *reinterpret_cast<const uint4*>(kp + base + k_lane + 16 * s);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x.v[j].load(vp + base + v_lane + static_cast<size_t>(j) * D * 2);
+    x.t0 = (live && pg >= 0) ? (ent & 0xFFFFF) * B + sub * SL : T;
+    x.fm = (ent >> 20) & kAll;
+    // keep the loads ahead of the previous slice's arithmetic
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Every fetched slice of the loop is processed, without a branch around
+  // it, so that no load stays in flight across the loop back edge.
+  auto process = [&](Slice& x) __attribute__((always_inline)) {
+    // ---- scores: rows 4 q4 + i are heads, column n16 is token t0 + n16
+    // lane (q4, n16) takes head n16's channels q4 D/4 + 8 s .. + 8 from LDS
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, q_lds[n16][q4 * KS + s]),
+                                                   __builtin_bit_cast(bf16x8_t, x.k[s]), sc, 0, 0, 0);
+    const int t = x.t0 + n16;
+    const bool valid = t < T;
+    const bool sw = t < ns || t >= win0;
+    bool changed = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * q4 + i;
+      if (4 * i >= 4 * G && G < 4) break;   // rows past G (G < 4) are never read
+      const bool inc = valid && h < G && (sw || ((x.fm >> h) & 1));
+      const float sv = inc ? P.sigma * sc[i] : kNegInf;
+      const float mnew = fmaxf(m_run[i], row16_max(sv));
+      const float cf = (mnew == m_run[i]) ? 1.f : fast_exp(m_run[i] - mnew);
+      changed |= (h < G) && (cf != 1.f);
+      m_run[i] = mnew;
+      if (h < G) {
+        s_pub[wave][h][n16] = sv;
+        if (n16 == 0) {
+          m_pub[wave][h] = mnew;
+          c_pub[wave][h] = cf;
+        }
+      }
+    }
+    // ---- rescale the p rows of heads whose maximum moved
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * q4 + i;
+        const float f = r < 2 * G ? c_pub[wave][r % G] : 1.f;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) acc[mt][tt][i] *= f;
+      }
+    // ---- value operand rows: lane (q4, n16) builds row 16 mt + n16 for
+    // tokens 4 q4 .. 4 q4 + 3
+    s16x4_t av[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = 16 * mt + n16;
+      const int typ = r / G;           // 0 p_hi, 1 p_lo, 2 w_hi, 3 w_lo, >= 4 unused
+      const int h = r % G;
+      const float4 s4 = *reinterpret_cast<const float4*>(&s_pub[wave][h][4 * q4]);
+      const float mh = m_pub[wave][h];
+      const float ch = c_pub[wave][h];
+      const float sj[4] = {s4.x, s4.y, s4.z, s4.w};
+      uint32_t bits[4];
+      float rs = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool inc = sj[j] != kNegInf;
+        const float pv = inc ? fast_exp(sj[j] - mh) : 0.f;
+        const float wv = inc ? 1.f + sj[j] : 0.f;
+        float val = typ < 2 ? pv : wv;
+        val = typ < 4 ? val : 0.f;
+        rs += val;
+        const uint32_t hi = bf16_bits_rne(val);
+        const uint32_t lo = bf16_bits_rne(val - __uint_as_float(hi << 16));
+        bits[j] = (typ & 1) ? lo : hi;
+      }
+      l_acc[mt] = fmaf(l_acc[mt], typ < 2 ? ch : 1.f, rs);
+      av[mt] = __builtin_bit_cast(s16x4_t, make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)));
+    }
+    // ---- values: tile t takes channel t of each lane's V rows; rows past
+    // the end of the sequence may hold anything and enter as zero
+    bool vrow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vrow[j] = x.t0 + 4 * q4 + j < T;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const uint32_t sel = (tt & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t vw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vw[j] = vrow[j] ? x.v[j].word(tt / 2) : 0u;
+      const uint32_t lo = __builtin_amdgcn_perm(vw[1], vw[0], sel);
+      const uint32_t hi = __builtin_amdgcn_perm(vw[3], vw[2], sel);
+      const s16x4_t bv = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt][tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[mt], bv, acc[mt][tt], 0, 0, 0);
+    }
+  };
+
+  // Three slices in flight per wavefront.  The loop has a single exit: a
+  // count that is not a multiple of three ends with fully masked slices.
+  Slice sa, sb, sc;
+  fetch(0, sa);
+  fetch(1, sb);
+  for (int kk = 0; kk < nk; kk += 3) {
+    fetch(kk + 2, sc);
+    process(sa);
+    fetch(kk + 3, sa);
+    process(sb);
+    fetch(kk + 4, sb);
+    process(sc);
+  }
+
+  // ---- per-wavefront sums: hi + lo rows, then p v / w v per head to LDS
+  // Row r of value tile (mt, t) sits in lane group q4 = (r % 16) / 4, entry
+  // r % 4, column n16 = channel NT n16 + t.
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int c = NT * n16 + tt;
+    if constexpr (G == 1) {
+      if (q4 == 0) {
+        red[wave][0][0][c] = acc[0][tt][0] + acc[0][tt][1];
+        red[wave][1][0][c] = acc[0][tt][2] + acc[0][tt][3];
+      }
+    } else if constexpr (G == 2) {
+      if (q4 < 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) red[wave][q4][h][c] = acc[0][tt][h] + acc[0][tt][h + 2];
+      }
+    } else if constexpr (G == 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = pair_sum<16>(acc[0][tt][i]);   // hi row + lo row
+        if (q4 == 0 || q4 == 2) red[wave][q4 / 2][i][c] = v;
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = pair_sum<32>(acc[mt][tt][i]);
+          if (q4 < 2) red[wave][mt][4 * q4 + i][c] = v;
+        }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const float v = pair_sum<32>(pair_sum<16>(l_acc[mt]));   // over the four token groups
+    const int r = 16 * mt + n16;
+    if (q4 == 0 && r < R) {
+      const int typ = r / G;
+      if (typ == 0) wst[wave][r % G][1] = v;
+      if (typ == 2) wst[wave][r % G][2] = v;
+    }
+  }
+  if (lane < G) wst[wave][lane][0] = m_pub[wave][lane];
+  __syncthreads();
+
+  float* outp = P.part + (static_cast<size_t>(pair) * P.max_split + split) * G * P.pstride;
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int h = idx / D;
+    const int c = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wst[w][h][0]);
+    float a = 0.f, la = 0.f, l = 0.f, ld = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = wst[w][h][0];
+      const float e = mw == kNegInf ? 0.f : fast_exp(mw - M);
+      a = fmaf(e, red[w][0][h][c], a);
+      l = fmaf(e, wst[w][h][1], l);
+      la += red[w][1][h][c];
+      ld += wst[w][h][2];
+    }
+    float* o = outp + static_cast<size_t>(h) * P.pstride;
+    o[4 + c] = a;
+    o[4 + D + c] = la;
+    if (c == 0) {
+      o[0] = M;
+      o[1] = l;
+      o[2] = ld;
+      o[3] = 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 4. Merge of the splits and the residual linear part
 // ---------------------------------------------------------------------------
 // One workgroup per (sequence, query head); NP = 256 / D lanes share a
@@ -1023,30 +1364,21 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
   }
   if (rec) rec(ctx, 1, "select");
   {
-    const int nwords = (p.nc_max + 63) / 64;
-    const size_t bits = static_cast<size_t>(G) * nwords * sizeof(uint64_t);
-    const int kpl = ceil_div(std::max(p.nc_max, 1), kWave);
-    auto go = [&](auto kernel, size_t lds) -> hipError_t {
-      if (lds > 32 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-      }
-      hipLaunchKernelGGL(kernel, dim3(pairs), dim3(kWave * G), lds, stream, P);
-      return launch_status("k_select");
-    };
-    hipError_t e;
-    if (kpl <= 2) e = go(k_select<G, 2>, bits);
-    else if (kpl <= 4) e = go(k_select<G, 4>, bits);
-    else if (kpl <= 8) e = go(k_select<G, 8>, bits);
-    else if (kpl <= 16) e = go(k_select<G, 16>, bits);
-    else if (kpl <= 32) e = go(k_select<G, 32>, bits);
-    else e = go(k_select_generic<G>, bits + (L.keys_staged ? static_cast<size_t>(G) * p.nc_max * sizeof(uint32_t) : 0));
+    const size_t lds = L.sl.total;
+    if (lds > 32 * 1024) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<G>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_select<G>), dim3(pairs), dim3(kThreads), lds, stream, P);
+    hipError_t e = launch_status("k_select");
     if (e != hipSuccess) return e;
   }
   if (rec) rec(ctx, 2, "attend");
   {
-    if (p.B >= kUnit)
+    if constexpr (KV::kBytes == 2)
+      hipLaunchKernelGGL((k_attend_mfma<D, G>), dim3(pairs * L.max_split), dim3(kThreads), 0, stream, P);
+    else if (p.B >= kUnit)
       hipLaunchKernelGGL((k_attend<KV, D, G, true>), dim3(pairs * L.max_split), dim3(kThreads), 0, stream, P);
     else
       hipLaunchKernelGGL((k_attend<KV, D, G, false>), dim3(pairs * L.max_split), dim3(kThreads), 0, stream, P);
@@ -1086,21 +1418,38 @@ DecodeLayout decode_layout(const Problem& p) {
   L.score_wgs = p.nc_max > 0 ? ceil_div(p.nc_max, L.score_chunk) : 0;
   L.ro_rows = kRoRows;
   L.ro_wgs = p.linear_tail ? p.D / L.ro_rows : 0;
-  {
-    const size_t bits = static_cast<size_t>(p.G) * ((p.nc_max + 63) / 64) * sizeof(uint64_t);
-    const size_t keys = static_cast<size_t>(p.G) * p.nc_max * sizeof(uint32_t);
-    L.keys_staged = (bits + keys) <= 96 * 1024 ? 1 : 0;
-  }
   const int sink_blocks = p.ns / p.B;
   const long sel_blocks = std::min<long>(static_cast<long>(p.G) * p.top_k, p.nc_max);
   const long bound = static_cast<long>(sink_blocks) + sel_blocks + 2 + p.W / p.B + 1;
   L.umax = static_cast<int>(std::max<long>(1, std::min<long>(bound, p.nblk_max)));
-  L.bps = std::max(1, kUnitsPerWg * kUnit / p.B);
-  L.max_split = ceil_div(L.umax, L.bps);
+  {
+    const int want = std::max(1, (kAttendWgsTarget + pairs / 2) / pairs);
+    const int splits = std::min(L.umax, std::max(want, ceil_div(L.umax, kWave)));
+    L.bps = ceil_div(L.umax, splits);   // <= 64: one union entry per lane
+    L.max_split = ceil_div(L.umax, L.bps);
+  }
   L.pstride = 2 * p.D + 4;
+  L.sstride = std::max(4, (p.nc_max + 3) / 4 * 4);
+  L.nwords = std::max(1, (p.nc_max + 63) / 64);
+  L.keys_staged = static_cast<size_t>(p.G) * L.sstride * sizeof(uint32_t) <= kKeysStageBytes ? 1 : 0;
+  L.bt_staged = static_cast<size_t>(p.nblk_max) * sizeof(int32_t) <= kBtStageBytes ? 1 : 0;
+  {
+    uint32_t o = 0;
+    auto take = [&](uint32_t bytes) {
+      const uint32_t at = o;
+      o += (bytes + 15u) & ~15u;
+      return at;
+    };
+    L.sl.bits = take(static_cast<uint32_t>(p.G * L.nwords * sizeof(uint64_t)));
+    L.sl.hist = take(4 * 256 * sizeof(uint32_t));
+    L.sl.umask = take(kWave * sizeof(uint64_t));
+    L.sl.keys = take(L.keys_staged ? static_cast<uint32_t>(p.G * L.sstride * sizeof(uint32_t)) : 0u);
+    L.sl.btrow = take(L.bt_staged ? static_cast<uint32_t>(p.nblk_max * sizeof(int32_t)) : 0u);
+    L.sl.total = o;
+  }
   size_t off = 0;
   L.off_scores = off;
-  off = align_up(off + sizeof(float) * static_cast<size_t>(p.batch) * p.Hq * std::max(1, p.nc_max));
+  off = align_up(off + sizeof(uint32_t) * static_cast<size_t>(p.batch) * p.Hq * L.sstride);
   L.off_ro = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(pairs) * std::max(1, L.ro_wgs) * p.G * p.D);
   L.off_roz = off;
@@ -1132,11 +1481,11 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.seq_lens = a.seq_lens;
   P.out = a.out;
   P.sel_idx = a.sel_idx;
-  P.scores = reinterpret_cast<float*>(a.ws + L.off_scores);
-  P.ro = reinterpret_cast<float*>(a.ws + L.off_ro);
-  P.roz = reinterpret_cast<float*>(a.ws + L.off_roz);
+  P.keys = reinterpret_cast<uint32_t*>(a.ws + L.off_scores);
   P.ulist = reinterpret_cast<int32_t*>(a.ws + L.off_union);
   P.upage = reinterpret_cast<int32_t*>(a.ws + L.off_upage);
+  P.ro = reinterpret_cast<float*>(a.ws + L.off_ro);
+  P.roz = reinterpret_cast<float*>(a.ws + L.off_roz);
   P.ucount = reinterpret_cast<int32_t*>(a.ws + L.off_ucount);
   P.part = reinterpret_cast<float*>(a.ws + L.off_part);
   P.Hq = p.Hq;
@@ -1152,7 +1501,11 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.nblk_max = p.nblk_max;
   P.score_wgs = L.score_wgs;
   P.ro_wgs = L.ro_wgs;
+  P.sstride = L.sstride;
+  P.nwords = L.nwords;
   P.keys_staged = L.keys_staged;
+  P.bt_staged = L.bt_staged;
+  P.sl = L.sl;
   P.umax = L.umax;
   P.bps = L.bps;
   P.max_split = L.max_split;

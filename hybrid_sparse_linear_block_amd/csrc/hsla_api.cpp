@@ -51,9 +51,9 @@ hsla_status resolve(const hsla_config* cfg, int32_t batch, int32_t max_seq_len,
   p.max_blocks = max_blocks;
   p.nblk_max = static_cast<int>(nblk);
   p.nc_max = hsla::candidate_range(max_seq_len, B, p.ns, p.W).count;
-  // Per-head selection bitmaps of the select kernel live in LDS.
+  // Per-head selection bitmaps of an attention workgroup live in LDS.
   const size_t bitmap = static_cast<size_t>(G) * ((p.nc_max + 63) / 64) * 8;
-  if (bitmap > 64 * 1024) return HSLA_ERR_UNSUPPORTED;
+  if (bitmap > 16 * 1024) return HSLA_ERR_UNSUPPORTED;
   *out = p;
   return HSLA_OK;
 }

@@ -29,6 +29,15 @@ struct Problem {
 };
 
 // ---------------------------------------------------------------- decode
+// Byte offsets into the dynamic LDS of the selection kernel: per-head
+// selection bitmaps [G][nwords] (uint64), wavefront-private radix
+// histograms [4][256] (uint32), union chunk masks [64] (uint64), then, when
+// staged, the order keys [G][sstride] (uint32) and the sequence's
+// block-table row [nblk_max] (int32).
+struct SelLayout {
+  uint32_t bits, hist, umask, keys, btrow, total;
+};
+
 struct DecodeLayout {
   int score_chunk;     // candidates per scoring workgroup
   int score_wgs;       // scoring workgroups per (sequence, kv head)
@@ -38,7 +47,11 @@ struct DecodeLayout {
   int bps;             // union blocks per attention split
   int max_split;       // attention splits per (sequence, kv head)
   int pstride;         // floats per (split, head) partial
-  int keys_staged;     // select kernel keeps the order keys in LDS
+  int sstride;         // order keys per (sequence, head) row, multiple of 4
+  int nwords;          // 64-bit words of a per-head selection bitmap
+  int keys_staged;     // order keys of the G heads staged in LDS
+  int bt_staged;       // block-table row staged in LDS
+  SelLayout sl;
   size_t off_scores, off_ro, off_roz, off_union, off_upage, off_ucount, off_part, total;
 };
 DecodeLayout decode_layout(const Problem& p);

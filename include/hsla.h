@@ -65,7 +65,9 @@ extern "C" {
 typedef enum hsla_status {
   HSLA_OK = 0,
   HSLA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer */
-  HSLA_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, group, block size, dtype */
+  HSLA_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, group, block size, dtype,
+                                or more candidate blocks than one workgroup's selection
+                                bitmaps hold (G * ceil(n_candidates / 64) * 8 > 16384) */
   HSLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   HSLA_ERR_HIP = -4          /* a kernel launch failed */
 } hsla_status;
