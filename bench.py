@@ -47,6 +47,12 @@ def parse():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="only the work profiled for HBM traffic: a device copy of known size, then a few steps")
+    ap.add_argument("--traffic-collect", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="rocprofv3 counter files of two --traffic-run passes -> profiles/attend_traffic.json")
+    ap.add_argument("--profile-summary", nargs=2, metavar=("STATS_CSV", "COMMAND"),
+                    help="rocprofv3 --stats kernel file -> markdown summary on stdout")
     return ap.parse_args()
 
 
@@ -134,8 +140,8 @@ def source_sha():
 
 
 def traffic_entry(workload_name):
-    """HBM traffic of k_attend from the committed rocprofv3 counter runs, if
-    they were taken on the current kernel source."""
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter runs, if they were taken on the current kernel source."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -144,6 +150,93 @@ def traffic_entry(workload_name):
     if not ent or ent.get("source_sha") != source_sha():
         return None
     return ent.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters
+# ---------------------------------------------------------------------------
+COPY_BYTES = 256 << 20
+TRAFFIC_STEPS = 8
+
+
+def traffic_run(args):
+    """The profiled program of the two counter passes: one device copy of
+    COPY_BYTES (the calibration of FETCH_SIZE / WRITE_SIZE against bytes
+    known to move), then warmup and TRAFFIC_STEPS decode steps."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    env = setup(args, TRAFFIC_STEPS)
+    preps, R = env["preps"], env["R"]
+    for i in range(args.warmup + TRAFFIC_STEPS):
+        preps[i % R]()
+    torch.cuda.synchronize()
+    print(f"[traffic] {TRAFFIC_STEPS} steps done", file=sys.stderr)
+
+
+def _counter_rows(path, counter):
+    import csv
+    rows = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_collect(fetch_csv, write_csv):
+    """Per-launch HBM bytes of the attention kernel: the counters' KiB per
+    dispatch, each scaled by (bytes the copy moved) / (what the counter read
+    for the copy), averaged over the attention dispatches."""
+    out = {}
+    scales, per = {}, {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, counter)
+        copy = [v for n, v in rows if "k_" not in n and v * 1024 > COPY_BYTES / 4]
+        attend = [v for n, v in rows if "k_attend" in n]
+        if not copy or not attend:
+            raise SystemExit(f"{path}: no copy or attention dispatches for {counter}")
+        scales[counter] = COPY_BYTES / (max(copy) * 1024.0)
+        per[counter] = float(np.mean(attend)) * 1024.0 * scales[counter]
+    name = workload(parse_known_workload()).name
+    try:
+        out = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        out = {}
+    out[name] = {"source_sha": source_sha(), "bytes_per_launch": int(per["FETCH_SIZE"] + per["WRITE_SIZE"]),
+                 "fetch_bytes": int(per["FETCH_SIZE"]), "write_bytes": int(per["WRITE_SIZE"]),
+                 "fetch_scale": round(scales["FETCH_SIZE"], 4), "write_scale": round(scales["WRITE_SIZE"], 4),
+                 "copy_bytes": COPY_BYTES}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out[name]))
+
+
+def parse_known_workload():
+    for i, a in enumerate(sys.argv):
+        if a == "--workload" and i + 1 < len(sys.argv):
+            return sys.argv[i + 1]
+        if a.startswith("--workload="):
+            return a.split("=", 1)[1]
+    return "llama8b_32k"
+
+
+def profile_summary(stats_csv, command):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel file."""
+    import csv
+    import re
+    lines = [f"Command: `{command}`", "", "| kernel | calls | avg us | min us | max us | total % |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in csv.DictReader(open(stats_csv)):
+        n = re.sub(r"\(anonymous namespace\)::|hsla::|void ", "", r["Name"])
+        n = re.sub(r"\(.*$", "", n)
+        lines.append(f"| `{n[:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    return "\n".join(lines)
 
 
 def cpu_baseline(wl, inp_q, gpu_out, gpu_sel, budget_s):
@@ -192,12 +285,8 @@ def cpu_baseline(wl, inp_q, gpu_out, gpu_sel, budget_s):
                 seconds=round(t_heads, 3), ms_per_step=round(step_s * 1e3, 1)), worst
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus above 1 is not supported "
-              "(the path shards by (sequence, kv head) with no exchange, see the design notes).", file=sys.stderr)
-        sys.exit(2)
+def setup(args, extra_steps):
+    """Inputs, R independent caches (built), prepared steps."""
     import torch
 
     import workloads as W
@@ -207,7 +296,7 @@ def main():
     torch.cuda.set_device(0)
     wl = workload(args.workload)
     steps, warm, R = args.steps, args.warmup, max(1, args.replicas)
-    appends_per_replica = -(-(2 * steps + warm) // R) + 1   # warmup, timed and profiled steps
+    appends_per_replica = -(-(extra_steps + warm) // R) + 1
     wl = W.dataclasses.replace(wl, append_room=1 + -(-appends_per_replica // wl.block_size))
     t0 = time.perf_counter()
     inp = W.make_inputs(wl, keep_pairs=False)
@@ -241,6 +330,33 @@ def main():
         qs.append(q)
         preps.append(PreparedDecodeStep(dc, q, k_tok, v_tok, out, sel))
     print(f"[bench] {R} caches built; build {np.mean(build_ms) * 1e3:.1f} us each", file=sys.stderr, flush=True)
+    return dict(wl=wl, inp=inp, caches=caches, preps=preps, qs=qs, build_ms=build_ms, hip=hip, stream=stream, R=R)
+
+
+def main():
+    args = parse()
+    if args.traffic_collect:
+        traffic_collect(*args.traffic_collect)
+        return
+    if args.profile_summary:
+        print(profile_summary(*args.profile_summary))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus above 1 is not supported "
+              "(the path shards by (sequence, kv head) with no exchange, see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from hybrid_sparse_linear_block_amd import hsla_profile
+
+    torch.cuda.set_device(0)
+    if args.traffic_run:
+        traffic_run(args)
+        return
+    steps, warm = args.steps, args.warmup
+    env = setup(args, 2 * steps)   # timed and profiled steps
+    wl, inp, caches, preps, qs = env["wl"], env["inp"], env["caches"], env["preps"], env["qs"]
+    build_ms, hip, stream, R = env["build_ms"], env["hip"], env["stream"], env["R"]
 
     # Spot check before any append: replica 0's decode at the prefilled length.
     out0, sel0 = caches[0].decode(qs[0])
@@ -263,9 +379,13 @@ def main():
     # Per-kernel breakdown: another K steps with an event before each kernel
     # (events without the system-scope fence, so the kernels run as in the
     # timed loop); reported separately, never folded into `value`.
+    # hsla_profile records an event before each decode kernel and one after
+    # the last; the append call is bracketed by two events of its own.  An
+    # interval between events includes the dispatch of its kernel, so it
+    # reads a few percent above the kernel's own duration in rocprofv3.
     nev = 8
     evs = [[hip.event(no_fence=True) for _ in range(nev)] for _ in range(steps)]
-    ev_app = [hip.event(no_fence=True) for _ in range(steps)]
+    ev_app = [(hip.event(no_fence=True), hip.event(no_fence=True)) for _ in range(steps)]
     profs = []
     for i in range(steps):
         pr = hsla_profile()
@@ -275,15 +395,15 @@ def main():
         profs.append(pr)
     torch.cuda.synchronize()
     for i in range(steps):
-        hip.record(ev_app[i], stream)
-        preps[i % R](profs[i])
+        hip.record(ev_app[i][0], stream)
+        preps[i % R](profs[i], between=lambda e=ev_app[i][1]: hip.record(e, stream))
     torch.cuda.synchronize()
     nrec = profs[0].recorded
     names = [profs[0].names[j].decode() for j in range(nrec - 1)]
     per_kernel = {n: float(np.mean([hip.ms(evs[i][j], evs[i][j + 1]) for i in range(steps)]) * 1e3)
                   for j, n in enumerate(names)}
-    per_kernel["append"] = float(np.mean([hip.ms(ev_app[i], evs[i][0]) for i in range(steps)]) * 1e3)
-    gpu_step_us = float(np.mean([hip.ms(ev_app[i], evs[i][nrec - 1]) for i in range(steps)]) * 1e3)
+    per_kernel["append"] = float(np.mean([hip.ms(ev_app[i][0], ev_app[i][1]) for i in range(steps)]) * 1e3)
+    gpu_step_us = float(np.mean([hip.ms(ev_app[i][0], evs[i][nrec - 1]) for i in range(steps)]) * 1e3)
 
     # Algorithmic bytes from each replica's selections at its final length.
     per_rep = []

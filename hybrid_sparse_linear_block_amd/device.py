@@ -128,7 +128,9 @@ class PreparedDecodeStep:
         self.byref = ctypes.byref
         self.prof_type = hsla_profile
 
-    def __call__(self, prof=None) -> None:
+    def __call__(self, prof=None, between=None) -> None:
+        """One step; `between`, if given, is called after the append was
+        enqueued and before the decode is."""
         dc = self.dc
         assert dc.max_seq_len + 1 <= dc.capacity_len
         cur, nxt = dc.cur, 1 - dc.cur
@@ -139,6 +141,8 @@ class PreparedDecodeStep:
             raise RuntimeError(f"hsla_append_token failed: {st}")
         dc.cur = nxt
         dc.host_lens += 1
+        if between is not None:
+            between()
         st = self.lib.hsla_decode(br(self.cfg), br(self.pool), br(self.state), self.q, self.lens[nxt], dc.batch,
                                   dc.max_seq_len, self.out, self.sel, self.ws, self.ws_bytes, self.stream,
                                   br(prof) if prof is not None else None)
