@@ -14,6 +14,7 @@
 // FMAs on VALU.
 // k_build_reduce: sums the chunk partials in chunk order (deterministic).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -40,48 +41,43 @@ struct BuildParams {
   size_t part_stride;
 };
 
-typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ int clamp_len(int T, int max_len) { return min(max(T, 0), max_len); }
 
-// Statistics of the full blocks inside a staged tile, channel c, values
-// fetched through get(t) for tile-relative token t.  Two passes: mean, then
-// the population variance around it.
-template <typename Get>
-__device__ __forceinline__ void tile_block_stats(const BuildParams& P, int b, int g, int D, int c,
-                                                 int tile0, int TT, int T, Get get) {
-  const int B = P.B;
-  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
-  for (int t0 = 0; t0 < TT; t0 += B) {
-    const int blk = (tile0 + t0) / B;
-    if ((blk + 1) * B > T) break;
-    float s = 0.f;
-    for (int t = 0; t < B; ++t) s += get(t0 + t);
-    const float mu = s / static_cast<float>(B);
-    float q = 0.f;
-    for (int t = 0; t < B; ++t) {
-      const float dlt = get(t0 + t) - mu;
-      q = fmaf(dlt, dlt, q);
-    }
-    const size_t off = (static_cast<size_t>(bt[blk]) * P.Hkv + g) * D + c;
-    P.blk_mean[off] = mu;
-    P.blk_var[off] = q / static_cast<float>(B);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // bf16: MFMA
 // ---------------------------------------------------------------------------
-template <int D, int TT>
-__global__ __launch_bounds__(kThreads) void k_build_bf16(BuildParams P) {
-  constexpr int LD = TT + kPad;                    // LDS row length (bf16)
-  constexpr int TASKS = (TT / 8) * (D / 8) * 2;    // 8x8 sub-tiles of K and V
-  constexpr int TPT = (TASKS + kThreads - 1) / kThreads;
+// One workgroup per (sequence, kv head, chunk of tokens); tiles of 64 tokens.
+// Thread task = 8 tokens x 8 channels of K or V (eight 16-byte row loads of
+// one page); the 8 x 8 block is transposed in registers and stored
+// channel-major in LDS, so that
+//   * the MFMA operands (8 consecutive tokens of one channel) are single
+//     16-byte LDS reads: S += K^T V with v_mfma_f32_32x32x16_bf16, wave
+//     (wi, wj) owning a D/2 x D/2 quarter of S;
+//   * thread c < D reads channel c of K as contiguous vectors for the block
+//     statistics (two-pass within the tile, combined across the tiles of a
+//     block larger than 64 tokens by the pairwise update of Chan et al.) and
+//     threads D..2D-1 sum V for sv.
+// The chunk's block-table entries are staged in LDS once; every load is
+// unconditional (rows past the end are read from a mapped page and zeroed),
+// and three tiles are in flight while one is processed.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kTile = 64;           // tokens per tile
+constexpr int kMaxChunkBlocks = 256;  // block-table entries staged per chunk
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void k_build_bf16(BuildParams P) {
+  constexpr int LD = kTile + kPad;                 // LDS row length (bf16)
+  constexpr int TASKS = (kTile / 8) * (D / 8) * 2;
+  static_assert(TASKS % kThreads == 0 || kThreads % TASKS == 0, "whole tasks per thread");
+  constexpr int TPT = TASKS >= kThreads ? TASKS / kThreads : 1;   // tasks per thread
+  constexpr bool kPartial = TASKS < kThreads;      // D = 64: waves 2, 3 have no load task
   constexpr int TI = D / 64;                       // 32x32 tiles per wave, each dim
-  extern __shared__ uint16_t lds[];
-  uint16_t* Kt = lds;                              // [D][LD] channel-major
-  uint16_t* Vt = lds + D * LD;
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * LD];   // [D][LD] channel-major
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * LD];
+  __shared__ int32_t pages[kMaxChunkBlocks];
 
   const int pair = blockIdx.y;
   const int b = pair / P.Hkv;
@@ -90,11 +86,21 @@ __global__ __launch_bounds__(kThreads) void k_build_bf16(BuildParams P) {
   const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
   const int c_begin = chunk * P.chunk;
   const int c_end = min(c_begin + P.chunk, T);
+  if (c_begin >= c_end) {
+    // still write a zero partial so that the reduction reads defined data
+    float* part = P.ws + (static_cast<size_t>(pair) * P.nchunk + chunk) * P.part_stride;
+    for (int i = threadIdx.x; i < D * D + 2 * D; i += kThreads) part[i] = 0.f;
+    return;
+  }
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
-  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
   const int B = P.B;
+  const int blk0 = c_begin / B;                             // chunks start on block boundaries
+  const int nblk = ceil_div(c_end - c_begin, B);            // blocks touched by the chunk
+  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  for (int i = tid; i < nblk; i += kThreads) pages[i] = bt[blk0 + i];
+  __syncthreads();
 
   f32x16_t acc[TI][TI];
 #pragma unroll
@@ -103,99 +109,170 @@ __global__ __launch_bounds__(kThreads) void k_build_bf16(BuildParams P) {
     for (int j = 0; j < TI; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  float csum = 0.f;  // z (threads < D) or sv (threads D..2D-1) partial
+  float csum = 0.f;                   // z (threads < D) or sv (threads D..2D-1) partial
+  float run_mean = 0.f, run_m2 = 0.f; // statistics of a block spanning tiles (B > 64)
+  int run_n = 0;
 
-  uint4 buf[TPT][8];
-  auto load_tile = [&](int tile0) {
+  const char* kbase = reinterpret_cast<const char*>(P.k_pages);
+  const char* vbase = reinterpret_cast<const char*>(P.v_pages);
+  struct TileRegs {
+    uint4 w[TPT][8];
+  };
+  auto load_tile = [&](int tile0, TileRegs& x) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < TPT; ++x) {
-      const int task = tid + x * kThreads;
-      if (task < TASKS) {
-        const int tensor = task / ((TT / 8) * (D / 8));
-        const int rem = task % ((TT / 8) * (D / 8));
-        const int tg = rem / (D / 8);
-        const int cg = rem % (D / 8);
-        const char* base = reinterpret_cast<const char*>(tensor ? P.v_pages : P.k_pages);
+    for (int u = 0; u < TPT; ++u) {
+      const int task = tid + u * kThreads;
+      if (kPartial && task >= TASKS) break;
+      const int tensor = task / ((kTile / 8) * (D / 8));
+      const int rem = task % ((kTile / 8) * (D / 8));
+      const int tg = rem / (D / 8);
+      const int cg = rem % (D / 8);
+      // first token of the group, clamped to the last group that holds a
+      // token (a multiple of 8, so the 8 rows stay inside one page)
+      const int t8 = min(tile0 + tg * 8, (c_end - 1) & ~7);
+      const int page = pages[(t8 - c_begin) / B];
+      const int row0 = t8 % B;                                 // 8 | B: the group is in one page
+      const char* base = (tensor ? vbase : kbase) +
+                         (((static_cast<size_t>(page) * P.Hkv + g) * B + row0) * D + cg * 8) * 2;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int t = tile0 + tg * 8 + r;
-          if (t < c_end) {
-            const size_t row = (static_cast<size_t>(bt[t / B]) * P.Hkv + g) * B + (t % B);
-            buf[x][r] = *reinterpret_cast<const uint4*>(base + (row * D + cg * 8) * 2);
-          } else {
-            buf[x][r] = make_uint4(0, 0, 0, 0);
-          }
+      for (int r = 0; r < 8; ++r) x.w[u][r] = *reinterpret_cast<const uint4*>(base + r * D * 2);
+    }
+  };
+  auto store_tile = [&](int tile0, const TileRegs& x) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int task = tid + u * kThreads;
+      if (kPartial && task >= TASKS) break;
+      const int tensor = task / ((kTile / 8) * (D / 8));
+      const int rem = task % ((kTile / 8) * (D / 8));
+      const int tg = rem / (D / 8);
+      const int cg = rem % (D / 8);
+      uint16_t* dst = tensor ? Vt : Kt;
+      uint32_t w[8][4];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const bool live = tile0 + tg * 8 + r < c_end;   // rows past the end enter as zero
+        w[r][0] = live ? x.w[u][r].x : 0u;
+        w[r][1] = live ? x.w[u][r].y : 0u;
+        w[r][2] = live ? x.w[u][r].z : 0u;
+        w[r][3] = live ? x.w[u][r].w : 0u;
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t a = w[2 * j][c / 2];
+          const uint32_t bb = w[2 * j + 1][c / 2];
+          o[j] = (c & 1) ? __builtin_amdgcn_perm(bb, a, 0x07060302u) : __builtin_amdgcn_perm(bb, a, 0x05040100u);
         }
+        *reinterpret_cast<uint4*>(dst + (cg * 8 + c) * LD + tg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
   };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int x = 0; x < TPT; ++x) {
-      const int task = tid + x * kThreads;
-      if (task < TASKS) {
-        const int tensor = task / ((TT / 8) * (D / 8));
-        const int rem = task % ((TT / 8) * (D / 8));
-        const int tg = rem / (D / 8);
-        const int cg = rem % (D / 8);
-        uint16_t* dst = tensor ? Vt : Kt;
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(buf[x]);  // [r][4]
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          uint32_t o[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t a = w[(2 * j) * 4 + c / 2];
-            const uint32_t bb = w[(2 * j + 1) * 4 + c / 2];
-            o[j] = (c & 1) ? ((a >> 16) | (bb & 0xffff0000u)) : ((a & 0xffffu) | (bb << 16));
-          }
-          *reinterpret_cast<uint4*>(dst + (cg * 8 + c) * LD + tg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-      }
-    }
-  };
 
-  if (c_begin < c_end) load_tile(c_begin);
-  for (int tile0 = c_begin; tile0 < c_end; tile0 += TT) {
+  // Three tiles in flight.  The loop runs a multiple of three tiles so that
+  // every buffer is named statically (no load stays in flight across a
+  // branch); tiles past the chunk end load clamped rows and contribute zero.
+  const int ntile = ceil_div(c_end - c_begin, kTile);
+  const int nrun = ceil_div(ntile, 3) * 3;
+  TileRegs r0, r1, r2;
+  load_tile(c_begin, r0);
+  load_tile(c_begin + kTile, r1);
+  load_tile(c_begin + 2 * kTile, r2);
+  auto tile_step = [&](int it, TileRegs& buf) __attribute__((always_inline)) {
+    const int tile0 = c_begin + it * kTile;
+    __syncthreads();   // the previous tile's LDS reads are done
+    store_tile(tile0, buf);
     __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (tile0 + TT < c_end) load_tile(tile0 + TT);
+    load_tile(tile0 + 3 * kTile, buf);   // refill the buffer just stored
 
-    // Per-channel sums and the statistics of full blocks.
+    // ---- sums of K and V per channel; block statistics of K
     if (tid < 2 * D) {
-      const uint16_t* row = (tid < D ? Kt + tid * LD : Vt + (tid - D) * LD);
-      for (int t = 0; t < TT; t += 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(row + t);
-        csum += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
-                bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
-      }
+      const uint16_t* row = tid < D ? Kt + tid * LD : Vt + (tid - D) * LD;
+      uint4 q[kTile / 8];
+#pragma unroll
+      for (int v = 0; v < kTile / 8; ++v) q[v] = *reinterpret_cast<const uint4*>(row + v * 8);
+      auto xt = [&](int t) -> float {   // token t of the tile (t is a constant after unrolling)
+        const uint4 w = q[t / 8];
+        const uint32_t u = (t % 8) / 2 == 0 ? w.x : (t % 8) / 2 == 1 ? w.y : (t % 8) / 2 == 2 ? w.z : w.w;
+        return (t % 2) ? bf16_hi(u) : bf16_lo(u);
+      };
+#pragma unroll
+      for (int t = 0; t < kTile; ++t) csum += xt(t);
       if (tid < D) {
-        tile_block_stats(P, b, g, D, tid, tile0, TT, T, [&](int t) {
-          return __uint_as_float(static_cast<uint32_t>(row[t]) << 16);
-        });
+        auto stats = [&](auto seg_c) __attribute__((always_inline)) {
+          constexpr int SEG = decltype(seg_c)::value;   // tokens of one block inside the tile
+#pragma unroll
+          for (int s0 = 0; s0 < kTile; s0 += SEG) {
+            const int blk = (tile0 + s0) / B;
+            float sm = 0.f;
+#pragma unroll
+            for (int t = 0; t < SEG; ++t) sm += xt(s0 + t);
+            const float mu = sm / static_cast<float>(SEG);
+            float m2 = 0.f;
+#pragma unroll
+            for (int t = 0; t < SEG; ++t) {
+              const float dlt = xt(s0 + t) - mu;
+              m2 = fmaf(dlt, dlt, m2);
+            }
+            // fold the segment into its block (a new block starts the run)
+            if (run_n == 0) {
+              run_mean = mu;
+              run_m2 = m2;
+            } else {
+              const float n_a = static_cast<float>(run_n);
+              const float n_b = static_cast<float>(SEG);
+              const float dl = mu - run_mean;
+              run_mean = run_mean + dl * (n_b / (n_a + n_b));
+              run_m2 = run_m2 + m2 + dl * dl * (n_a * n_b / (n_a + n_b));
+            }
+            run_n += SEG;
+            if (run_n == B) {   // the block is complete
+              // only blocks that end inside the chunk (c_end <= T): the
+              // padding tiles past the chunk reach blocks whose pages are
+              // not staged
+              if ((blk + 1) * B <= c_end) {
+                const size_t off = (static_cast<size_t>(pages[blk - blk0]) * P.Hkv + g) * D + tid;
+                P.blk_mean[off] = run_mean;
+                P.blk_var[off] = run_m2 / static_cast<float>(B);
+              }
+              run_n = 0;
+            }
+          }
+        };
+        if (B == 16)
+          stats(std::integral_constant<int, 16>{});
+        else if (B == 32)
+          stats(std::integral_constant<int, 32>{});
+        else
+          stats(std::integral_constant<int, kTile>{});
       }
     }
 
-    // S += K^T V over the tile: wave (wi, wj) owns rows wi*TI*32.. and
-    // columns wj*TI*32.. of S.
+    // ---- S += K^T V over the tile
     const int rbase = (wave / 2) * TI * 32;
     const int cbase = (wave % 2) * TI * 32;
-    const int kl = (lane / 32) * 4;
-#pragma unroll 2
-    for (int k0 = 0; k0 < TT; k0 += 8) {
-      short4_t a[TI], bv[TI];
+    const int kl = (lane / 32) * 8;
+#pragma unroll
+    for (int k0 = 0; k0 < kTile; k0 += 16) {
+      bf16x8_t a[TI], bv[TI];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        a[i] = *reinterpret_cast<const short4_t*>(Kt + (rbase + i * 32 + lane % 32) * LD + k0 + kl);
-        bv[i] = *reinterpret_cast<const short4_t*>(Vt + (cbase + i * 32 + lane % 32) * LD + k0 + kl);
+        a[i] = *reinterpret_cast<const bf16x8_t*>(Kt + (rbase + i * 32 + lane % 32) * LD + k0 + kl);
+        bv[i] = *reinterpret_cast<const bf16x8_t*>(Vt + (cbase + i * 32 + lane % 32) * LD + k0 + kl);
       }
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a[i], bv[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bv[j], acc[i][j], 0, 0, 0);
     }
+  };
+  for (int it = 0; it < nrun; it += 3) {
+    tile_step(it, r0);
+    tile_step(it + 1, r1);
+    tile_step(it + 2, r2);
   }
 
   // Chunk partial: S (D*D), z (D), sv (D).
@@ -344,29 +421,13 @@ __global__ __launch_bounds__(kThreads) void k_build_reduce(BuildParams P) {
   *reinterpret_cast<float4*>(dst) = s;
 }
 
-template <int D, int TT>
-hipError_t launch_bf16(const Problem& p, const BuildLayout& L, const BuildParams& P, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(2) * D * (TT + kPad) * sizeof(uint16_t);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_build_bf16<D, TT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-  }
-  dim3 grid(L.nchunk, p.batch * p.Hkv);
-  hipLaunchKernelGGL((k_build_bf16<D, TT>), grid, dim3(kThreads), lds, s, P);
-  return launch_status("k_build_bf16");
-}
-
 template <int D>
 hipError_t launch_d(const Problem& p, const BuildLayout& L, const BuildParams& P, hipStream_t s) {
   hipError_t e;
   if (p.bf16) {
-    switch (L.tile) {
-      case 64: e = launch_bf16<D, 64>(p, L, P, s); break;
-      case 128: e = launch_bf16<D, 128>(p, L, P, s); break;
-      case 256: e = launch_bf16<D, 256>(p, L, P, s); break;
-      default: return hipErrorInvalidValue;
-    }
+    dim3 grid(L.nchunk, p.batch * p.Hkv);
+    hipLaunchKernelGGL((k_build_bf16<D>), grid, dim3(kThreads), 0, s, P);
+    e = launch_status("k_build_bf16");
   } else {
     dim3 grid(L.nchunk, p.batch * p.Hkv);
     hipLaunchKernelGGL((k_build_f32<D>), grid, dim3(kThreads), 0, s, P);
@@ -387,13 +448,15 @@ hipError_t launch_d(const Problem& p, const BuildLayout& L, const BuildParams& P
 
 BuildLayout build_layout(const Problem& p) {
   BuildLayout L{};
-  L.tile = p.bf16 ? std::max(64, p.B) : 32;
+  L.tile = p.bf16 ? kTile : 32;
   const long pairs = static_cast<long>(p.batch) * p.Hkv;
-  // Aim for >= 256 workgroups; chunks of at most 4096 tokens.
-  long want = (pairs * p.max_seq_len) / 256;
-  long chunk = L.tile;
-  while (chunk * 2 <= want && chunk * 2 <= 4096) chunk *= 2;
-  if (chunk < L.tile) chunk = L.tile;
+  // About two workgroups per CU (512); chunks are whole blocks and whole
+  // tiles, at most 4096 tokens and at most kMaxChunkBlocks blocks.
+  const long want = (pairs * p.max_seq_len) / 512;
+  const long unit = std::max<long>(L.tile, p.B);
+  const long cap = std::min<long>(4096, static_cast<long>(kMaxChunkBlocks) * p.B);
+  long chunk = unit;
+  while (chunk * 2 <= want && chunk * 2 <= cap) chunk *= 2;
   L.chunk = static_cast<int>(chunk);
   L.nchunk = ceil_div(p.max_seq_len, L.chunk);
   L.part_stride = static_cast<size_t>(p.D) * p.D + 2 * p.D;

@@ -1093,7 +1093,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     const int t = x.t0 + n16;
     const bool valid = t < T;
     const bool sw = t < ns || t >= win0;
-    bool changed = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * q4 + i;
@@ -1102,7 +1101,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
       const float sv = inc ? P.sigma * sc[i] : kNegInf;
       const float mnew = fmaxf(m_run[i], row16_max(sv));
       const float cf = (mnew == m_run[i]) ? 1.f : fast_exp(m_run[i] - mnew);
-      changed |= (h < G) && (cf != 1.f);
       m_run[i] = mnew;
       if (h < G) {
         s_pub[wave][h][n16] = sv;
