@@ -37,7 +37,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr float kNegInf = -INFINITY;
 constexpr int kScoreChunk = 64;  // candidates per scoring workgroup
-constexpr int kRoRows = 16;      // rows of S per readout workgroup
+constexpr int kRoRows = 32;      // rows of S per readout workgroup
 constexpr int kUnit = 64;        // tokens per attention work unit
 // Attention workgroups per launch: two per compute unit of MI355X (256
 // CUs), so that every CU carries the same number of splits.
@@ -167,8 +167,8 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
     v0[it] = *reinterpret_cast<const float4*>(P.blk_var + off);
     v1[it] = *reinterpret_cast<const float4*>(P.blk_var + off + 4);
   }
-  // sigma q and (sigma^2 / 2) q^2: the score is then two plain dot products.
-  float qs[G][8], qq[G][8];
+  // sigma q; the score is sigma q . mu + log(1 + sum_c (sigma q_c)^2 / 2 var_c).
+  float qs[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     QReg<KV> qr;
@@ -177,10 +177,7 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
     float qf[8];
     qr.to_f32(qf);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      qs[h][i] = P.sigma * qf[i];
-      qq[h][i] = 0.5f * qs[h][i] * qs[h][i];
-    }
+    for (int i = 0; i < 8; ++i) qs[h][i] = P.sigma * qf[i];
   }
   const int hsel = lig % G;   // the head whose score this lane finishes
 #pragma unroll
@@ -194,8 +191,9 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         a = fmaf(qs[h][i], mu[i], a);
-        c = fmaf(qq[h][i], va[i], c);
+        c = fmaf(qs[h][i] * qs[h][i], va[i], c);
       }
+      c *= 0.5f;
       a = reduce_sum_lanes<LPT>(a);
       c = reduce_sum_lanes<LPT>(c);
       d1 = (h == hsel) ? a : d1;
