@@ -384,14 +384,26 @@ __device__ __forceinline__ void radix_pick(const uint4 c4, int lane, int& digit,
 // with a 256-bin histogram private to the wavefront (no workgroup barrier).
 // KPL > 0: lane l holds keys l, l + 64, ... in registers; KPL == 0: keys
 // are read through key_at on every pass.
+// With keys in registers and k <= 64, the smallest of the 64 lane maxima is
+// a lower bound of the k-th largest key (each lane holds one key at least
+// that large), so only keys at or above it take part; they are few and
+// rarely share a radix bin.
 template <int KPL, typename KeyAt>
 __device__ __forceinline__ void wave_topk_threshold(const uint32_t* key, KeyAt key_at, int n, int k, int lane,
                                                     uint32_t* hist, uint32_t& thr, int& rem) {
   uint32_t kmin = 0xffffffffu, kmax = 0u;
+  uint32_t floor_key = 0u;   // keys below it cannot be among the k largest
   if constexpr (KPL > 0) {
+    if (k <= kWave && n >= kWave) {
+      uint32_t lmax = 0u;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j)
+        if (lane + kWave * j < n) lmax = max(lmax, key[j]);
+      floor_key = wave_min_u32(lmax);   // every lane holds a key (n >= 64)
+    }
 #pragma unroll
     for (int j = 0; j < KPL; ++j)
-      if (lane + kWave * j < n) {
+      if (lane + kWave * j < n && key[j] >= floor_key) {
         kmin = min(kmin, key[j]);
         kmax = max(kmax, key[j]);
       }
@@ -419,7 +431,8 @@ __device__ __forceinline__ void wave_topk_threshold(const uint32_t* key, KeyAt k
     if constexpr (KPL > 0) {
 #pragma unroll
       for (int j = 0; j < KPL; ++j)
-        if (lane + kWave * j < n && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+        if (lane + kWave * j < n && key[j] >= floor_key && (key[j] & mask) == prefix)
+          atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
     } else {
       for (int i = lane; i < n; i += kWave) {
         const uint32_t x = key_at(i);
@@ -452,6 +465,22 @@ __device__ __forceinline__ void head_select(KeyAt key_at, int nc, int k, int nwo
   int rem = k;
   if (!take_all && !take_none) wave_topk_threshold<KPL>(key, key_at, nc, k, lane, hist, thr, rem);
   int nsel = 0, neq = 0;
+  // When every key equal to the threshold is taken, the selection is just
+  // key >= thr and no rank among equal keys is needed.
+  bool simple = take_all || take_none;
+  if (!simple) {
+    int eq_total = 0;
+    if constexpr (KPL > 0) {
+#pragma unroll
+      for (int w = 0; w < KPL; ++w) eq_total += __popcll(__ballot(w * kWave + lane < nc && key[w] == thr));
+    } else {
+      for (int w = 0; w < nwords; ++w) {
+        const int i = w * kWave + lane;
+        eq_total += __popcll(__ballot(i < nc && key_at(i) == thr));
+      }
+    }
+    simple = eq_total == rem;
+  }
   auto word = [&](int w, uint32_t x) {
     const int i = w * kWave + lane;
     const bool valid = i < nc;
@@ -460,6 +489,8 @@ __device__ __forceinline__ void head_select(KeyAt key_at, int nc, int k, int nwo
       sel = false;
     } else if (take_all) {
       sel = valid;
+    } else if (simple) {
+      sel = valid && x >= thr;
     } else {
       const bool eq = valid && x == thr;
       const uint64_t eqm = __ballot(eq);
