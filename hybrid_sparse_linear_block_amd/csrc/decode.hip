@@ -42,7 +42,6 @@ constexpr int kUnit = 64;        // tokens per attention work unit
 // Attention workgroups per launch: two per compute unit of MI355X (256
 // CUs), so that every CU carries the same number of splits.
 constexpr int kAttendWgsTarget = 2 * 256;
-constexpr size_t kKeysStageBytes = 16 * 1024;   // order keys staged in LDS up to this size
 constexpr size_t kBtStageBytes = 8 * 1024;      // block-table row staged in LDS up to this size
 
 struct DecodeParams {
@@ -61,15 +60,14 @@ struct DecodeParams {
   uint32_t* keys;   // block-score order keys [batch, Hq, sstride]
   float* ro;
   float* roz;
-  int32_t* ulist;   // union entries [pairs, umax]: block | head mask << 20
-  int32_t* upage;   // their pages [pairs, umax]
+  uint64_t* bits;   // per-head selection bitmaps [batch, Hq, nwords]
   int32_t* ucount;
   float* part;
   int Hq, Hkv, B, top_k, ns, W, linear_tail;
   int max_blocks, max_seq_len, nc_max, nblk_max;
   int score_wgs, ro_wgs;
   int umax, bps, max_split, pstride;
-  int sstride, nwords, keys_staged, bt_staged;
+  int sstride, nwords, bt_staged;
   SelLayout sl;
   float sigma;
 };
@@ -518,159 +516,193 @@ __device__ __forceinline__ void head_select(KeyAt key_at, int nc, int k, int nwo
     for (int j = nsel + lane; j < k; j += kWave) out[j] = -1;
 }
 
-// Selection of one (sequence, kv head), one workgroup: stage the G heads'
-// order keys and the block-table row in LDS (every load of a round issued
-// before any store), top-k per head (wavefront w takes heads w, w + 4, ...),
-// then the union in ascending block order -- blocks below the candidates
-// (sinks), candidates selected by some head or holding sink or window
-// tokens, blocks past the candidates (window) -- written as entries
-// block | (mask of the heads that selected it) << 20 with their pages.
-template <int G>
-__global__ __launch_bounds__(kThreads) void k_select(DecodeParams P) {
-  constexpr int NW = kThreads / kWave;
-  extern __shared__ uint64_t dyn_lds[];
-  char* smem = reinterpret_cast<char*>(dyn_lds);
-  const int pair = blockIdx.x;
-  const int b = pair / P.Hkv;
-  const int g = pair % P.Hkv;
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+// Selection of one (sequence, query head), one wavefront: the head's order
+// keys straight into registers (KPL per lane; KPL = 0 reads them through
+// memory on every pass), the threshold, then the head's selection bitmap
+// (word w, bit i: candidate 64 w + i) and its selected block indices.
+template <int KPL>
+__global__ __launch_bounds__(kWave) void k_select(DecodeParams P) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+  const int bh = blockIdx.x;
+  const int b = bh / P.Hq;
+  const int lane = threadIdx.x;
   const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
-  uint64_t* bits = reinterpret_cast<uint64_t*>(smem + P.sl.bits);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(smem + P.sl.hist) + wave * 256;
-  uint64_t* umask = reinterpret_cast<uint64_t*>(smem + P.sl.umask);
-  uint32_t* keys = reinterpret_cast<uint32_t*>(smem + P.sl.keys);
-  int32_t* btrow = reinterpret_cast<int32_t*>(smem + P.sl.btrow);
-
   const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
   const int nc = min(cr.count, P.nc_max);
-  const int nwords = P.nwords;
-  const int nb = min(ceil_div(T, P.B), P.nblk_max);
-  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
-  const uint32_t* key0 = P.keys + (static_cast<size_t>(b) * P.Hq + g * G) * P.sstride;
-
-  if (P.keys_staged) {
-    const uint4* src = reinterpret_cast<const uint4*>(key0);
-    uint4* dst = reinterpret_cast<uint4*>(keys);
-    const int n4 = G * P.sstride / 4;
-    for (int base = 0; base < n4; base += 4 * kThreads) {
-      uint4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = src[min(base + tid + u * kThreads, n4 - 1)];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (base + tid + u * kThreads < n4) dst[base + tid + u * kThreads] = v[u];
-    }
-  }
-  if (P.bt_staged) {
-    for (int base = 0; base < nb; base += 4 * kThreads) {
-      int v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = bt[min(base + tid + u * kThreads, nb - 1)];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (base + tid + u * kThreads < nb) btrow[base + tid + u * kThreads] = v[u];
-    }
-  }
-  __syncthreads();
-
-  for (int hh = wave; hh < G; hh += NW) {
-    int32_t* out = P.sel_idx ? P.sel_idx + (static_cast<size_t>(b) * P.Hq + g * G + hh) * P.top_k : nullptr;
-    uint64_t* brow = bits + hh * nwords;
-    if (P.keys_staged) {
-      const uint32_t* kh = keys + hh * P.sstride;
-      auto key_at = [&](int i) -> uint32_t { return kh[i]; };
-      if (nc <= 4 * kWave)
-        head_select<4>(key_at, nc, P.top_k, nwords, lane, hist, brow, out, cr.lo);
-      else if (nc <= 8 * kWave)
-        head_select<8>(key_at, nc, P.top_k, nwords, lane, hist, brow, out, cr.lo);
-      else if (nc <= 16 * kWave)
-        head_select<16>(key_at, nc, P.top_k, nwords, lane, hist, brow, out, cr.lo);
-      else
-        head_select<0>(key_at, nc, P.top_k, nwords, lane, hist, brow, out, cr.lo);
-    } else {
-      const uint32_t* kh = key0 + static_cast<size_t>(hh) * P.sstride;
-      auto key_at = [&](int i) -> uint32_t { return kh[i]; };
-      head_select<0>(key_at, nc, P.top_k, nwords, lane, hist, brow, out, cr.lo);
-    }
-  }
-  __syncthreads();
-
-  const int win0 = T - P.W;
-  auto in_union = [&](int j, int& hm) -> bool {
-    hm = 0;
-    if (j >= nb) return false;
-    if (nc == 0 || j < cr.lo || j >= cr.lo + nc) return true;
-    const int c = j - cr.lo;
-#pragma unroll
-    for (int x = 0; x < G; ++x) hm |= static_cast<int>((bits[x * nwords + (c >> 6)] >> (c & 63)) & 1ull) << x;
-    const bool overlap = (j * P.B < P.ns) || ((j + 1) * P.B > win0);
-    return hm != 0 || overlap;
-  };
-  int32_t* ul = P.ulist + static_cast<size_t>(pair) * P.umax;
-  int32_t* up = P.upage + static_cast<size_t>(pair) * P.umax;
-  const int nch = ceil_div(nb, kWave);
-  // Chunk c = blocks 64 c .. 64 c + 63: inclusion masks (LDS, up to 64
-  // chunks per round), prefix counts by one scan, then every lane writes its
-  // block's entry at its position.
-  int done = 0;   // union entries of the chunks before this round
-  for (int c0 = 0; c0 < nch; c0 += kWave) {
-    const int ncr = min(kWave, nch - c0);
-    for (int c = wave; c < ncr; c += NW) {
-      int hm;
-      const uint64_t m = __ballot(in_union((c0 + c) * kWave + lane, hm));
-      if (lane == 0) umask[c] = m;
-    }
-    __syncthreads();
-    const uint64_t mymask = lane < ncr ? umask[lane] : 0ull;
-    const uint32_t cnt_c = static_cast<uint32_t>(__popcll(mymask));
-    const uint32_t incl = wave_scan_incl(cnt_c);
-    const int total = __builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1);
-    for (int c = wave; c < ncr; c += NW) {
-      const int base = done + __builtin_amdgcn_readlane(static_cast<int>(incl - cnt_c), c);
-      const uint64_t m = umask[c];
-      const int j = (c0 + c) * kWave + lane;
-      if ((m >> lane) & 1ull) {
-        const int pos = base + __popcll(m & lanes_below(lane));
-        if (pos < P.umax) {
-          int hm;
-          in_union(j, hm);
-          ul[pos] = j | (hm << 20);
-          up[pos] = P.bt_staged ? btrow[j] : bt[j];
-        }
-      }
-    }
-    done += total;
-    __syncthreads();   // umask is reused by the next round
-  }
-  if (tid == 0) P.ucount[pair] = min(done, P.umax);
+  const uint32_t* kh = P.keys + static_cast<size_t>(bh) * P.sstride;
+  auto key_at = [&](int i) -> uint32_t { return kh[i]; };
+  int32_t* out = P.sel_idx ? P.sel_idx + static_cast<size_t>(bh) * P.top_k : nullptr;
+  head_select<KPL>(key_at, nc, P.top_k, P.nwords, lane, hist, P.bits + static_cast<size_t>(bh) * P.nwords, out,
+                   cr.lo);
 }
 
-// The split's share of the union: split s takes entries s, s + S, s + 2S,
-// ... (S = max_split), so window and sink blocks, which every head of the
-// group needs, spread over the splits instead of piling into the last one.
-// Lane e < ne holds entry e and its page; the count and the entries come in
-// one round trip.
+// The split's share of the union, built by the attention workgroup itself
+// from the G heads' selection bitmaps: the union of the group's exact blocks
+// in ascending block order -- blocks below the candidates (sinks),
+// candidates selected by some head or holding sink or window tokens, blocks
+// past the candidates (window) -- of which split s takes positions s, s + S,
+// s + 2S, ... (S = max_split), so window and sink blocks, which every head
+// needs, spread over the splits.  One round trip brings the bitmaps and the
+// sequence's block-table row into LDS (`smem`, laid out by SelLayout); one
+// barrier later every wavefront forms the 64-block chunk masks in registers
+// (lane c: chunk c), scans their counts and, by a binary search over the
+// chunk prefixes and a rank search in the chunk's mask, gives lane e < ne its
+// entry (block | mask of the heads that selected it << 20) and page.  Has a
+// workgroup barrier: every thread calls it.  Split 0 also records the union
+// size for the merge.
 struct SplitShare {
   int ent;
   int page;    // -1 on lanes past ne
   int count;   // union size (uniform)
   int ne;      // entries of this split (uniform)
 };
-__device__ __forceinline__ SplitShare load_share(const DecodeParams& P, int pair, int split, int lane) {
-  const int ent_at = split + lane * P.max_split;
-  const bool ent_in = lane < P.bps && ent_at < P.umax;
-  const size_t off = static_cast<size_t>(pair) * P.umax + (ent_in ? ent_at : 0);
+template <int G, typename Stage>
+__device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, int b, int g, int T, int split,
+                                  Stage&& stage) {
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  uint64_t* bits = reinterpret_cast<uint64_t*>(smem + P.sl.bits);
+  uint64_t* umask = reinterpret_cast<uint64_t*>(smem + P.sl.umask) + wave * kWave;
+  int32_t* upre = reinterpret_cast<int32_t*>(smem + P.sl.upre) + wave * kWave;
+  int32_t* btrow = reinterpret_cast<int32_t*>(smem + P.sl.btrow);
+  const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
+  const int nc = min(cr.count, P.nc_max);
+  const int nwords = P.nwords;
+  const int nb = min(ceil_div(T, P.B), P.nblk_max);
+  const int S = P.max_split;
+  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+
+  // ---- bitmaps and block-table row.  The first round of both is loaded
+  // together with the caller's own staging (`stage`, e.g. the query), so
+  // that the usual sizes take a single round trip; larger rows loop on.
+  {
+    const uint64_t* src = P.bits + (static_cast<size_t>(b) * P.Hq + g * G) * nwords;
+    const int nbits = G * nwords;
+    const int nbt = P.bt_staged ? nb : 0;
+    uint64_t v[2];
+    int w[4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) v[u] = src[min(tid + u * kThreads, nbits - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = bt[min(tid + u * kThreads, nb - 1)];
+    stage();
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (tid + u * kThreads < nbits) bits[tid + u * kThreads] = v[u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (tid + u * kThreads < nbt) btrow[tid + u * kThreads] = w[u];
+    for (int base = 2 * kThreads; base < nbits; base += 2 * kThreads) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) v[u] = src[min(base + tid + u * kThreads, nbits - 1)];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (base + tid + u * kThreads < nbits) bits[base + tid + u * kThreads] = v[u];
+    }
+    for (int base = 4 * kThreads; base < nbt; base += 4 * kThreads) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = bt[min(base + tid + u * kThreads, nb - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (base + tid + u * kThreads < nbt) btrow[base + tid + u * kThreads] = w[u];
+    }
+  }
+  __syncthreads();
+
+  // Union membership of block j: every block when there are no candidates;
+  // otherwise blocks below a1 (sink tokens) or from a2 on (window tokens)
+  // and candidates some head selected.
+  const int a1 = nc > 0 ? ceil_div(P.ns, P.B) : nb;
+  const int a2 = nc > 0 ? (T - P.W) / P.B : nb;   // T - W > ns >= 0 here
+  auto head_mask = [&](int j) -> int {   // heads that selected candidate j
+    const int c = j - cr.lo;
+    int hm = 0;
+    if (nc > 0 && c >= 0 && c < nc) {
+#pragma unroll
+      for (int x = 0; x < G; ++x)
+        hm |= static_cast<int>((bits[x * nwords + (c >> 6)] >> (c & 63)) & 1ull) << x;
+    }
+    return hm;
+  };
+  // Lanes of blocks [j0, j0 + 64) inside [x, y), as a bit mask.
+  auto range_bits = [](int j0, int x, int y) -> uint64_t {
+    const int lo = min(max(x - j0, 0), kWave);
+    const int hi = min(max(y - j0, 0), kWave);
+    if (hi <= lo) return 0ull;
+    const uint64_t upto = hi == kWave ? ~0ull : ((1ull << hi) - 1ull);
+    return upto & ~((1ull << lo) - 1ull);
+  };
+  // Selected candidates among blocks [j0, j0 + 64): the bitmaps are indexed
+  // by candidate (block - lo), so each head's two overlapping words are
+  // shifted into place.
+  auto cand_bits = [&](int j0) -> uint64_t {
+    if (nc == 0) return 0ull;
+    const int a = j0 - cr.lo;
+    const int kw = a >> 6;   // floor
+    const int sh = a & 63;
+    uint64_t m = 0ull;
+#pragma unroll
+    for (int x = 0; x < G; ++x) {
+      const uint64_t* row = bits + x * nwords;
+      const uint64_t w0 = (kw >= 0 && kw < nwords) ? row[kw] : 0ull;
+      const uint64_t w1 = (sh != 0 && kw + 1 >= 0 && kw + 1 < nwords) ? row[kw + 1] : 0ull;
+      m |= (w0 >> sh) | (sh != 0 ? w1 << (64 - sh) : 0ull);
+    }
+    return m;
+  };
   SplitShare r;
-  r.count = __builtin_amdgcn_readfirstlane(min(P.ucount[pair], P.umax));
-  r.ent = P.ulist[off];
-  r.page = P.upage[off];
-  r.ne = split < r.count ? min(P.bps, ceil_div(r.count - split, P.max_split)) : 0;
-  if (!(ent_in && lane < r.ne)) {
+  r.ent = 0;
+  r.page = -1;
+  const int pos = split + lane * S;   // this lane's target position
+  const bool want = lane < P.bps;
+  const int nch = ceil_div(nb, kWave);
+  int done = 0;   // union entries in the chunks before this round
+  // Rounds of 64 chunks of 64 blocks; lane c holds chunk c's mask.  Every
+  // wavefront computes the whole share itself, so no barrier is needed.
+  for (int c0 = 0; c0 < nch; c0 += kWave) {
+    const int ncr = min(kWave, nch - c0);
+    const int j0 = (c0 + lane) * kWave;
+    uint64_t mymask = 0ull;
+    if (lane < ncr)
+      mymask = (cand_bits(j0) | range_bits(j0, 0, a1) | range_bits(j0, a2, nb)) & range_bits(j0, 0, nb);
+    const uint32_t cnt_c = static_cast<uint32_t>(__popcll(mymask));
+    const uint32_t incl = wave_scan_incl(cnt_c);
+    const int total = __builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1);
+    upre[lane] = done + static_cast<int>(incl - cnt_c);   // wavefront-private copies
+    umask[lane] = mymask;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (want && pos >= done && pos < done + total && pos < P.umax) {
+      int c = 0;   // last chunk of the round whose prefix is <= pos
+#pragma unroll
+      for (int step = 32; step >= 1; step >>= 1)
+        if (c + step < ncr && upre[c + step] <= pos) c += step;
+      int rnk = pos - upre[c];
+      uint64_t m = umask[c];
+      int bit = 0;
+#pragma unroll
+      for (int w = 32; w >= 1; w >>= 1) {   // rank search: the (rnk+1)-th set bit
+        const int low = __popcll(m & ((1ull << w) - 1ull));
+        if (rnk >= low) {
+          rnk -= low;
+          m >>= w;
+          bit += w;
+        }
+      }
+      const int j = (c0 + c) * kWave + bit;
+      r.ent = j | (head_mask(j) << 20);
+      r.page = P.bt_staged ? btrow[j] : bt[j];
+    }
+    done += total;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // reads above before the next round's writes
+  }
+  r.count = __builtin_amdgcn_readfirstlane(min(done, P.umax));
+  r.ne = split < r.count ? min(P.bps, ceil_div(r.count - split, S)) : 0;
+  if (lane >= r.ne) {
     r.ent = 0;
     r.page = -1;
   }
+  if (split == 0 && tid == 0) P.ucount[pair] = r.count;
   return r;
 }
 
@@ -714,7 +746,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
   const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
-  const SplitShare share = load_share(P, pair, split, lane);
+  const int lig = tid % LPT;
+  QReg<KV> qr[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qr[h].load(reinterpret_cast<const char*>(P.q) +
+               ((static_cast<size_t>(b) * P.Hq + g * G + h) * D + lig * 8) * KV::kBytes);
+  extern __shared__ uint64_t dyn_lds[];
+  const SplitShare share = union_share<G>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, T, split, [] {});
   if (split >= share.count) return;
   const int ne = share.ne;
   const int my_ent = share.ent;
@@ -722,17 +761,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
   const int B = P.B;
   const int ns = P.ns;
   const int win0 = T - P.W;
-  const int lig = tid % LPT;
   const int grp = tid / LPT;
   const int upb = BIG ? B / kUnit : 1;   // units per block
   const int epu = BIG ? 1 : kUnit / B;   // blocks per unit
   const int nu = BIG ? ne * upb : ceil_div(ne, epu);
-
-  QReg<KV> qr[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    qr[h].load(reinterpret_cast<const char*>(P.q) +
-               ((static_cast<size_t>(b) * P.Hq + g * G + h) * D + lig * 8) * KV::kBytes);
 
   float acc[G][8], lacc[G][8];
 #pragma unroll
@@ -1037,29 +1069,33 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
   const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
-  const SplitShare share = load_share(P, pair, split, lane);   // issued with the query loads below
   const int B = P.B;
   const int ns = P.ns;
   const int win0 = T - P.W;
   const int spb = B / SL;               // slices per block
 
-  // Query operand rows (heads; rows G..15 zero) staged in LDS, 16 bytes of
-  // padding per row so that the 16 rows fall on distinct banks.
-  for (int idx = tid; idx < 16 * (D / 8); idx += kThreads) {
-    const int row = idx / (D / 8);
-    const int col = idx % (D / 8);
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (row < G)
-      w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(P.q) +
-                                          (static_cast<size_t>(b) * P.Hq + g * G + row) * D + col * 8);
-    q_lds[row][col] = w;
-  }
   if (lane < G) {
     m_pub[wave][lane] = kNegInf;
     c_pub[wave][lane] = 1.f;
   }
+  // Query operand rows (heads; rows G..15 zero) staged in LDS, 16 bytes of
+  // padding per row so that the 16 rows fall on distinct banks; loaded in
+  // the same round trip as the split's union data.  The barriers inside
+  // union_share also publish q_lds.
+  auto stage_q = [&] {
+    for (int idx = tid; idx < 16 * (D / 8); idx += kThreads) {
+      const int row = idx / (D / 8);
+      const int col = idx % (D / 8);
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (row < G)
+        w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(P.q) +
+                                            (static_cast<size_t>(b) * P.Hq + g * G + row) * D + col * 8);
+      q_lds[row][col] = w;
+    }
+  };
+  extern __shared__ uint64_t dyn_lds[];
+  const SplitShare share = union_share<G>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, T, split, stage_q);
   if (split >= share.count) return;
-  __syncthreads();   // q_lds
   const int ne = share.ne;
   const int my_ent = share.ent;
   const int my_page = share.page;
@@ -1391,24 +1427,30 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
   }
   if (rec) rec(ctx, 1, "select");
   {
-    const size_t lds = L.sl.total;
-    if (lds > 32 * 1024) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_select<G>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((k_select<G>), dim3(pairs), dim3(kThreads), lds, stream, P);
+    const dim3 grid(p.batch * p.Hq);
+    if (p.nc_max <= 4 * kWave)
+      hipLaunchKernelGGL((k_select<4>), grid, dim3(kWave), 0, stream, P);
+    else if (p.nc_max <= 8 * kWave)
+      hipLaunchKernelGGL((k_select<8>), grid, dim3(kWave), 0, stream, P);
+    else if (p.nc_max <= 16 * kWave)
+      hipLaunchKernelGGL((k_select<16>), grid, dim3(kWave), 0, stream, P);
+    else if (p.nc_max <= 32 * kWave)
+      hipLaunchKernelGGL((k_select<32>), grid, dim3(kWave), 0, stream, P);
+    else
+      hipLaunchKernelGGL((k_select<0>), grid, dim3(kWave), 0, stream, P);
     hipError_t e = launch_status("k_select");
     if (e != hipSuccess) return e;
   }
   if (rec) rec(ctx, 2, "attend");
   {
+    const size_t lds = L.sl.total;   // union data; within the default dynamic LDS limit
+    const dim3 grid(pairs * L.max_split);
     if constexpr (KV::kBytes == 2)
-      hipLaunchKernelGGL((k_attend_mfma<D, G>), dim3(pairs * L.max_split), dim3(kThreads), 0, stream, P);
+      hipLaunchKernelGGL((k_attend_mfma<D, G>), grid, dim3(kThreads), lds, stream, P);
     else if (p.B >= kUnit)
-      hipLaunchKernelGGL((k_attend<KV, D, G, true>), dim3(pairs * L.max_split), dim3(kThreads), 0, stream, P);
+      hipLaunchKernelGGL((k_attend<KV, D, G, true>), grid, dim3(kThreads), lds, stream, P);
     else
-      hipLaunchKernelGGL((k_attend<KV, D, G, false>), dim3(pairs * L.max_split), dim3(kThreads), 0, stream, P);
+      hipLaunchKernelGGL((k_attend<KV, D, G, false>), grid, dim3(kThreads), lds, stream, P);
     hipError_t e = launch_status("k_attend");
     if (e != hipSuccess) return e;
   }
@@ -1458,7 +1500,6 @@ DecodeLayout decode_layout(const Problem& p) {
   L.pstride = 2 * p.D + 4;
   L.sstride = std::max(4, (p.nc_max + 3) / 4 * 4);
   L.nwords = std::max(1, (p.nc_max + 63) / 64);
-  L.keys_staged = static_cast<size_t>(p.G) * L.sstride * sizeof(uint32_t) <= kKeysStageBytes ? 1 : 0;
   L.bt_staged = static_cast<size_t>(p.nblk_max) * sizeof(int32_t) <= kBtStageBytes ? 1 : 0;
   {
     uint32_t o = 0;
@@ -1468,9 +1509,8 @@ DecodeLayout decode_layout(const Problem& p) {
       return at;
     };
     L.sl.bits = take(static_cast<uint32_t>(p.G * L.nwords * sizeof(uint64_t)));
-    L.sl.hist = take(4 * 256 * sizeof(uint32_t));
-    L.sl.umask = take(kWave * sizeof(uint64_t));
-    L.sl.keys = take(L.keys_staged ? static_cast<uint32_t>(p.G * L.sstride * sizeof(uint32_t)) : 0u);
+    L.sl.umask = take((kThreads / kWave) * kWave * sizeof(uint64_t));
+    L.sl.upre = take((kThreads / kWave) * kWave * sizeof(int32_t));
     L.sl.btrow = take(L.bt_staged ? static_cast<uint32_t>(p.nblk_max * sizeof(int32_t)) : 0u);
     L.sl.total = o;
   }
@@ -1481,10 +1521,8 @@ DecodeLayout decode_layout(const Problem& p) {
   off = align_up(off + sizeof(float) * static_cast<size_t>(pairs) * std::max(1, L.ro_wgs) * p.G * p.D);
   L.off_roz = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(pairs) * std::max(1, L.ro_wgs) * p.G);
-  L.off_union = off;
-  off = align_up(off + sizeof(int32_t) * static_cast<size_t>(pairs) * L.umax);
-  L.off_upage = off;
-  off = align_up(off + sizeof(int32_t) * static_cast<size_t>(pairs) * L.umax);
+  L.off_bits = off;
+  off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(p.batch) * p.Hq * L.nwords);
   L.off_ucount = off;
   off = align_up(off + sizeof(int32_t) * static_cast<size_t>(pairs));
   L.off_part = off;
@@ -1509,8 +1547,7 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.out = a.out;
   P.sel_idx = a.sel_idx;
   P.keys = reinterpret_cast<uint32_t*>(a.ws + L.off_scores);
-  P.ulist = reinterpret_cast<int32_t*>(a.ws + L.off_union);
-  P.upage = reinterpret_cast<int32_t*>(a.ws + L.off_upage);
+  P.bits = reinterpret_cast<uint64_t*>(a.ws + L.off_bits);
   P.ro = reinterpret_cast<float*>(a.ws + L.off_ro);
   P.roz = reinterpret_cast<float*>(a.ws + L.off_roz);
   P.ucount = reinterpret_cast<int32_t*>(a.ws + L.off_ucount);
@@ -1530,7 +1567,6 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.ro_wgs = L.ro_wgs;
   P.sstride = L.sstride;
   P.nwords = L.nwords;
-  P.keys_staged = L.keys_staged;
   P.bt_staged = L.bt_staged;
   P.sl = L.sl;
   P.umax = L.umax;

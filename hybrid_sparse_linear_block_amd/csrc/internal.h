@@ -29,13 +29,13 @@ struct Problem {
 };
 
 // ---------------------------------------------------------------- decode
-// Byte offsets into the dynamic LDS of the selection kernel: per-head
-// selection bitmaps [G][nwords] (uint64), wavefront-private radix
-// histograms [4][256] (uint32), union chunk masks [64] (uint64), then, when
-// staged, the order keys [G][sstride] (uint32) and the sequence's
-// block-table row [nblk_max] (int32).
+// Byte offsets into the dynamic LDS of an attention workgroup, where it
+// builds its share of the union: the G heads' selection bitmaps [G][nwords]
+// (uint64), wavefront-private union chunk masks [4][64] (uint64) and chunk
+// prefixes [4][64] (int32), then, when staged, the sequence's block-table
+// row [nblk_max] (int32).
 struct SelLayout {
-  uint32_t bits, hist, umask, keys, btrow, total;
+  uint32_t bits, umask, upre, btrow, total;
 };
 
 struct DecodeLayout {
@@ -49,10 +49,9 @@ struct DecodeLayout {
   int pstride;         // floats per (split, head) partial
   int sstride;         // order keys per (sequence, head) row, multiple of 4
   int nwords;          // 64-bit words of a per-head selection bitmap
-  int keys_staged;     // order keys of the G heads staged in LDS
   int bt_staged;       // block-table row staged in LDS
   SelLayout sl;
-  size_t off_scores, off_ro, off_roz, off_union, off_upage, off_ucount, off_part, total;
+  size_t off_scores, off_ro, off_roz, off_bits, off_ucount, off_part, total;
 };
 DecodeLayout decode_layout(const Problem& p);
 
