@@ -551,13 +551,14 @@ __global__ __launch_bounds__(kWave) void k_select(DecodeParams P) {
 // workgroup barrier: every thread calls it.  Split 0 also records the union
 // size for the merge.
 struct SplitShare {
+  int T;       // sequence length (uniform)
   int ent;
   int page;    // -1 on lanes past ne
   int count;   // union size (uniform)
   int ne;      // entries of this split (uniform)
 };
 template <int G, typename Stage>
-__device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, int b, int g, int T, int split,
+__device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, int b, int g, int split,
                                   Stage&& stage) {
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -566,26 +567,28 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
   uint64_t* umask = reinterpret_cast<uint64_t*>(smem + P.sl.umask) + wave * kWave;
   int32_t* upre = reinterpret_cast<int32_t*>(smem + P.sl.upre) + wave * kWave;
   int32_t* btrow = reinterpret_cast<int32_t*>(smem + P.sl.btrow);
-  const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
-  const int nc = min(cr.count, P.nc_max);
   const int nwords = P.nwords;
-  const int nb = min(ceil_div(T, P.B), P.nblk_max);
   const int S = P.max_split;
   const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  const uint64_t* src = P.bits + (static_cast<size_t>(b) * P.Hq + g * G) * nwords;
+  const int nbits = G * nwords;
 
   // ---- bitmaps and block-table row.  The first round of both is loaded
-  // together with the caller's own staging (`stage`, e.g. the query), so
-  // that the usual sizes take a single round trip; larger rows loop on.
+  // before the sequence length is read and together with the caller's own
+  // loads, which `stage` then stores, so that the usual sizes take a single
+  // round trip; larger rows loop on.
+  uint64_t v[2];
+  int w[4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) v[u] = src[min(tid + u * kThreads, nbits - 1)];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) w[u] = bt[min(tid + u * kThreads, P.nblk_max - 1)];
+  const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
+  const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
+  const int nc = min(cr.count, P.nc_max);
+  const int nb = min(ceil_div(T, P.B), P.nblk_max);
   {
-    const uint64_t* src = P.bits + (static_cast<size_t>(b) * P.Hq + g * G) * nwords;
-    const int nbits = G * nwords;
     const int nbt = P.bt_staged ? nb : 0;
-    uint64_t v[2];
-    int w[4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) v[u] = src[min(tid + u * kThreads, nbits - 1)];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) w[u] = bt[min(tid + u * kThreads, nb - 1)];
     stage();
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -652,6 +655,7 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
     return m;
   };
   SplitShare r;
+  r.T = T;
   r.ent = 0;
   r.page = -1;
   const int pos = split + lane * S;   // this lane's target position
@@ -745,7 +749,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
   const int lane = tid % kWave;
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
-  const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
   const int lig = tid % LPT;
   QReg<KV> qr[G];
 #pragma unroll
@@ -753,7 +756,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
     qr[h].load(reinterpret_cast<const char*>(P.q) +
                ((static_cast<size_t>(b) * P.Hq + g * G + h) * D + lig * 8) * KV::kBytes);
   extern __shared__ uint64_t dyn_lds[];
-  const SplitShare share = union_share<G>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, T, split, [] {});
+  const SplitShare share = union_share<G>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, [] {});
+  const int T = share.T;
   if (split >= share.count) return;
   const int ne = share.ne;
   const int my_ent = share.ent;
@@ -1068,10 +1072,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   const int n16 = lane % 16;
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
-  const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
   const int B = P.B;
   const int ns = P.ns;
-  const int win0 = T - P.W;
   const int spb = B / SL;               // slices per block
 
   if (lane < G) {
@@ -1079,22 +1081,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     c_pub[wave][lane] = 1.f;
   }
   // Query operand rows (heads; rows G..15 zero) staged in LDS, 16 bytes of
-  // padding per row so that the 16 rows fall on distinct banks; loaded in
-  // the same round trip as the split's union data.  The barriers inside
-  // union_share also publish q_lds.
+  // padding per row so that the 16 rows fall on distinct banks.  Loaded
+  // first, in the same round trip as the split's union data; union_share
+  // stores them and its barrier publishes q_lds.
+  static_assert(16 * (D / 8) <= kThreads, "one query chunk per thread");
+  const int q_row = tid / (D / 8);
+  const int q_col = tid % (D / 8);
+  uint4 qv = make_uint4(0, 0, 0, 0);
+  if (q_row < G)
+    qv = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(P.q) +
+                                         (static_cast<size_t>(b) * P.Hq + g * G + q_row) * D + q_col * 8);
   auto stage_q = [&] {
-    for (int idx = tid; idx < 16 * (D / 8); idx += kThreads) {
-      const int row = idx / (D / 8);
-      const int col = idx % (D / 8);
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (row < G)
-        w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(P.q) +
-                                            (static_cast<size_t>(b) * P.Hq + g * G + row) * D + col * 8);
-      q_lds[row][col] = w;
-    }
+    if (q_row < 16) q_lds[q_row][q_col] = qv;
   };
   extern __shared__ uint64_t dyn_lds[];
-  const SplitShare share = union_share<G>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, T, split, stage_q);
+  const SplitShare share = union_share<G>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, stage_q);
+  const int T = share.T;
+  const int win0 = T - P.W;
   if (split >= share.count) return;
   const int ne = share.ne;
   const int my_ent = share.ent;
