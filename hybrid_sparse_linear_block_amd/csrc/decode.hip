@@ -133,29 +133,30 @@ __device__ __forceinline__ float q_elem(const void* q, size_t idx) {
 // 1. Block scores + global-state readout
 // ---------------------------------------------------------------------------
 template <typename KV, int D, int G>
-__device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, int T, int chunk) {
+__device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, int chunk) {
   constexpr int LPT = D / 8;            // lanes per candidate (8 channels each)
   constexpr int CPP = kThreads / LPT;   // candidates per pass
   constexpr int NIT = kScoreChunk / CPP;
   static_assert(G <= LPT, "one writer lane per head");
-  const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
-  const int nc = min(cr.count, P.nc_max);
-  const int c_begin = chunk * kScoreChunk;
-  if (c_begin >= nc) return;
+  const int c_begin = chunk * kScoreChunk;   // < nc_max
   const int tid = threadIdx.x;
   const int lig = tid % LPT;
   const int slot = tid / LPT;
   const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  const int lo = P.ns / P.B;   // first candidate block, whatever the length
 
-  // Issue every load of the chunk before any arithmetic: page ids, then the
-  // statistics rows, then the queries.
+  // Issue every load of the chunk before any arithmetic: page ids (bounded
+  // by the longest sequence, so that they need not wait for this one's
+  // length), then the statistics rows, then the queries.
   int page[NIT];
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int c = c_begin + slot + it * CPP;
-    const int pg = bt[cr.lo + min(c, nc - 1)];
-    page[it] = (c < nc) ? pg : -1;
-  }
+  for (int it = 0; it < NIT; ++it) page[it] = bt[lo + min(c_begin + slot + it * CPP, P.nc_max - 1)];
+  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
+  const int nc = min(candidate_range(T, P.B, P.ns, P.W).count, P.nc_max);
+  if (c_begin >= nc) return;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+    if (c_begin + slot + it * CPP >= nc) page[it] = -1;
   float4 m0[NIT], m1[NIT], v0[NIT], v1[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {   // unconditional loads; unused slots read page 0
@@ -290,8 +291,7 @@ __global__ __launch_bounds__(kThreads) void k_score_readout(DecodeParams P) {
   const int g = pair % P.Hkv;
   const int x = blockIdx.x;
   if (x < P.score_wgs) {
-    const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
-    score_part<KV, D, G>(P, b, g, T, x);
+    score_part<KV, D, G>(P, b, g, x);
   } else {
     readout_part<KV, D, G>(P, b, g, x - P.score_wgs);
   }
@@ -300,14 +300,11 @@ __global__ __launch_bounds__(kThreads) void k_score_readout(DecodeParams P) {
 // ---------------------------------------------------------------------------
 // 2. Top-k selection and the union of the group's exact blocks
 // ---------------------------------------------------------------------------
-// Every attention workgroup of a (sequence, kv head) recomputes the selection
-// from the block scores (a few KB, cache resident) before it touches K/V:
-// the G heads' top-k blocks (score desc, index asc), the union of the
-// group's exact blocks in ascending block order (SPLA Figure 1(a)), and its
-// own share of that union.  A separate selection kernel would leave every
-// attention workgroup a dependent round trip for the union at its start,
-// which queues behind the K/V loads the first workgroups have already
-// issued; recomputing it costs a few microseconds of arithmetic instead.
+// Selection runs per query head: one wavefront takes the head's block-score
+// order keys, finds the k-th largest by a radix search and writes the head's
+// selection bitmap and its selected indices.  The union of a group's exact
+// blocks (SPLA Figure 1(a)) is not materialised here: each attention
+// workgroup forms its own share of it from the G bitmaps (section 3).
 // Wavefront-wide min / max of uint32 without LDS: DPP permutations inside
 // each row of 16 lanes, then the permlane swaps across rows.
 template <bool MAX>
@@ -450,13 +447,8 @@ __device__ __forceinline__ void wave_topk_threshold(const uint32_t* key, KeyAt k
 // (word w, bit i: candidate 64 w + i) and, when `out` is set, the selected
 // block indices in ascending order padded with -1.
 template <int KPL, typename KeyAt>
-__device__ __forceinline__ void head_select(KeyAt key_at, int nc, int k, int nwords, int lane, uint32_t* hist,
-                                            uint64_t* bits_row, int32_t* out, int lo) {
-  uint32_t key[KPL > 0 ? KPL : 1];
-  if constexpr (KPL > 0) {
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) key[j] = key_at(min(lane + kWave * j, max(nc - 1, 0)));
-  }
+__device__ __forceinline__ void head_select(KeyAt key_at, const uint32_t* key, int nc, int k, int nwords, int lane,
+                                            uint32_t* hist, uint64_t* bits_row, int32_t* out, int lo) {
   const bool take_all = k >= nc;
   const bool take_none = (k <= 0) || (nc == 0);
   uint32_t thr = 0;
@@ -526,13 +518,20 @@ __global__ __launch_bounds__(kWave) void k_select(DecodeParams P) {
   const int bh = blockIdx.x;
   const int b = bh / P.Hq;
   const int lane = threadIdx.x;
+  const uint32_t* kh = P.keys + static_cast<size_t>(bh) * P.sstride;
+  // The keys go into registers before the sequence length is known (the
+  // row holds sstride >= nc_max keys; those past nc are never used).
+  uint32_t key[KPL > 0 ? KPL : 1];
+  if constexpr (KPL > 0) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) key[j] = kh[min(lane + kWave * j, P.sstride - 1)];
+  }
   const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
   const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
   const int nc = min(cr.count, P.nc_max);
-  const uint32_t* kh = P.keys + static_cast<size_t>(bh) * P.sstride;
   auto key_at = [&](int i) -> uint32_t { return kh[i]; };
   int32_t* out = P.sel_idx ? P.sel_idx + static_cast<size_t>(bh) * P.top_k : nullptr;
-  head_select<KPL>(key_at, nc, P.top_k, P.nwords, lane, hist, P.bits + static_cast<size_t>(bh) * P.nwords, out,
+  head_select<KPL>(key_at, key, nc, P.top_k, P.nwords, lane, hist, P.bits + static_cast<size_t>(bh) * P.nwords, out,
                    cr.lo);
 }
 
@@ -1329,10 +1328,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
 // 4. Merge of the splits and the residual linear part
 // ---------------------------------------------------------------------------
 // One workgroup per (sequence, query head); NP = 256 / D lanes share a
-// channel and walk the splits with a running maximum, then combine.
+// channel and walk the splits with a running maximum, then combine.  Every
+// load of the usual case -- the first NP * 8 splits' partials, the readout
+// partials, sv, the union size and the sequence length -- goes out in one
+// round trip: partials of splits past the union size are loaded and ignored.
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
   constexpr int NP = kThreads / D;
+  constexpr int RO = D / kRoRows;   // readout partials per head
+  constexpr int NPC = 8;            // splits per lane whose loads are issued together
   __shared__ float part_m[NP][D], part_num[NP][D], part_den[NP][D], part_lnum[NP][D], part_lden[NP][D];
   const int bh = blockIdx.x;
   const int b = bh / P.Hq;
@@ -1343,26 +1347,39 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
   const int tid = threadIdx.x;
   const int c = tid % D;
   const int pp = tid / D;
-  const int count = min(P.ucount[pair], P.umax);
-  const int nsplit = min(count, P.max_split);   // split s holds entries s, s + max_split, ...
   const size_t sstride = static_cast<size_t>(G) * P.pstride;
   const float* pb = P.part + (static_cast<size_t>(pair) * P.max_split * G + hh) * P.pstride;
 
-  float M = 0.f;   // the linear part is in unshifted units (log-scale 0)
-  float num = 0.f, den = 0.f, lnum = 0.f, lden = 0.f;
-  constexpr int NPC = 8;   // splits per lane whose loads are issued together
-  for (int s0 = pp; s0 < nsplit; s0 += NP * NPC) {
-    float ms[NPC], ls[NPC], lds[NPC], a[NPC], la[NPC];
+  float ms[NPC], ls[NPC], lds[NPC], a[NPC], la[NPC];
+  auto load_chunk = [&](int s0, int bound) {
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
-      const int sidx = min(s0 + i * NP, nsplit - 1);
-      const float* ps = pb + sidx * sstride;
+      const float* ps = pb + min(s0 + i * NP, bound - 1) * sstride;
       ms[i] = ps[0];
       ls[i] = ps[1];
       lds[i] = ps[2];
       a[i] = ps[4 + c];
       la[i] = ps[4 + D + c];
     }
+  };
+  load_chunk(pp, P.max_split);
+  float ro_p[RO], rz_p[RO], svc = 0.f;
+  if (P.linear_tail) {
+#pragma unroll
+    for (int rc = 0; rc < RO; ++rc) {
+      ro_p[rc] = P.ro[((static_cast<size_t>(pair) * RO + rc) * G + hh) * D + c];
+      rz_p[rc] = P.roz[(static_cast<size_t>(pair) * RO + rc) * G + hh];
+    }
+    svc = P.sv[static_cast<size_t>(pair) * D + c];
+  }
+  const int count = min(P.ucount[pair], P.umax);
+  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
+  const int nsplit = min(count, P.max_split);   // split s holds entries s, s + max_split, ...
+
+  float M = 0.f;   // the linear part is in unshifted units (log-scale 0)
+  float num = 0.f, den = 0.f, lnum = 0.f, lden = 0.f;
+  for (int s0 = pp; s0 < nsplit; s0 += NP * NPC) {
+    if (s0 != pp) load_chunk(s0, nsplit);
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
       if (s0 + i * NP >= nsplit) break;
@@ -1399,16 +1416,15 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
     lnum += part_lnum[x][c];
     lden += part_lden[x][c];
   }
-  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
   const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
   if (P.linear_tail && P.top_k < min(cr.count, P.nc_max)) {
     float ro = 0.f, rz = 0.f;
-#pragma unroll 8
-    for (int rc = 0; rc < P.ro_wgs; ++rc) {
-      ro += P.ro[((static_cast<size_t>(pair) * P.ro_wgs + rc) * G + hh) * D + c];
-      rz += P.roz[(static_cast<size_t>(pair) * P.ro_wgs + rc) * G + hh];
+#pragma unroll
+    for (int rc = 0; rc < RO; ++rc) {
+      ro += ro_p[rc];
+      rz += rz_p[rc];
     }
-    const float num_u = P.sv[static_cast<size_t>(pair) * D + c] + P.sigma * ro - lnum;
+    const float num_u = svc + P.sigma * ro - lnum;
     const float den_u = static_cast<float>(T) + P.sigma * rz - lden;
     const float em = __expf(-M);
     num = fmaf(em, num_u, num);
