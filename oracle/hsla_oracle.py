@@ -63,6 +63,7 @@ class Params:
     window: int
     linear_tail: int = 1
     scale: float = 0.0
+    grouped: int = 0   # 1: one selection shared by the G query heads of a kv head
 
     @property
     def group(self) -> int:
@@ -152,6 +153,51 @@ def select_top_k(cands: np.ndarray, scores: np.ndarray, k: int) -> np.ndarray:
     order = sorted(range(len(cands)), key=lambda i: (-scores[i], cands[i]))
     chosen = [int(cands[i]) for i in order[:k]]
     return np.array(sorted(chosen), dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------
+# Grouped selection (variant): one block selection shared by the G query
+# heads of a kv head.  [SPLA table of contents, section "Grouped Sparsity";
+# the section's text is not on the page.]
+# Reading: a head's block score estimates the log of the head's attention
+# mass on the block, so a softmax over the candidates gives the block's share
+# of that head's candidate mass.  The group's weight of a block is the sum of
+# these shares over its G heads (every head counts equally, whatever its
+# score offset), and the k blocks of largest weight are taken, lower index
+# first on ties.  With G = 1 this is the per-head selection.
+# ----------------------------------------------------------------------------
+
+def group_block_weights(scores_by_head: np.ndarray) -> np.ndarray:
+    """scores [G, n] (one row per query head of the group) -> weight [n]."""
+    G, n = scores_by_head.shape
+    w = np.zeros(n)
+    for h in range(G):
+        s = scores_by_head[h]
+        e = np.exp(s - s.max())
+        w += e / e.sum()
+    return w
+
+
+def select_top_k_grouped(cands: np.ndarray, scores_by_head: np.ndarray, k: int) -> np.ndarray:
+    """The shared selection of a group: top-k of the group weights, ascending."""
+    if len(cands) == 0:
+        return np.zeros(0, np.int64)
+    return select_top_k(cands, group_block_weights(scores_by_head), k)
+
+
+def group_selection(qs: np.ndarray, K: np.ndarray, p: Params, stats=None):
+    """qs [G, d] (the group's queries), K [T, d] -> (candidates, per-head
+    scores [G, n], group weights [n], shared selection)."""
+    T = K.shape[0]
+    cands = candidate_blocks(T, p)
+    if stats is None:
+        stats = block_statistics(K, p.block_size)
+    mean, var = stats
+    if len(cands) == 0:
+        return cands, np.zeros((len(qs), 0)), np.zeros(0), np.zeros(0, np.int64)
+    scores = np.stack([block_score(q, mean[cands], var[cands], p.sigma) for q in qs])
+    w = group_block_weights(scores)
+    return cands, scores, w, select_top_k(cands, w, p.top_k)
 
 
 # ----------------------------------------------------------------------------
@@ -323,13 +369,21 @@ def decode_batch(q: np.ndarray, pairs: dict, p: Params, seq_lens: Sequence[int],
     if heads is None:
         heads = [(b, h) for b in range(batch) for h in range(Hq)]
     res = {}
+    shared = {}   # grouped selection per (b, g)
     for b, h in heads:
         g = kv_head_of(h, p)
         K, V = pairs[(b, g)]
         assert K.shape[0] == seq_lens[b]
+        sel = None if selected is None else selected.get((b, h))
+        if sel is None and p.grouped:
+            if (b, g) not in shared:
+                G = p.group
+                shared[(b, g)] = group_selection(q[b, g * G:(g + 1) * G], K, p,
+                                                 stats=None if stats is None else stats.get((b, g)))[3]
+            sel = shared[(b, g)]
         res[(b, h)] = decode_head(
             q[b, h], K, V, p,
-            selected=None if selected is None else selected.get((b, h)),
+            selected=sel,
             form=form,
             state=None if states is None else states.get((b, g)),
             stats=None if stats is None else stats.get((b, g)))

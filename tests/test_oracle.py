@@ -405,3 +405,72 @@ def test_generator_paging_round_trip():
         ids = inp["block_table"][b, :wl.blocks_mapped(b)].tolist()
         assert not used & set(ids)
         used |= set(ids)
+
+
+# ----------------------------------------------------------------------------
+# Grouped selection (one selection per kv head)
+# ----------------------------------------------------------------------------
+
+def test_golden_grouped_selection():
+    ex = json.load(open(GOLDEN))["grouped_selection"]
+    cands = np.array(ex["candidates"])
+    c0 = ex["cases"][0]
+    sc = np.array(c0["scores_num"])
+    w = O.group_block_weights(sc)
+    np.testing.assert_allclose(w * 20, c0["weights_over_20"], rtol=1e-14)
+    for k, want in c0["selected"].items():
+        assert O.select_top_k_grouped(cands, sc, int(k)).tolist() == want
+    for h in range(2):   # the shared choice differs from each head's own top-1
+        assert O.select_top_k(cands, sc[h], 1).tolist() == c0["per_head_top1"][h]
+    c1 = ex["cases"][1]
+    for k, want in c1["selected"].items():
+        assert O.select_top_k_grouped(cands, np.array(c1["scores_num"]), int(k)).tolist() == want
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_grouped_with_one_head_is_the_per_head_selection(seed):
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(1, 80))
+    cands = np.arange(n) + 1
+    sc = rng.standard_normal(n) * 3
+    for k in [0, 1, 5, n // 2, n, n + 2]:
+        assert O.select_top_k_grouped(cands, sc[None, :], k).tolist() == O.select_top_k(cands, sc, k).tolist()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_group_weights_sum_to_group_size_and_ignore_head_offsets(seed):
+    rng = np.random.default_rng(400 + seed)
+    G, n = int(rng.integers(2, 9)), int(rng.integers(2, 200))
+    sc = rng.standard_normal((G, n)) * 4
+    w = O.group_block_weights(sc)
+    assert w.sum() == pytest.approx(G, rel=1e-12)
+    assert (w > 0).all()
+    shifted = sc + rng.standard_normal((G, 1)) * 50   # a constant per head
+    np.testing.assert_allclose(O.group_block_weights(shifted), w, rtol=1e-9)
+
+
+def test_identical_heads_select_as_one_head():
+    rng = np.random.default_rng(7)
+    p = _params(num_q_heads=4, num_kv_heads=1, head_dim=8, block_size=4, top_k=3, num_sink=2, window=8, grouped=1)
+    K = rng.standard_normal((64, 8))
+    q = rng.standard_normal(8)
+    cands, scores, w, sel = O.group_selection(np.stack([q] * 4), K, p)
+    assert sel.tolist() == O.select_top_k(cands, scores[0], p.top_k).tolist()
+
+
+def test_grouped_batch_shares_the_selection_across_the_group():
+    rng = np.random.default_rng(11)
+    p = _params(num_q_heads=4, num_kv_heads=2, head_dim=8, block_size=4, top_k=2, num_sink=1, window=8, grouped=1)
+    T = 48
+    pairs = {(0, g): (rng.standard_normal((T, 8)), rng.standard_normal((T, 8))) for g in range(2)}
+    q = rng.standard_normal((1, 4, 8))
+    res = O.decode_batch(q, pairs, p, [T])
+    for g in range(2):
+        sels = [res[(0, h)].selected.tolist() for h in (2 * g, 2 * g + 1)]
+        assert sels[0] == sels[1]
+        K, V = pairs[(0, g)]
+        _, _, _, shared = O.group_selection(q[0, 2 * g:2 * g + 2], K, p)
+        assert sels[0] == shared.tolist()
+        for h in (2 * g, 2 * g + 1):   # each head decodes over the shared selection
+            ref = O.decode_head(q[0, h], K, V, p, selected=shared)
+            np.testing.assert_array_equal(res[(0, h)].out, ref.out)
