@@ -24,6 +24,8 @@ HSLA_ERR_WORKSPACE = -3
 HSLA_ERR_HIP = -4
 HSLA_F32 = 0
 HSLA_BF16 = 1
+HSLA_SEL_PER_HEAD = 0
+HSLA_SEL_GROUPED = 1
 HSLA_MAX_PROFILE_EVENTS = 8
 
 EXPORTED = ("hsla_status_string", "hsla_version", "hsla_build_workspace_size", "hsla_build_state",
@@ -35,7 +37,8 @@ class hsla_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("num_sink", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("linear_tail", ctypes.c_int32),
-                ("kv_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("kv_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("selection", ctypes.c_int32)]
 
 
 class hsla_kv_pool(ctypes.Structure):
@@ -126,10 +129,12 @@ class Config:
     linear_tail: int = 1
     kv_dtype: int = HSLA_BF16
     scale: float = 0.0
+    selection: int = HSLA_SEL_PER_HEAD
 
     def c(self) -> hsla_config:
         return hsla_config(self.num_q_heads, self.num_kv_heads, self.head_dim, self.block_size, self.top_k,
-                           self.num_sink, self.window, self.linear_tail, self.kv_dtype, self.scale)
+                           self.num_sink, self.window, self.linear_tail, self.kv_dtype, self.scale,
+                           self.selection)
 
 
 def _ptr(t) -> Optional[int]:

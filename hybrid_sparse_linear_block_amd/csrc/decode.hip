@@ -445,10 +445,13 @@ __device__ __forceinline__ void wave_topk_threshold(const uint32_t* key, KeyAt k
 
 // One head's selection: threshold, then the bitmap of selected candidates
 // (word w, bit i: candidate 64 w + i) and, when `out` is set, the selected
-// block indices in ascending order padded with -1.
+// block indices in ascending order padded with -1.  Both are written to
+// `ncopy` consecutive heads' rows (bitmap rows nwords apart, index rows k
+// apart).
 template <int KPL, typename KeyAt>
 __device__ __forceinline__ void head_select(KeyAt key_at, const uint32_t* key, int nc, int k, int nwords, int lane,
-                                            uint32_t* hist, uint64_t* bits_row, int32_t* out, int lo) {
+                                            uint32_t* hist, uint64_t* bits_row, int32_t* out, int lo,
+                                            int ncopy = 1) {
   const bool take_all = k >= nc;
   const bool take_none = (k <= 0) || (nc == 0);
   uint32_t thr = 0;
@@ -490,9 +493,11 @@ __device__ __forceinline__ void head_select(KeyAt key_at, const uint32_t* key, i
     }
     const uint64_t sm = __ballot(sel);
     const int pos = nsel + __popcll(sm & lanes_below(lane));
-    if (sel && out && pos < k) out[pos] = lo + i;
+    for (int x = 0; x < ncopy; ++x) {
+      if (sel && out && pos < k) out[pos + x * k] = lo + i;
+      if (lane == 0) bits_row[w + x * nwords] = sm;
+    }
     nsel += __popcll(sm);
-    if (lane == 0) bits_row[w] = sm;
   };
   if constexpr (KPL > 0) {
 #pragma unroll
@@ -505,7 +510,8 @@ __device__ __forceinline__ void head_select(KeyAt key_at, const uint32_t* key, i
     }
   }
   if (out)
-    for (int j = nsel + lane; j < k; j += kWave) out[j] = -1;
+    for (int x = 0; x < ncopy; ++x)
+      for (int j = nsel + lane; j < k; j += kWave) out[j + x * k] = -1;
 }
 
 // Selection of one (sequence, query head), one wavefront: the head's order
@@ -533,6 +539,83 @@ __global__ __launch_bounds__(kWave) void k_select(DecodeParams P) {
   int32_t* out = P.sel_idx ? P.sel_idx + static_cast<size_t>(bh) * P.top_k : nullptr;
   head_select<KPL>(key_at, key, nc, P.top_k, P.nwords, lane, hist, P.bits + static_cast<size_t>(bh) * P.nwords, out,
                    cr.lo);
+}
+
+// Grouped selection of one (sequence, kv head), one wavefront: the G heads'
+// order keys are decoded back to scores; each head's scores become a softmax
+// over the candidates (the head's maximum, then its sum of exponentials,
+// both wavefront reductions) and the G shares are summed per block.  The
+// top-k of these sums is the selection of every head of the group: its
+// bitmap and indices are written to all G heads' rows, so that the union
+// and attention stages run unchanged.  KPL > 0 keeps G x KPL keys per lane
+// in registers; KPL == 0 streams them and writes the sums as order keys over
+// the first head's key row, which the threshold search then reads.
+template <int KPL, int G>
+__global__ __launch_bounds__(kWave) void k_select_grouped(DecodeParams P) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+  const int pair = blockIdx.x;
+  const int b = pair / P.Hkv;
+  const int g = pair % P.Hkv;
+  const int lane = threadIdx.x;
+  const size_t row0 = static_cast<size_t>(b) * P.Hq + g * G;
+  uint32_t* k0 = P.keys + row0 * P.sstride;
+  const int ss = P.sstride;
+  uint32_t kr[G][KPL > 0 ? KPL : 1];
+  if constexpr (KPL > 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) kr[h][j] = k0[h * ss + min(lane + kWave * j, ss - 1)];
+  }
+  const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
+  const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
+  const int nc = min(cr.count, P.nc_max);
+  uint32_t agg[KPL > 0 ? KPL : 1];
+  if constexpr (KPL > 0) {
+    float w[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) w[j] = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      uint32_t kmax = 0u;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j)
+        if (lane + kWave * j < nc) kmax = max(kmax, kr[h][j]);
+      const float m = f32_from_order_key(wave_max_u32(kmax));
+      float e[KPL], sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        e[j] = lane + kWave * j < nc ? fast_exp(f32_from_order_key(kr[h][j]) - m) : 0.f;
+        sum += e[j];
+      }
+      const float inv = 1.f / wave_sum(sum);
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) w[j] = fmaf(e[j], inv, w[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) agg[j] = f32_order_key(w[j]);
+  } else if (nc > 0) {
+    float m[G], inv[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      uint32_t kmax = 0u;
+      for (int i = lane; i < nc; i += kWave) kmax = max(kmax, k0[h * ss + i]);
+      m[h] = f32_from_order_key(wave_max_u32(kmax));
+      float sum = 0.f;
+      for (int i = lane; i < nc; i += kWave) sum += fast_exp(f32_from_order_key(k0[h * ss + i]) - m[h]);
+      inv[h] = 1.f / wave_sum(sum);
+    }
+    for (int i = lane; i < nc; i += kWave) {   // every key of index i is read before it is overwritten
+      float w = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) w = fmaf(fast_exp(f32_from_order_key(k0[h * ss + i]) - m[h]), inv[h], w);
+      k0[i] = f32_order_key(w);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+  auto key_at = [&](int i) -> uint32_t { return k0[i]; };
+  int32_t* out = P.sel_idx ? P.sel_idx + row0 * P.top_k : nullptr;
+  head_select<KPL>(key_at, agg, nc, P.top_k, P.nwords, lane, hist, P.bits + row0 * P.nwords, out, cr.lo, G);
 }
 
 // The split's share of the union, built by the attention workgroup itself
@@ -1445,7 +1528,22 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
     if (e != hipSuccess) return e;
   }
   if (rec) rec(ctx, 1, "select");
-  {
+  if (p.grouped) {
+    // keys in registers up to G x KPL <= 64 per lane
+    const dim3 grid(pairs);
+    const int kpl = p.nc_max <= 4 * kWave ? 4 : p.nc_max <= 8 * kWave ? 8 : p.nc_max <= 16 * kWave ? 16 : 0;
+    if (kpl == 4) {
+      hipLaunchKernelGGL((k_select_grouped<4, G>), grid, dim3(kWave), 0, stream, P);
+    } else if (kpl == 8) {
+      hipLaunchKernelGGL((k_select_grouped<8, G>), grid, dim3(kWave), 0, stream, P);
+    } else if (kpl == 16 && G <= 4) {
+      if constexpr (G <= 4) hipLaunchKernelGGL((k_select_grouped<16, G>), grid, dim3(kWave), 0, stream, P);
+    } else {
+      hipLaunchKernelGGL((k_select_grouped<0, G>), grid, dim3(kWave), 0, stream, P);
+    }
+    hipError_t e = launch_status("k_select_grouped");
+    if (e != hipSuccess) return e;
+  } else {
     const dim3 grid(p.batch * p.Hq);
     if (p.nc_max <= 4 * kWave)
       hipLaunchKernelGGL((k_select<4>), grid, dim3(kWave), 0, stream, P);
@@ -1507,7 +1605,7 @@ DecodeLayout decode_layout(const Problem& p) {
   L.ro_rows = kRoRows;
   L.ro_wgs = p.linear_tail ? p.D / L.ro_rows : 0;
   const int sink_blocks = p.ns / p.B;
-  const long sel_blocks = std::min<long>(static_cast<long>(p.G) * p.top_k, p.nc_max);
+  const long sel_blocks = std::min<long>(static_cast<long>(p.grouped ? 1 : p.G) * p.top_k, p.nc_max);
   const long bound = static_cast<long>(sink_blocks) + sel_blocks + 2 + p.W / p.B + 1;
   L.umax = static_cast<int>(std::max<long>(1, std::min<long>(bound, p.nblk_max)));
   {

@@ -21,6 +21,7 @@ inline hipError_t launch_status(const char* what) {
 // Resolved, validated problem description handed to the launchers.
 struct Problem {
   int Hq, Hkv, G, D, B, top_k, ns, W, linear_tail, bf16;
+  int grouped;     // one selection per kv head (HSLA_SEL_GROUPED)
   float sigma;
   int batch, max_seq_len;
   int max_blocks;  // block table row stride

@@ -11,7 +11,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (HSLA_BF16, HSLA_F32, Config, Pool, State, hsla_append_token, hsla_build_state,
+from . import (HSLA_BF16, HSLA_F32, HSLA_SEL_GROUPED, HSLA_SEL_PER_HEAD, Config, Pool, State, hsla_append_token, hsla_build_state,
                hsla_build_workspace_size, hsla_decode, hsla_decode_workspace_size)
 
 
@@ -96,9 +96,10 @@ class DeviceCache:
 
 
 def config_for(num_q_heads, num_kv_heads, head_dim, block_size, top_k, num_sink, window, linear_tail,
-               kv_dtype: str, scale: float = 0.0) -> Config:
+               kv_dtype: str, scale: float = 0.0, grouped: int = 0) -> Config:
     return Config(num_q_heads, num_kv_heads, head_dim, block_size, top_k, num_sink, window, linear_tail,
-                  HSLA_BF16 if kv_dtype == "bf16" else HSLA_F32, scale)
+                  HSLA_BF16 if kv_dtype == "bf16" else HSLA_F32, scale,
+                  HSLA_SEL_GROUPED if grouped else HSLA_SEL_PER_HEAD)
 
 
 class PreparedDecodeStep:

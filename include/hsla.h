@@ -74,6 +74,18 @@ typedef enum hsla_status {
 
 typedef enum hsla_dtype { HSLA_F32 = 0, HSLA_BF16 = 1 } hsla_dtype;
 
+/* Block selection.
+ * HSLA_SEL_PER_HEAD: every query head keeps its own top_k blocks (the method
+ *   as defined above).
+ * HSLA_SEL_GROUPED: the G query heads of a kv head share one selection
+ *   [SPLA table of contents, "Grouped Sparsity"; the section's text is not on
+ *   the page, so this is a reading]: each head's block scores become a
+ *   softmax over its candidates, the G softmaxes are summed per block, and
+ *   the top_k blocks by that sum (lower index first on ties) are the
+ *   selection of every head of the group.  With G = 1 it equals
+ *   HSLA_SEL_PER_HEAD. */
+typedef enum hsla_selection { HSLA_SEL_PER_HEAD = 0, HSLA_SEL_GROUPED = 1 } hsla_selection;
+
 /* The problem statement's parameters.
  * num_q_heads, num_kv_heads: GQA heads; num_q_heads / num_kv_heads must be
  *   1, 2, 4 or 8.
@@ -87,7 +99,8 @@ typedef enum hsla_dtype { HSLA_F32 = 0, HSLA_BF16 = 1 } hsla_dtype;
  *   Attention (RLA)"]; 0 = drop U (plain block-sparse attention, the
  *   "discard" behaviour of SPLA Figure 1(c)).
  * kv_dtype: hsla_dtype of keys, values, queries and appended tokens.
- * scale: sigma; 0 selects 1/sqrt(head_dim). */
+ * scale: sigma; 0 selects 1/sqrt(head_dim).
+ * selection: hsla_selection (0 = per head). */
 typedef struct hsla_config {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -99,6 +112,7 @@ typedef struct hsla_config {
   int32_t linear_tail;
   int32_t kv_dtype;
   float scale;
+  int32_t selection;
 } hsla_config;
 
 /* Paged KV cache [SPLA, "Page Attention and Selection"].

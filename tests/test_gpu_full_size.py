@@ -26,7 +26,8 @@ if not torch.cuda.is_available():  # collected on CPU hosts, skipped there
 
 from hybrid_sparse_linear_block_amd.device import DeviceCache, to_device  # noqa: E402
 
-FULL = {"llama8b_32k": W.llama8b_32k, "needle_128k": W.needle_128k, "ragged_paged": W.ragged_paged}
+FULL = {"llama8b_32k": W.llama8b_32k, "needle_128k": W.needle_128k, "ragged_paged": W.ragged_paged,
+        "llama8b_32k_grouped": lambda: W.dataclasses.replace(W.llama8b_32k(), grouped=1)}
 
 
 def run_full(wl, inp):

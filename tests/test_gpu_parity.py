@@ -4,6 +4,7 @@ Every case prints its name, seed and shape before touching the GPU."""
 import dataclasses
 import math
 import sys
+from types import SimpleNamespace
 
 import numpy as np
 import pytest
@@ -32,12 +33,12 @@ def _announce(wl, extra=""):
 
 def cfg_of(wl):
     return config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
-                      wl.window, wl.linear_tail, wl.kv_dtype, wl.scale)
+                      wl.window, wl.linear_tail, wl.kv_dtype, wl.scale, grouped=wl.grouped)
 
 
 def params_of(wl):
     return O.Params(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
-                    wl.window, wl.linear_tail, wl.scale)
+                    wl.window, wl.linear_tail, wl.scale, grouped=wl.grouped)
 
 
 def run_gpu(wl, inp, capacity_len=None):
@@ -86,12 +87,22 @@ def check_case(wl, inp, dc, out, sel, heads=None, check_build=True, pair_data=No
                                sv_g[b, g].astype(np.float64), T)
             assert_state_close(gs, state, Kf, Vf, state_depth(T), f"pair {(b, g)}")
     worst, flips = 0.0, 0
+    shared = {}   # grouped selection: (candidates, group weights, selection) per pair
     for b, h in heads:
-        Kf, Vf, stats, state = cache[(b, h // G)]
-        r = O.decode_head(q64[b, h], Kf, Vf, p, stats=stats, state=state)
+        g = h // G
+        Kf, Vf, stats, state = cache[(b, g)]
+        if wl.grouped:
+            if (b, g) not in shared:
+                cands, _, w, gsel = O.group_selection(q64[b, g * G:(g + 1) * G], Kf, p, stats=stats)
+                shared[(b, g)] = SimpleNamespace(candidates=cands, scores=w, selected=gsel)
+            ref_sel = shared[(b, g)]
+            r = O.decode_head(q64[b, h], Kf, Vf, p, stats=stats, state=state, selected=ref_sel.selected)
+        else:
+            r = O.decode_head(q64[b, h], Kf, Vf, p, stats=stats, state=state)
+            ref_sel = r
         if sel is not None:
             gs = gpu_selection(sel[b, h])
-            ok, flip, msg = check_selection(r, gs, wl.top_k)
+            ok, flip, msg = check_selection(ref_sel, gs, wl.top_k)
             assert ok, f"(b={b}, h={h}) {msg}"
             if flip:
                 flips += 1
@@ -293,3 +304,44 @@ def test_append_matches_rebuild(dtype):
         m, v = O.block_statistics(Kf, full.block_size)
         pages = table[b, :Kf.shape[0] // full.block_size]
         assert_stats_close(mean_g[pages, g], var_g[pages, g], m, v, Kf, full.block_size)
+
+
+# ----------------------------------------------------------------------------
+# Grouped selection: one selection per kv head
+# ----------------------------------------------------------------------------
+
+GROUPED = [
+    # (name, workload overrides); the last two exceed the register-resident
+    # key counts (G x ceil(n_cand / 64) > 64) and take the streaming path
+    ("llama8b_small", {}),
+    ("needle_small", {}),
+    ("ragged_small", {}),
+    ("tiny_f32_2k", {}),
+    ("G8_B16_long", dict(num_q_heads=16, num_kv_heads=2, block_size=16, window=256, top_k=12,
+                         seq_lens=(10017, 9601))),
+    ("G4_B16_long", dict(block_size=16, window=256, top_k=20, seq_lens=(20011, 17000))),
+]
+
+
+@pytest.mark.parametrize("case", GROUPED, ids=lambda c: c[0])
+def test_grouped_selection(case):
+    name, over = case
+    if name in ("llama8b_small", "needle_small", "ragged_small", "tiny_f32_2k"):
+        wl = dataclasses.replace(W.small(name), grouped=1)
+    else:
+        wl = dataclasses.replace(_wl("grouped_" + name, 70 + GROUPED.index(case), **over), grouped=1)
+    _announce(wl, "grouped selection")
+    inp = W.make_inputs(wl)
+    dc, out, sel = run_gpu(wl, inp)
+    worst, flips = check_case(wl, inp, dc, out, sel, check_build=False)
+    G = wl.group
+    for b in range(wl.batch):   # every head of a group carries the same selection
+        for g in range(wl.num_kv_heads):
+            for h in range(g * G + 1, (g + 1) * G):
+                assert np.array_equal(sel[b, h], sel[b, g * G]), (b, h)
+    if wl.needles_per_pair:
+        for b in range(wl.batch):
+            for g in range(wl.num_kv_heads):
+                for blk, h in W.needle_plan(wl, b, g):
+                    assert blk in sel[b, h].tolist(), (b, g, blk, h)
+    print(f"  worst row error {worst:.3e}, near-tie flips {flips}")

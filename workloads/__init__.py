@@ -58,6 +58,7 @@ class Workload:
     append_room: int = 1          # blocks mapped past the end of each sequence
     scale: float = 0.0            # 0 means 1/sqrt(head_dim)
     layer: int = 0
+    grouped: int = 0              # one block selection per kv head
 
     @property
     def group(self) -> int:
