@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b_32k", choices=["llama8b_32k", "needle_128k", "ragged_paged"])
     ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--grouped", action="store_true",
+                    help="the grouped-selection variant (one block selection per kv head)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-run", action="store_true",
@@ -56,9 +58,14 @@ def parse():
     return ap.parse_args()
 
 
-def workload(name):
+def workload(name, grouped=False):
     import workloads as W
-    return {"llama8b_32k": W.llama8b_32k, "needle_128k": W.needle_128k, "ragged_paged": W.ragged_paged}[name]()
+    wl = {"llama8b_32k": W.llama8b_32k, "needle_128k": W.needle_128k, "ragged_paged": W.ragged_paged}[name]()
+    return W.dataclasses.replace(wl, grouped=1) if grouped else wl
+
+
+def traffic_key(wl):
+    return wl.name + ("+grouped" if wl.grouped else "")
 
 
 class Hip:
@@ -201,7 +208,7 @@ def traffic_collect(fetch_csv, write_csv):
             raise SystemExit(f"{path}: no copy or attention dispatches for {counter}")
         scales[counter] = COPY_BYTES / (max(copy) * 1024.0)
         per[counter] = float(np.mean(attend)) * 1024.0 * scales[counter]
-    name = workload(parse_known_workload()).name
+    name = traffic_key(workload(parse_known_workload(), "--grouped" in sys.argv))
     try:
         out = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -251,7 +258,7 @@ def cpu_baseline(wl, inp_q, gpu_out, gpu_sel, budget_s):
     except Exception:  # pragma: no cover
         threads = 1
     p = O.Params(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
-                 wl.window, wl.linear_tail, wl.scale)
+                 wl.window, wl.linear_tail, wl.scale, grouped=wl.grouped)
     heads_done, t_heads, worst = 0, 0.0, 0.0
     t_start = time.perf_counter()
     for b in range(wl.batch):
@@ -260,11 +267,17 @@ def cpu_baseline(wl, inp_q, gpu_out, gpu_sel, budget_s):
             Kf, Vf = O.to_f64(K, wl.kv_dtype), O.to_f64(V, wl.kv_dtype)
             stats = O.block_statistics(Kf, wl.block_size)
             state = O.global_state(Kf, Vf)
+            shared = None
+            if wl.grouped:   # the group's selection, timed with the group's decodes
+                qg = O.to_f64(inp_q[b, g * wl.group:(g + 1) * wl.group], wl.kv_dtype)
+                t0 = time.perf_counter()
+                shared = O.group_selection(qg, Kf, p, stats=stats)[3]
+                t_heads += time.perf_counter() - t0
             for hh in range(wl.group):
                 h = g * wl.group + hh
                 q = O.to_f64(inp_q[b, h], wl.kv_dtype)
                 t0 = time.perf_counter()
-                r = O.decode_head(q, Kf, Vf, p, stats=stats, state=state)
+                r = O.decode_head(q, Kf, Vf, p, stats=stats, state=state, selected=shared)
                 t_heads += time.perf_counter() - t0
                 heads_done += 1
                 gsel = [int(x) for x in gpu_sel[b, h] if x >= 0]
@@ -280,8 +293,8 @@ def cpu_baseline(wl, inp_q, gpu_out, gpu_sel, budget_s):
     return dict(value=wl.batch / step_s, unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=(f"{heads_done} of {wl.batch * wl.num_q_heads} (sequence, query head) decodes of one "
                         f"step at T={max(wl.seq_lens)}, fp64 subtraction form with statistics and state "
-                        f"precomputed; step time = mean per head x {wl.batch * wl.num_q_heads}; append "
-                        f"not included"),
+                        f"precomputed{'; grouped selection timed with its heads' if wl.grouped else ''}; "
+                        f"step time = mean per head x {wl.batch * wl.num_q_heads}; append not included"),
                 seconds=round(t_heads, 3), ms_per_step=round(step_s * 1e3, 1)), worst
 
 
@@ -294,7 +307,7 @@ def setup(args, extra_steps):
     from hybrid_sparse_linear_block_amd.device import DeviceCache, PreparedDecodeStep, config_for, to_device
 
     torch.cuda.set_device(0)
-    wl = workload(args.workload)
+    wl = workload(args.workload, args.grouped)
     steps, warm, R = args.steps, args.warmup, max(1, args.replicas)
     appends_per_replica = -(-(extra_steps + warm) // R) + 1
     wl = W.dataclasses.replace(wl, append_room=1 + -(-appends_per_replica // wl.block_size))
@@ -303,7 +316,7 @@ def setup(args, extra_steps):
     t_gen = time.perf_counter() - t0
     print(f"[bench] {wl.name}: inputs generated in {t_gen:.1f}s", file=sys.stderr, flush=True)
     cfg = config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
-                     wl.window, wl.linear_tail, wl.kv_dtype)
+                     wl.window, wl.linear_tail, wl.kv_dtype, grouped=wl.grouped)
     cap = max(wl.seq_lens) + appends_per_replica + 1
     hip = Hip()
     stream = torch.cuda.current_stream().cuda_stream
@@ -417,7 +430,7 @@ def main():
     attend_us = per_kernel["attend"]
     ms_per_step = wall / steps * 1e3
     tokens_s = wl.batch / (wall / steps)
-    traffic = traffic_entry(wl.name)
+    traffic = traffic_entry(traffic_key(wl))
     roofline = {"bound": "hbm", "kernel": "k_attend", "achieved": round(avg["attend"] / (attend_us * 1e-6) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(avg["attend"] / (attend_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -430,7 +443,7 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "ctx": int(max(wl.seq_lens)), "q_heads": wl.num_q_heads,
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block": wl.block_size,
                    "top_k": wl.top_k, "sinks": wl.num_sink, "window": wl.window, "replicas": R,
-                   "step": "append + decode"},
+                   "selection": "grouped" if wl.grouped else "per_head", "step": "append + decode"},
         "us_per_step": round(ms_per_step * 1e3, 2),
         "gpu_us_per_step": round(gpu_step_us, 2),
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
