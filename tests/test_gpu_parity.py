@@ -345,3 +345,25 @@ def test_grouped_selection(case):
                 for blk, h in W.needle_plan(wl, b, g):
                     assert blk in sel[b, h].tolist(), (b, g, blk, h)
     print(f"  worst row error {worst:.3e}, near-tie flips {flips}")
+
+
+LONG_ROWS = [
+    # candidate rows past the register-resident sizes of the per-head
+    # selection (n_cand > 1024 and > 2048), a block-table row too long to
+    # stage in LDS (> 2048 blocks), and more than 64 chunks of 64 blocks in
+    # the union prologue (> 4096 blocks)
+    ("B16_20k", dict(block_size=16, window=256, top_k=20, seq_lens=(20011, 17000))),
+    ("B16_40k", dict(block_size=16, window=256, top_k=24, seq_lens=(40000, 36999))),
+    ("B16_70k", dict(batch=1, block_size=16, window=512, top_k=9, seq_lens=(70001,))),
+]
+
+
+@pytest.mark.parametrize("case", LONG_ROWS, ids=lambda c: c[0])
+def test_long_candidate_rows(case):
+    name, over = case
+    wl = _wl("long_" + name, 80 + LONG_ROWS.index(case), **over)
+    _announce(wl)
+    inp = W.make_inputs(wl)
+    dc, out, sel = run_gpu(wl, inp)
+    worst, flips = check_case(wl, inp, dc, out, sel, check_build=False)
+    print(f"  worst row error {worst:.3e}, near-tie flips {flips}")

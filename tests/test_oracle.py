@@ -425,6 +425,12 @@ def test_golden_grouped_selection():
     c1 = ex["cases"][1]
     for k, want in c1["selected"].items():
         assert O.select_top_k_grouped(cands, np.array(c1["scores_num"]), int(k)).tolist() == want
+    c2 = ex["cases"][2]   # the softmax shares, not the raw scores, are summed
+    sc2 = np.array(c2["scores_num"], float)
+    np.testing.assert_allclose(O.group_block_weights(sc2), c2["weights"], atol=1e-9)
+    for k, want in c2["selected"].items():
+        assert O.select_top_k_grouped(cands, sc2, int(k)).tolist() == want
+    assert O.select_top_k(cands, sc2.sum(axis=0), 1).tolist() == c2["raw_sum_top1"]
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -474,3 +480,19 @@ def test_grouped_batch_shares_the_selection_across_the_group():
         for h in (2 * g, 2 * g + 1):   # each head decodes over the shared selection
             ref = O.decode_head(q[0, h], K, V, p, selected=shared)
             np.testing.assert_array_equal(res[(0, h)].out, ref.out)
+
+
+def test_group_selection_scores_every_head_of_the_group():
+    """The group's selection is the grouped top-k of the G heads' own block
+    scores, as the per-head decode reports them."""
+    rng = np.random.default_rng(19)
+    G = 4
+    p1 = _params(num_q_heads=G, num_kv_heads=1, head_dim=8, block_size=4, top_k=3, num_sink=1, window=8)
+    pg = _params(num_q_heads=G, num_kv_heads=1, head_dim=8, block_size=4, top_k=3, num_sink=1, window=8, grouped=1)
+    K, V = rng.standard_normal((80, 8)), rng.standard_normal((80, 8))
+    qs = rng.standard_normal((G, 8)) * 2
+    per_head = [O.decode_head(q, K, V, p1) for q in qs]
+    want = O.select_top_k_grouped(per_head[0].candidates, np.stack([r.scores for r in per_head]), 3)
+    cands, scores, w, sel = O.group_selection(qs, K, pg)
+    assert sel.tolist() == want.tolist()
+    np.testing.assert_array_equal(scores, np.stack([r.scores for r in per_head]))
