@@ -39,9 +39,12 @@ constexpr float kNegInf = -INFINITY;
 constexpr int kScoreChunk = 64;  // candidates per scoring workgroup
 constexpr int kRoRows = 32;      // rows of S per readout workgroup
 constexpr int kUnit = 64;        // tokens per attention work unit
-// Attention workgroups per launch: two per compute unit of MI355X (256
-// CUs), so that every CU carries the same number of splits.
-constexpr int kAttendWgsTarget = 2 * 256;
+// Attention workgroups per launch: one per compute unit of MI355X (256
+// CUs), so that every CU carries the same number of splits.  With one slice
+// in flight per wavefront this keeps 8-16 MB in flight, enough to saturate
+// HBM; two workgroups per CU measured 2-3% slower (longer queues, and the
+// younger workgroup of a CU starts its loop late).
+constexpr int kAttendWgsTarget = 256;
 constexpr size_t kBtStageBytes = 8 * 1024;      // block-table row staged in LDS up to this size
 
 struct DecodeParams {
