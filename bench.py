@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b_32k", choices=["llama8b_32k", "needle_128k", "ragged_paged"])
     ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--deterministic", action="store_true",
+                    help="fixed split of the attention work (bitwise reproducible) instead of the dynamic one")
     ap.add_argument("--grouped", action="store_true",
                     help="the grouped-selection variant (one block selection per kv head)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
@@ -316,7 +318,8 @@ def setup(args, extra_steps):
     t_gen = time.perf_counter() - t0
     print(f"[bench] {wl.name}: inputs generated in {t_gen:.1f}s", file=sys.stderr, flush=True)
     cfg = config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
-                     wl.window, wl.linear_tail, wl.kv_dtype, grouped=wl.grouped)
+                     wl.window, wl.linear_tail, wl.kv_dtype, grouped=wl.grouped,
+                     deterministic=int(args.deterministic))
     cap = max(wl.seq_lens) + appends_per_replica + 1
     hip = Hip()
     stream = torch.cuda.current_stream().cuda_stream
@@ -443,7 +446,8 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "ctx": int(max(wl.seq_lens)), "q_heads": wl.num_q_heads,
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block": wl.block_size,
                    "top_k": wl.top_k, "sinks": wl.num_sink, "window": wl.window, "replicas": R,
-                   "selection": "grouped" if wl.grouped else "per_head", "step": "append + decode"},
+                   "selection": "grouped" if wl.grouped else "per_head",
+                   "attention_split": "fixed" if args.deterministic else "dynamic", "step": "append + decode"},
         "us_per_step": round(ms_per_step * 1e3, 2),
         "gpu_us_per_step": round(gpu_step_us, 2),
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},

@@ -38,7 +38,7 @@ class hsla_config(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("num_sink", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("linear_tail", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("selection", ctypes.c_int32)]
+                ("selection", ctypes.c_int32), ("deterministic", ctypes.c_int32)]
 
 
 class hsla_kv_pool(ctypes.Structure):
@@ -130,11 +130,12 @@ class Config:
     kv_dtype: int = HSLA_BF16
     scale: float = 0.0
     selection: int = HSLA_SEL_PER_HEAD
+    deterministic: int = 0
 
     def c(self) -> hsla_config:
         return hsla_config(self.num_q_heads, self.num_kv_heads, self.head_dim, self.block_size, self.top_k,
                            self.num_sink, self.window, self.linear_tail, self.kv_dtype, self.scale,
-                           self.selection)
+                           self.selection, self.deterministic)
 
 
 def _ptr(t) -> Optional[int]:

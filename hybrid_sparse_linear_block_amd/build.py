@@ -23,6 +23,9 @@ CFLAGS = [
     "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++20",
     # packed fp32 VALU forms stay disabled on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no wavefront-level rewrite of atomics: it reads an atomic's result back
+    # at once, which would drain the attention loop's loads at every claim
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

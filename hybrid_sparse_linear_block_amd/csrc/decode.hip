@@ -45,6 +45,9 @@ constexpr int kUnit = 64;        // tokens per attention work unit
 // HBM; two workgroups per CU measured 2-3% slower (longer queues, and the
 // younger workgroup of a CU starts its loop late).
 constexpr int kAttendWgsTarget = 256;
+constexpr int kCtrStride = 32;       // ints between two pairs' work counters (one 128-byte line each)
+constexpr int kUnitSlices = 4;       // slices per dynamically claimed unit
+constexpr int kMaxDynList = 2048;    // union entries a dynamic attention workgroup holds in LDS
 constexpr size_t kBtStageBytes = 8 * 1024;      // block-table row staged in LDS up to this size
 
 struct DecodeParams {
@@ -65,12 +68,14 @@ struct DecodeParams {
   float* roz;
   uint64_t* bits;   // per-head selection bitmaps [batch, Hq, nwords]
   int32_t* ucount;
+  int32_t* ctr;     // per-pair work counters (kCtrStride apart), dynamic attention only
   float* part;
   int Hq, Hkv, B, top_k, ns, W, linear_tail;
   int max_blocks, max_seq_len, nc_max, nblk_max;
   int score_wgs, ro_wgs;
   int umax, bps, max_split, pstride;
   int sstride, nwords, bt_staged;
+  int dyn;          // attention workgroups of a pair claim its slices dynamically
   SelLayout sl;
   float sigma;
 };
@@ -540,6 +545,10 @@ __global__ __launch_bounds__(kWave) void k_select(DecodeParams P) {
   const int nc = min(cr.count, P.nc_max);
   auto key_at = [&](int i) -> uint32_t { return kh[i]; };
   int32_t* out = P.sel_idx ? P.sel_idx + static_cast<size_t>(bh) * P.top_k : nullptr;
+  const int G = P.Hq / P.Hkv;
+  if (P.dyn && lane == 0 && (bh % P.Hq) % G == 0)   // the pair's work counter for the attention kernel
+    __hip_atomic_store(P.ctr + static_cast<size_t>(bh / G) * kCtrStride, 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   head_select<KPL>(key_at, key, nc, P.top_k, P.nwords, lane, hist, P.bits + static_cast<size_t>(bh) * P.nwords, out,
                    cr.lo);
 }
@@ -618,6 +627,8 @@ __global__ __launch_bounds__(kWave) void k_select_grouped(DecodeParams P) {
   }
   auto key_at = [&](int i) -> uint32_t { return k0[i]; };
   int32_t* out = P.sel_idx ? P.sel_idx + row0 * P.top_k : nullptr;
+  if (P.dyn && lane == 0)   // the pair's work counter for the attention kernel
+    __hip_atomic_store(P.ctr + static_cast<size_t>(pair) * kCtrStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   head_select<KPL>(key_at, agg, nc, P.top_k, P.nwords, lane, hist, P.bits + row0 * P.nwords, out, cr.lo, G);
 }
 
@@ -642,9 +653,10 @@ struct SplitShare {
   int count;   // union size (uniform)
   int ne;      // entries of this split (uniform)
 };
-template <int G, typename Stage>
+template <int G, bool FULL, typename Stage>
 __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, int b, int g, int split,
                                   Stage&& stage) {
+  constexpr int NW = kThreads / kWave;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -758,6 +770,26 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
     const uint32_t cnt_c = static_cast<uint32_t>(__popcll(mymask));
     const uint32_t incl = wave_scan_incl(cnt_c);
     const int total = __builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1);
+    if constexpr (FULL) {
+      // the whole list: wavefront w writes the entries of chunks w, w + NW, ...
+      int32_t* uent = reinterpret_cast<int32_t*>(smem + P.sl.ulist);
+      int32_t* upg = uent + P.umax;
+      const int excl = done + static_cast<int>(incl - cnt_c);
+      for (int c = wave; c < ncr; c += NW) {
+        const uint64_t m = (static_cast<uint64_t>(static_cast<uint32_t>(
+                                __builtin_amdgcn_readlane(static_cast<int>(mymask >> 32), c))) << 32) |
+                           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mymask), c));
+        const int base = __builtin_amdgcn_readlane(excl, c);
+        const int at = base + __popcll(m & lanes_below(lane));
+        if (((m >> lane) & 1ull) && at < P.umax) {
+          const int j = (c0 + c) * kWave + lane;
+          uent[at] = j | (head_mask(j) << 20);
+          upg[at] = P.bt_staged ? btrow[j] : bt[j];
+        }
+      }
+      done += total;
+      continue;
+    }
     upre[lane] = done + static_cast<int>(incl - cnt_c);   // wavefront-private copies
     umask[lane] = mymask;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -786,6 +818,11 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // reads above before the next round's writes
   }
   r.count = __builtin_amdgcn_readfirstlane(min(done, P.umax));
+  if constexpr (FULL) {
+    __syncthreads();   // the list is complete
+    r.ne = 0;
+    return r;
+  }
   r.ne = split < r.count ? min(P.bps, ceil_div(r.count - split, S)) : 0;
   if (lane >= r.ne) {
     r.ent = 0;
@@ -841,7 +878,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
     qr[h].load(reinterpret_cast<const char*>(P.q) +
                ((static_cast<size_t>(b) * P.Hq + g * G + h) * D + lig * 8) * KV::kBytes);
   extern __shared__ uint64_t dyn_lds[];
-  const SplitShare share = union_share<G>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, [] {});
+  const SplitShare share = union_share<G, false>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, [] {});
   const int T = share.T;
   if (split >= share.count) return;
   const int ne = share.ne;
@@ -1132,7 +1169,7 @@ struct VSlice<4> {   // D = 64: 4 channels of a row per lane
   __device__ __forceinline__ void zero() { r = make_uint2(0, 0); }
 };
 
-template <int D, int G>
+template <int D, int G, bool DYN>
 __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   constexpr int NW = kThreads / kWave;
   constexpr int KS = D / 32;            // score MFMAs per slice (32 channels each)
@@ -1180,10 +1217,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     if (q_row < 16) q_lds[q_row][q_col] = qv;
   };
   extern __shared__ uint64_t dyn_lds[];
-  const SplitShare share = union_share<G>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, stage_q);
+  const SplitShare share = union_share<G, DYN>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, stage_q);
   const int T = share.T;
   const int win0 = T - P.W;
-  if (split >= share.count) return;
+  if (!DYN && split >= share.count) return;
   const int ne = share.ne;
   const int my_ent = share.ent;
   const int my_page = share.page;
@@ -1213,15 +1250,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     int t0;   // first token (uniform); T for a slice without a page (no row valid)
     int fm;   // heads that selected the block (uniform)
   };
-  // A fetch past the wavefront's last slice re-reads that slice (an L2 hit)
-  // and marks every row invalid.
-  auto fetch = [&](int kk, Slice& x) __attribute__((always_inline)) {
-    const bool live = kk < nk;
-    const int sl = wave + NW * (live ? kk : max(nk - 1, 0));
-    const int e = sl / spb;
-    const int sub = sl - e * spb;
-    const int ent = __builtin_amdgcn_readlane(my_ent, e);
-    const int pg = __builtin_amdgcn_readlane(my_page, e);
+  // Slice `sub` of union entry (ent, page pg); a dead slice re-reads a live
+  // one (an L2 hit) and marks every row invalid.
+  auto load_slice = [&](int ent, int pg, int sub, bool live, Slice& x) __attribute__((always_inline)) {
     const size_t base = ((static_cast<size_t>(max(pg, 0)) * P.Hkv + g) * B + sub * SL) * D * 2;
 #pragma unroll
     for (int s = 0; s < KS; ++s) x.k[s] = *reinterpret_cast<const uint4*>(kp + base + k_lane + 16 * s);
@@ -1231,6 +1262,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     x.fm = (ent >> 20) & kAll;
     // keep the loads ahead of the previous slice's arithmetic
     __builtin_amdgcn_sched_barrier(0);
+  };
+  // Static split: slice kk of this wavefront is slice wave + NW kk of the
+  // split, whose entries lane e holds.
+  auto fetch = [&](int kk, Slice& x) __attribute__((always_inline)) {
+    const bool live = kk < nk;
+    const int sl = wave + NW * (live ? kk : max(nk - 1, 0));
+    const int e = sl / spb;
+    const int sub = sl - e * spb;
+    load_slice(__builtin_amdgcn_readlane(my_ent, e), __builtin_amdgcn_readlane(my_page, e), sub, live, x);
   };
 
   // Every fetched slice of the loop is processed, without a branch around
@@ -1323,17 +1363,60 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   };
 
   // The next slice is in flight while one is processed.  Two (16 KB per
-  // wavefront, 32 MB over the grid at llama8b_32k) measured faster than
-  // three or four: deeper queues only lengthen the memory latency that the
-  // prologue loads and the last slices wait through.  The loop has a single
-  // exit: an odd count ends with a fully masked slice.
+  // wavefront) measured faster than three or four: deeper queues only
+  // lengthen the memory latency that the prologue loads and the last slices
+  // wait through.
   Slice sa, sb;
-  fetch(0, sa);
-  for (int kk = 0; kk < nk; kk += 2) {
-    fetch(kk + 1, sb);
-    process(sa);
-    fetch(kk + 2, sa);
-    process(sb);
+  if constexpr (DYN) {
+    // The pair's slices, in units of kUnitSlices, go to whichever wavefront
+    // of the pair's workgroups claims them next (a device-scope counter per
+    // pair, zeroed by the selection kernel), so that workgroups on a slower
+    // XCD take fewer.  A wavefront claims its next unit when it starts one
+    // and reads the claim when it prefetches that unit's first slice, three
+    // slices later: the atomic's latency stays hidden, and no wavefront holds
+    // more than the unit it is working on.
+    const int32_t* uent = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(dyn_lds) + P.sl.ulist);
+    const int32_t* upg = uent + P.umax;
+    const int total = share.count * spb;
+    const int nunits = ceil_div(total, kUnitSlices);
+    int32_t* ctr = P.ctr + static_cast<size_t>(pair) * kCtrStride;
+    auto claim = [&]() -> int {   // the claimed unit, in lane 0
+      int v = 0;
+      if (lane == 0) v = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return v;
+    };
+    auto fetch_u = [&](int u, int i, Slice& x) __attribute__((always_inline)) {
+      const int q = u * kUnitSlices + i;
+      const bool live = u < nunits && q < total;
+      const int e = (live ? q : 0) / spb;
+      const int sub = (live ? q : 0) - e * spb;
+      load_slice(__builtin_amdgcn_readfirstlane(uent[e]), __builtin_amdgcn_readfirstlane(upg[e]), sub, live, x);
+    };
+    static_assert(kUnitSlices == 4, "the loop body processes four slices");
+    int ua = __builtin_amdgcn_readfirstlane(claim());
+    fetch_u(ua, 0, sa);
+    while (ua < nunits) {
+      const int cn = claim();
+      fetch_u(ua, 1, sb);
+      process(sa);
+      fetch_u(ua, 2, sa);
+      process(sb);
+      fetch_u(ua, 3, sb);
+      process(sa);
+      ua = __builtin_amdgcn_readfirstlane(cn);
+      fetch_u(ua, 0, sa);
+      process(sb);
+    }
+  } else {
+    // Static split.  The loop has a single exit: an odd count ends with a
+    // fully masked slice.
+    fetch(0, sa);
+    for (int kk = 0; kk < nk; kk += 2) {
+      fetch(kk + 1, sb);
+      process(sa);
+      fetch(kk + 2, sa);
+      process(sb);
+    }
   }
 
   // ---- per-wavefront sums: hi + lo rows, then p v / w v per head to LDS
@@ -1460,7 +1543,9 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
   }
   const int count = min(P.ucount[pair], P.umax);
   const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
-  const int nsplit = min(count, P.max_split);   // split s holds entries s, s + max_split, ...
+  // static: split s holds entries s, s + max_split, ...; dynamic: every
+  // workgroup of the pair wrote a partial (possibly empty)
+  const int nsplit = P.dyn ? P.max_split : min(count, P.max_split);
 
   float M = 0.f;   // the linear part is in unshifted units (log-scale 0)
   float num = 0.f, den = 0.f, lnum = 0.f, lden = 0.f;
@@ -1565,8 +1650,12 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
   {
     const size_t lds = L.sl.total;   // union data; within the default dynamic LDS limit
     const dim3 grid(pairs * L.max_split);
-    if constexpr (KV::kBytes == 2)
-      hipLaunchKernelGGL((k_attend_mfma<D, G>), grid, dim3(kThreads), lds, stream, P);
+    if constexpr (KV::kBytes == 2) {
+      if (P.dyn)
+        hipLaunchKernelGGL((k_attend_mfma<D, G, true>), grid, dim3(kThreads), lds, stream, P);
+      else
+        hipLaunchKernelGGL((k_attend_mfma<D, G, false>), grid, dim3(kThreads), lds, stream, P);
+    }
     else if (p.B >= kUnit)
       hipLaunchKernelGGL((k_attend<KV, D, G, true>), grid, dim3(kThreads), lds, stream, P);
     else
@@ -1611,11 +1700,19 @@ DecodeLayout decode_layout(const Problem& p) {
   const long sel_blocks = std::min<long>(static_cast<long>(p.grouped ? 1 : p.G) * p.top_k, p.nc_max);
   const long bound = static_cast<long>(sink_blocks) + sel_blocks + 2 + p.W / p.B + 1;
   L.umax = static_cast<int>(std::max<long>(1, std::min<long>(bound, p.nblk_max)));
+  // Dynamic attention (bf16 path): the pair's workgroups share its union
+  // list, which the prologue keeps whole in LDS.
+  L.dyn = (p.bf16 && !p.deterministic && L.umax <= kMaxDynList) ? 1 : 0;
   {
     const int want = std::max(1, (kAttendWgsTarget + pairs / 2) / pairs);
-    const int splits = std::min(L.umax, std::max(want, ceil_div(L.umax, kWave)));
-    L.bps = ceil_div(L.umax, splits);   // <= 64: one union entry per lane
-    L.max_split = ceil_div(L.umax, L.bps);
+    if (L.dyn) {
+      L.max_split = std::min(L.umax, want);
+      L.bps = ceil_div(L.umax, L.max_split);
+    } else {
+      const int splits = std::min(L.umax, std::max(want, ceil_div(L.umax, kWave)));
+      L.bps = ceil_div(L.umax, splits);   // <= 64: one union entry per lane
+      L.max_split = ceil_div(L.umax, L.bps);
+    }
   }
   L.pstride = 2 * p.D + 4;
   L.sstride = std::max(4, (p.nc_max + 3) / 4 * 4);
@@ -1632,6 +1729,7 @@ DecodeLayout decode_layout(const Problem& p) {
     L.sl.umask = take((kThreads / kWave) * kWave * sizeof(uint64_t));
     L.sl.upre = take((kThreads / kWave) * kWave * sizeof(int32_t));
     L.sl.btrow = take(L.bt_staged ? static_cast<uint32_t>(p.nblk_max * sizeof(int32_t)) : 0u);
+    L.sl.ulist = take(L.dyn ? static_cast<uint32_t>(2 * L.umax * sizeof(int32_t)) : 0u);
     L.sl.total = o;
   }
   size_t off = 0;
@@ -1645,6 +1743,8 @@ DecodeLayout decode_layout(const Problem& p) {
   off = align_up(off + sizeof(uint64_t) * static_cast<size_t>(p.batch) * p.Hq * L.nwords);
   L.off_ucount = off;
   off = align_up(off + sizeof(int32_t) * static_cast<size_t>(pairs));
+  L.off_ctr = off;
+  off = align_up(off + sizeof(int32_t) * static_cast<size_t>(pairs) * kCtrStride);
   L.off_part = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(pairs) * L.max_split * p.G * L.pstride);
   L.total = off;
@@ -1671,6 +1771,8 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.ro = reinterpret_cast<float*>(a.ws + L.off_ro);
   P.roz = reinterpret_cast<float*>(a.ws + L.off_roz);
   P.ucount = reinterpret_cast<int32_t*>(a.ws + L.off_ucount);
+  P.ctr = reinterpret_cast<int32_t*>(a.ws + L.off_ctr);
+  P.dyn = L.dyn;
   P.part = reinterpret_cast<float*>(a.ws + L.off_part);
   P.Hq = p.Hq;
   P.Hkv = p.Hkv;

@@ -23,6 +23,7 @@ hsla_status resolve(const hsla_config* cfg, int32_t batch, int32_t max_seq_len,
   if (cfg->top_k < 0 || cfg->num_sink < 0 || cfg->window < 1) return HSLA_ERR_INVALID_ARG;
   if (cfg->linear_tail != 0 && cfg->linear_tail != 1) return HSLA_ERR_INVALID_ARG;
   if (cfg->selection != HSLA_SEL_PER_HEAD && cfg->selection != HSLA_SEL_GROUPED) return HSLA_ERR_INVALID_ARG;
+  if (cfg->deterministic != 0 && cfg->deterministic != 1) return HSLA_ERR_INVALID_ARG;
   if (!(cfg->scale >= 0.0f) || !isfinite(cfg->scale)) return HSLA_ERR_INVALID_ARG;
   if (batch < 1 || max_seq_len < 1) return HSLA_ERR_INVALID_ARG;
   const int G = cfg->num_q_heads / cfg->num_kv_heads;
@@ -46,6 +47,7 @@ hsla_status resolve(const hsla_config* cfg, int32_t batch, int32_t max_seq_len,
   p.W = cfg->window;
   p.linear_tail = cfg->linear_tail;
   p.grouped = cfg->selection == HSLA_SEL_GROUPED ? 1 : 0;
+  p.deterministic = cfg->deterministic;
   p.bf16 = cfg->kv_dtype == HSLA_BF16;
   p.sigma = cfg->scale > 0.0f ? cfg->scale : 1.0f / sqrtf(static_cast<float>(cfg->head_dim));
   p.batch = batch;

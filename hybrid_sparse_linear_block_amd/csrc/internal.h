@@ -22,6 +22,7 @@ inline hipError_t launch_status(const char* what) {
 struct Problem {
   int Hq, Hkv, G, D, B, top_k, ns, W, linear_tail, bf16;
   int grouped;     // one selection per kv head (HSLA_SEL_GROUPED)
+  int deterministic;  // static split-K attention (bitwise reproducible)
   float sigma;
   int batch, max_seq_len;
   int max_blocks;  // block table row stride
@@ -33,10 +34,11 @@ struct Problem {
 // Byte offsets into the dynamic LDS of an attention workgroup, where it
 // builds its share of the union: the G heads' selection bitmaps [G][nwords]
 // (uint64), wavefront-private union chunk masks [4][64] (uint64) and chunk
-// prefixes [4][64] (int32), then, when staged, the sequence's block-table
-// row [nblk_max] (int32).
+// prefixes [4][64] (int32), when staged the sequence's block-table row
+// [nblk_max] (int32), and for dynamic attention the whole union list:
+// entries [umax] and pages [umax] (int32).
 struct SelLayout {
-  uint32_t bits, umask, upre, btrow, total;
+  uint32_t bits, umask, upre, btrow, ulist, total;
 };
 
 struct DecodeLayout {
@@ -51,8 +53,9 @@ struct DecodeLayout {
   int sstride;         // order keys per (sequence, head) row, multiple of 4
   int nwords;          // 64-bit words of a per-head selection bitmap
   int bt_staged;       // block-table row staged in LDS
+  int dyn;             // attention workgroups of a pair claim its slices dynamically
   SelLayout sl;
-  size_t off_scores, off_ro, off_roz, off_bits, off_ucount, off_part, total;
+  size_t off_scores, off_ro, off_roz, off_bits, off_ucount, off_ctr, off_part, total;
 };
 DecodeLayout decode_layout(const Problem& p);
 

@@ -96,10 +96,10 @@ class DeviceCache:
 
 
 def config_for(num_q_heads, num_kv_heads, head_dim, block_size, top_k, num_sink, window, linear_tail,
-               kv_dtype: str, scale: float = 0.0, grouped: int = 0) -> Config:
+               kv_dtype: str, scale: float = 0.0, grouped: int = 0, deterministic: int = 0) -> Config:
     return Config(num_q_heads, num_kv_heads, head_dim, block_size, top_k, num_sink, window, linear_tail,
                   HSLA_BF16 if kv_dtype == "bf16" else HSLA_F32, scale,
-                  HSLA_SEL_GROUPED if grouped else HSLA_SEL_PER_HEAD)
+                  HSLA_SEL_GROUPED if grouped else HSLA_SEL_PER_HEAD, int(deterministic))
 
 
 class PreparedDecodeStep:

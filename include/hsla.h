@@ -100,7 +100,13 @@ typedef enum hsla_selection { HSLA_SEL_PER_HEAD = 0, HSLA_SEL_GROUPED = 1 } hsla
  *   "discard" behaviour of SPLA Figure 1(c)).
  * kv_dtype: hsla_dtype of keys, values, queries and appended tokens.
  * scale: sigma; 0 selects 1/sqrt(head_dim).
- * selection: hsla_selection (0 = per head). */
+ * selection: hsla_selection (0 = per head).
+ * deterministic: 1 = bitwise reproducible results: every attention
+ *   workgroup of a (sequence, kv head) takes a fixed share of its exact
+ *   blocks.  0 = those workgroups claim the blocks from a shared counter as
+ *   they go, so that workgroups on faster XCDs take more; the summation
+ *   order, and so the last bits of the output, then vary from run to run
+ *   (selections do not).  fp32 keys/values always run the fixed split. */
 typedef struct hsla_config {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -113,6 +119,7 @@ typedef struct hsla_config {
   int32_t kv_dtype;
   float scale;
   int32_t selection;
+  int32_t deterministic;
 } hsla_config;
 
 /* Paged KV cache [SPLA, "Page Attention and Selection"].

@@ -33,7 +33,8 @@ def _announce(wl, extra=""):
 
 def cfg_of(wl):
     return config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
-                      wl.window, wl.linear_tail, wl.kv_dtype, wl.scale, grouped=wl.grouped)
+                      wl.window, wl.linear_tail, wl.kv_dtype, wl.scale, grouped=wl.grouped,
+                      deterministic=wl.deterministic)
 
 
 def params_of(wl):
@@ -240,7 +241,7 @@ def test_exact_ties_go_to_the_lower_block():
 
 
 def test_page_order_does_not_change_results():
-    wl1 = _wl("pages_a", 51, shuffle_pages=False)
+    wl1 = _wl("pages_a", 51, shuffle_pages=False, deterministic=1)
     wl2 = dataclasses.replace(wl1, name="pages_b", shuffle_pages=True, spare_pages=7)
     _announce(wl1)
     inp1, inp2 = W.make_inputs(wl1), W.make_inputs(wl2)
@@ -251,8 +252,10 @@ def test_page_order_does_not_change_results():
 
 
 def test_runs_are_bitwise_reproducible():
-    wl = W.small("llama8b_small")
-    _announce(wl)
+    """With the fixed split every bit repeats; the dynamic split (below)
+    only changes the summation order."""
+    wl = dataclasses.replace(W.small("llama8b_small"), deterministic=1)
+    _announce(wl, "deterministic")
     inp = W.make_inputs(wl)
     dc, o1, s1 = run_gpu(wl, inp)
     S1 = dc.S.cpu().numpy().copy()
@@ -262,6 +265,37 @@ def test_runs_are_bitwise_reproducible():
     assert np.array_equal(S1.view(np.uint32), dc.S.cpu().numpy().view(np.uint32))
     assert np.array_equal(o1.view(np.uint32), o2.cpu().numpy().view(np.uint32))
     assert np.array_equal(s1, s2.cpu().numpy())
+
+
+def test_dynamic_split_repeats_within_rounding():
+    """The dynamic split: selections repeat exactly, outputs to fp32
+    summation-order rounding, and both match the fixed split."""
+    wl = W.small("llama8b_small")
+    _announce(wl, "dynamic vs fixed split")
+    inp = W.make_inputs(wl)
+    dc, o1, s1 = run_gpu(wl, inp)
+    outs = [o1]
+    for _ in range(3):
+        o, s = dc.decode(to_device(inp["q"]))
+        torch.cuda.synchronize()
+        assert np.array_equal(s1, s.cpu().numpy())
+        outs.append(o.cpu().numpy())
+    _, od, sd = run_gpu(dataclasses.replace(wl, deterministic=1), inp)
+    assert np.array_equal(s1, sd)
+    for o in outs:
+        for b in range(wl.batch):
+            for h in range(wl.num_q_heads):
+                assert row_rel_err(o[b, h], od[b, h]) < 1e-5, (b, h)
+
+
+@pytest.mark.parametrize("name", ["llama8b_small", "needle_small", "ragged_small"])
+def test_fixed_split_workloads(name):
+    wl = dataclasses.replace(W.small(name), deterministic=1)
+    _announce(wl, "fixed split")
+    inp = W.make_inputs(wl)
+    dc, out, sel = run_gpu(wl, inp)
+    worst, flips = check_case(wl, inp, dc, out, sel, check_build=False)
+    print(f"  worst row error {worst:.3e}, near-tie flips {flips}")
 
 
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])

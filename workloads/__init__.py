@@ -59,6 +59,7 @@ class Workload:
     scale: float = 0.0            # 0 means 1/sqrt(head_dim)
     layer: int = 0
     grouped: int = 0              # one block selection per kv head
+    deterministic: int = 0        # fixed split of the attention work (bitwise reproducible)
 
     @property
     def group(self) -> int:
