@@ -1609,7 +1609,7 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
                         hipStream_t stream, RecordFn rec, void* ctx) {
   const int pairs = p.batch * p.Hkv;
   if (rec) rec(ctx, 0, "score_readout");
-  {
+  if (L.score_wgs + L.ro_wgs > 0) {   // neither candidates nor a linear tail: nothing to score or read out
     dim3 grid(L.score_wgs + L.ro_wgs, pairs);
     hipLaunchKernelGGL((k_score_readout<KV, D, G>), grid, dim3(kThreads), 0, stream, P);
     hipError_t e = launch_status("k_score_readout");

@@ -185,8 +185,11 @@ def test_sinks_and_window_only():
 
 
 @pytest.mark.parametrize("lens", [(1, 5), (64, 260), (300, 261), (255, 320)])
-def test_short_sequences_have_no_candidates(lens):
-    wl = _wl(f"short_{lens[0]}_{lens[1]}", 32, seq_lens=lens, window=256, num_sink=4)
+@pytest.mark.parametrize("lin", [1, 0])
+def test_short_sequences_have_no_candidates(lens, lin):
+    """No candidate block anywhere in the batch; without the linear tail the
+    scoring launch then has no work at all."""
+    wl = _wl(f"short_{lens[0]}_{lens[1]}", 32, seq_lens=lens, window=256, num_sink=4, linear_tail=lin)
     _announce(wl)
     inp = W.make_inputs(wl)
     dc, out, sel = run_gpu(wl, inp)
