@@ -646,6 +646,10 @@ __global__ __launch_bounds__(kWave) void k_select_grouped(DecodeParams P) {
 // entry (block | mask of the heads that selected it << 20) and page.  Has a
 // workgroup barrier: every thread calls it.  Split 0 also records the union
 // size for the merge.
+// FULL (the dynamic split): instead of one share, the whole list -- entries
+// and pages, in union order -- is written to LDS (SelLayout::ulist), each
+// wavefront writing the entries of every NW-th chunk, and a second barrier
+// publishes it.
 struct SplitShare {
   int T;       // sequence length (uniform)
   int ent;
@@ -1129,10 +1133,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
 // so the products match the fp32 vector path to ~2^-17 relative while keys,
 // values and queries enter exactly (they are bf16 already).
 //
-// Work: the split's union blocks are cut into slices of 16 rows of one page;
-// wavefront w of the workgroup takes slices w, w + 4, ...  Each wavefront
-// keeps its own running maximum per head, so the slice loop has no
-// workgroup barrier; the four wavefronts are combined once at the end.
+// Work: the union blocks are cut into slices of 16 rows of one page.  With
+// the fixed split (DYN false) wavefront w of the workgroup takes slices w,
+// w + 4, ... of its split; with the dynamic split the wavefronts of all the
+// pair's workgroups claim units of four slices from the pair's counter.
+// Each wavefront keeps its own running maximum per head, so the slice loop
+// has no workgroup barrier; the four wavefronts are combined once at the
+// end.
 // Lane l = 16 q + n: in the score MFMA it carries token n (channels
 // q D/4 .. q D/4 + D/4 of its K row); in the value MFMA it carries tokens
 // 4q .. 4q + 3 of the slice at channels (D/16) n .. (D/16) n + D/16, and its

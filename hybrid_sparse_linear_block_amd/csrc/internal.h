@@ -47,8 +47,8 @@ struct DecodeLayout {
   int ro_wgs;          // readout workgroups per (sequence, kv head)
   int ro_rows;         // rows of S per readout workgroup
   int umax;            // union-list capacity per (sequence, kv head)
-  int bps;             // union blocks per attention split
-  int max_split;       // attention splits per (sequence, kv head)
+  int bps;             // union blocks per attention split (fixed split)
+  int max_split;       // attention workgroups per (sequence, kv head)
   int pstride;         // floats per (split, head) partial
   int sstride;         // order keys per (sequence, head) row, multiple of 4
   int nwords;          // 64-bit words of a per-head selection bitmap
