@@ -1,6 +1,6 @@
 // Decode step of hybrid sparse-plus-linear attention on gfx950.
 //
-// Four kernels, all enqueued on the caller's stream:
+// Up to four kernels, all enqueued on the caller's stream:
 //   1. k_score_readout  per (sequence, kv head): block scores of the candidate
 //      blocks for the G query heads of the group, read from the per-block
 //      mean / variance statistics ("SPLA: Block Sparse Plus Linear Attention
@@ -8,16 +8,19 @@
 //      Taylor Expansion"), and, in the same launch, the readout of the global
 //      linear state S^T q, q.z for those heads ("Residual Linear Attention
 //      (RLA)").
-//   2. k_select         one wavefront per query head: radix select of the
-//      top-k candidates (score desc, index asc), ascending index output, and
-//      the per-(sequence, kv head) union of the group's exact blocks (sinks,
-//      window and selected blocks) with a per-block mask of the heads that
-//      selected it (SPLA Figure 1(a)).
-//   3. k_attend         split-K over the union: each page is read once per kv
-//      head and serves every query head that needs it; online softmax for
-//      the exact part plus the first-order-Taylor sums sum(1+s)v, sum(1+s)
-//      of the exact tokens, which are subtracted from the global state
-//      (SPLA Abstract, "global minus selected").
+//   2. selection        top-k candidates per query head (score desc, index
+//      asc), ascending index output, as a bitmap per head.  Up to 1024
+//      candidates it runs inside the attention prologue (each wavefront one
+//      head); beyond that, and for the grouped variant, in its own kernel
+//      (k_select / k_select_grouped).
+//   3. k_attend         split-K over the union of the group's exact blocks
+//      (sinks, window and selected blocks, SPLA Figure 1(a)), which each
+//      workgroup builds from the bitmaps with a per-block mask of the heads
+//      that selected it: each page is read once per kv head and serves every
+//      query head that needs it; online softmax for the exact part plus the
+//      first-order-Taylor sums sum(1+s)v, sum(1+s) of the exact tokens, which
+//      are subtracted from the global state (SPLA Abstract, "global minus
+//      selected").
 //   4. k_merge          log-sum-exp combination of the splits and the
 //      residual linear part into the normalised output.
 #include <math.h>
@@ -48,6 +51,7 @@ constexpr int kAttendWgsTarget = 256;
 constexpr int kCtrStride = 32;       // ints between two pairs' work counters (one 128-byte line each)
 constexpr int kUnitSlices = 4;       // slices per dynamically claimed unit
 constexpr int kMaxDynList = 2048;    // union entries a dynamic attention workgroup holds in LDS
+constexpr int kFusedKplMax = 16;     // keys per lane of the selection fused into the attention prologue: 8 or 16
 constexpr size_t kBtStageBytes = 8 * 1024;      // block-table row staged in LDS up to this size
 
 struct DecodeParams {
@@ -76,6 +80,7 @@ struct DecodeParams {
   int umax, bps, max_split, pstride;
   int sstride, nwords, bt_staged;
   int dyn;          // attention workgroups of a pair claim its slices dynamically
+  int fused_sel;    // per-head selection inside the attention prologue (no selection kernel)
   SelLayout sl;
   float sigma;
 };
@@ -298,6 +303,8 @@ __global__ __launch_bounds__(kThreads) void k_score_readout(DecodeParams P) {
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
   const int x = blockIdx.x;
+  if (P.dyn && P.fused_sel && x == 0 && threadIdx.x == 0)   // the pair's work counter for the attention kernel
+    __hip_atomic_store(P.ctr + static_cast<size_t>(pair) * kCtrStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (x < P.score_wgs) {
     score_part<KV, D, G>(P, b, g, x);
   } else {
@@ -657,7 +664,7 @@ struct SplitShare {
   int count;   // union size (uniform)
   int ne;      // entries of this split (uniform)
 };
-template <int G, bool FULL, typename Stage>
+template <int G, bool FULL, int FK, typename Stage>
 __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, int b, int g, int split,
                                   Stage&& stage) {
   constexpr int NW = kThreads / kWave;
@@ -672,16 +679,29 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
   const int S = P.max_split;
   const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
   const uint64_t* src = P.bits + (static_cast<size_t>(b) * P.Hq + g * G) * nwords;
-  const int nbits = G * nwords;
+  const int nbits = P.fused_sel ? 0 : G * nwords;   // bitmaps loaded from the selection kernel
+  constexpr int HPW = (G + NW - 1) / NW;            // heads per wavefront of the fused selection
 
-  // ---- bitmaps and block-table row.  The first round of both is loaded
-  // before the sequence length is read and together with the caller's own
-  // loads, which `stage` then stores, so that the usual sizes take a single
-  // round trip; larger rows loop on.
+  // ---- bitmaps (or, with the selection fused here, the order keys of the
+  // wavefront's heads) and block-table row.  The first round of each is
+  // loaded before the sequence length is read and together with the
+  // caller's own loads, which `stage` then stores, so that the usual sizes
+  // take a single round trip; larger rows loop on.
   uint64_t v[2];
   int w[4];
+  uint32_t kr[HPW][FK];
+  if (P.fused_sel) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u) v[u] = src[min(tid + u * kThreads, nbits - 1)];
+    for (int i = 0; i < HPW; ++i) {
+      const int h = min(wave + NW * i, G - 1);
+      const uint32_t* kh = P.keys + (static_cast<size_t>(b) * P.Hq + g * G + h) * P.sstride;
+#pragma unroll
+      for (int j = 0; j < FK; ++j) kr[i][j] = kh[min(lane + kWave * j, P.sstride - 1)];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) v[u] = src[min(tid + u * kThreads, max(nbits, 1) - 1)];
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) w[u] = bt[min(tid + u * kThreads, P.nblk_max - 1)];
   const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
@@ -710,6 +730,22 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (base + tid + u * kThreads < nbt) btrow[base + tid + u * kThreads] = w[u];
+    }
+  }
+  if (P.fused_sel) {
+    // each wavefront selects for its heads; the bitmaps go to LDS and, from
+    // the pair's first workgroup, the indices to sel_idx
+    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + P.sl.hist) + wave * 256;
+    auto no_key = [](int) -> uint32_t { return 0u; };   // the keys are all in registers
+#pragma unroll
+    for (int i = 0; i < HPW; ++i) {
+      const int h = wave + NW * i;
+      if (h < G) {
+        int32_t* out = (P.sel_idx && split == 0)
+                           ? P.sel_idx + (static_cast<size_t>(b) * P.Hq + g * G + h) * P.top_k
+                           : nullptr;
+        head_select<FK>(no_key, kr[i], nc, P.top_k, nwords, lane, hist, bits + h * nwords, out, cr.lo);
+      }
     }
   }
   __syncthreads();
@@ -882,7 +918,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
     qr[h].load(reinterpret_cast<const char*>(P.q) +
                ((static_cast<size_t>(b) * P.Hq + g * G + h) * D + lig * 8) * KV::kBytes);
   extern __shared__ uint64_t dyn_lds[];
-  const SplitShare share = union_share<G, false>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, [] {});
+  const SplitShare share = union_share<G, false, kFusedKplMax>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split,
+                                                               [] {});
   const int T = share.T;
   if (split >= share.count) return;
   const int ne = share.ne;
@@ -1176,7 +1213,7 @@ struct VSlice<4> {   // D = 64: 4 channels of a row per lane
   __device__ __forceinline__ void zero() { r = make_uint2(0, 0); }
 };
 
-template <int D, int G, bool DYN>
+template <int D, int G, bool DYN, int FK>
 __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   constexpr int NW = kThreads / kWave;
   constexpr int KS = D / 32;            // score MFMAs per slice (32 channels each)
@@ -1224,7 +1261,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     if (q_row < 16) q_lds[q_row][q_col] = qv;
   };
   extern __shared__ uint64_t dyn_lds[];
-  const SplitShare share = union_share<G, DYN>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, stage_q);
+  const SplitShare share = union_share<G, DYN, FK>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, stage_q);
   const int T = share.T;
   const int win0 = T - P.W;
   if (!DYN && split >= share.count) return;
@@ -1615,15 +1652,18 @@ template <typename KV, int D, int G>
 hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodeParams& P,
                         hipStream_t stream, RecordFn rec, void* ctx) {
   const int pairs = p.batch * p.Hkv;
-  if (rec) rec(ctx, 0, "score_readout");
+  int ev = 0;   // profiling events: one before each launched kernel, one after the last
+  if (rec) rec(ctx, ev++, "score_readout");
   if (L.score_wgs + L.ro_wgs > 0) {   // neither candidates nor a linear tail: nothing to score or read out
     dim3 grid(L.score_wgs + L.ro_wgs, pairs);
     hipLaunchKernelGGL((k_score_readout<KV, D, G>), grid, dim3(kThreads), 0, stream, P);
     hipError_t e = launch_status("k_score_readout");
     if (e != hipSuccess) return e;
   }
-  if (rec) rec(ctx, 1, "select");
-  if (p.grouped) {
+  if (L.fused_sel) {
+    // selection runs in the attention prologue
+  } else if (p.grouped) {
+    if (rec) rec(ctx, ev++, "select");
     // keys in registers up to G x KPL <= 64 per lane
     const dim3 grid(pairs);
     const int kpl = p.nc_max <= 4 * kWave ? 4 : p.nc_max <= 8 * kWave ? 8 : p.nc_max <= 16 * kWave ? 16 : 0;
@@ -1639,6 +1679,7 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
     hipError_t e = launch_status("k_select_grouped");
     if (e != hipSuccess) return e;
   } else {
+    if (rec) rec(ctx, ev++, "select");
     const dim3 grid(p.batch * p.Hq);
     if (p.nc_max <= 4 * kWave)
       hipLaunchKernelGGL((k_select<4>), grid, dim3(kWave), 0, stream, P);
@@ -1653,15 +1694,21 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
     hipError_t e = launch_status("k_select");
     if (e != hipSuccess) return e;
   }
-  if (rec) rec(ctx, 2, "attend");
+  if (rec) rec(ctx, ev++, "attend");
   {
     const size_t lds = L.sl.total;   // union data; within the default dynamic LDS limit
     const dim3 grid(pairs * L.max_split);
     if constexpr (KV::kBytes == 2) {
-      if (P.dyn)
-        hipLaunchKernelGGL((k_attend_mfma<D, G, true>), grid, dim3(kThreads), lds, stream, P);
+      // keys per lane of the fused selection: 8 up to 512 candidates
+      const bool fk8 = p.nc_max <= 8 * kWave;
+      if (P.dyn && fk8)
+        hipLaunchKernelGGL((k_attend_mfma<D, G, true, 8>), grid, dim3(kThreads), lds, stream, P);
+      else if (P.dyn)
+        hipLaunchKernelGGL((k_attend_mfma<D, G, true, 16>), grid, dim3(kThreads), lds, stream, P);
+      else if (fk8)
+        hipLaunchKernelGGL((k_attend_mfma<D, G, false, 8>), grid, dim3(kThreads), lds, stream, P);
       else
-        hipLaunchKernelGGL((k_attend_mfma<D, G, false>), grid, dim3(kThreads), lds, stream, P);
+        hipLaunchKernelGGL((k_attend_mfma<D, G, false, 16>), grid, dim3(kThreads), lds, stream, P);
     }
     else if (p.B >= kUnit)
       hipLaunchKernelGGL((k_attend<KV, D, G, true>), grid, dim3(kThreads), lds, stream, P);
@@ -1670,13 +1717,13 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
     hipError_t e = launch_status("k_attend");
     if (e != hipSuccess) return e;
   }
-  if (rec) rec(ctx, 3, "merge");
+  if (rec) rec(ctx, ev++, "merge");
   {
     hipLaunchKernelGGL((k_merge<D, G>), dim3(p.batch * p.Hq), dim3(kThreads), 0, stream, P);
     hipError_t e = launch_status("k_merge");
     if (e != hipSuccess) return e;
   }
-  if (rec) rec(ctx, 4, nullptr);
+  if (rec) rec(ctx, ev, nullptr);
   return hipSuccess;
 }
 
@@ -1709,7 +1756,11 @@ DecodeLayout decode_layout(const Problem& p) {
   L.umax = static_cast<int>(std::max<long>(1, std::min<long>(bound, p.nblk_max)));
   // Dynamic attention (bf16 path): the pair's workgroups share its union
   // list, which the prologue keeps whole in LDS.
-  L.dyn = (p.bf16 && !p.deterministic && L.umax <= kMaxDynList) ? 1 : 0;
+  L.fused_sel = (!p.grouped && p.nc_max <= kFusedKplMax * kWave) ? 1 : 0;
+  // with the selection fused, the scoring kernel zeroes the work counters,
+  // so the dynamic split needs that launch
+  const bool scores_launched = (p.nc_max > 0) || p.linear_tail;
+  L.dyn = (p.bf16 && !p.deterministic && L.umax <= kMaxDynList && (!L.fused_sel || scores_launched)) ? 1 : 0;
   {
     const int want = std::max(1, (kAttendWgsTarget + pairs / 2) / pairs);
     if (L.dyn) {
@@ -1737,6 +1788,7 @@ DecodeLayout decode_layout(const Problem& p) {
     L.sl.upre = take((kThreads / kWave) * kWave * sizeof(int32_t));
     L.sl.btrow = take(L.bt_staged ? static_cast<uint32_t>(p.nblk_max * sizeof(int32_t)) : 0u);
     L.sl.ulist = take(L.dyn ? static_cast<uint32_t>(2 * L.umax * sizeof(int32_t)) : 0u);
+    L.sl.hist = take(L.fused_sel ? static_cast<uint32_t>((kThreads / kWave) * 256 * sizeof(uint32_t)) : 0u);
     L.sl.total = o;
   }
   size_t off = 0;
@@ -1780,6 +1832,7 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.ucount = reinterpret_cast<int32_t*>(a.ws + L.off_ucount);
   P.ctr = reinterpret_cast<int32_t*>(a.ws + L.off_ctr);
   P.dyn = L.dyn;
+  P.fused_sel = L.fused_sel;
   P.part = reinterpret_cast<float*>(a.ws + L.off_part);
   P.Hq = p.Hq;
   P.Hkv = p.Hkv;

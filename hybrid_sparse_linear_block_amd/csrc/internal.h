@@ -35,10 +35,11 @@ struct Problem {
 // builds its share of the union: the G heads' selection bitmaps [G][nwords]
 // (uint64), wavefront-private union chunk masks [4][64] (uint64) and chunk
 // prefixes [4][64] (int32), when staged the sequence's block-table row
-// [nblk_max] (int32), and for dynamic attention the whole union list:
-// entries [umax] and pages [umax] (int32).
+// [nblk_max] (int32), for dynamic attention the whole union list: entries
+// [umax] and pages [umax] (int32), and for the fused selection the
+// wavefronts' radix histograms [4][256] (uint32).
 struct SelLayout {
-  uint32_t bits, umask, upre, btrow, ulist, total;
+  uint32_t bits, umask, upre, btrow, ulist, hist, total;
 };
 
 struct DecodeLayout {
@@ -54,6 +55,7 @@ struct DecodeLayout {
   int nwords;          // 64-bit words of a per-head selection bitmap
   int bt_staged;       // block-table row staged in LDS
   int dyn;             // attention workgroups of a pair claim its slices dynamically
+  int fused_sel;       // per-head selection in the attention prologue
   SelLayout sl;
   size_t off_scores, off_ro, off_roz, off_bits, off_ucount, off_ctr, off_part, total;
 };
