@@ -472,56 +472,98 @@ __device__ __forceinline__ void head_select(KeyAt key_at, const uint32_t* key, i
   uint32_t thr = 0;
   int rem = k;
   if (!take_all && !take_none) wave_topk_threshold<KPL>(key, key_at, nc, k, lane, hist, thr, rem);
-  int nsel = 0, neq = 0;
-  // When every key equal to the threshold is taken, the selection is just
-  // key >= thr and no rank among equal keys is needed.
-  bool simple = take_all || take_none;
-  if (!simple) {
-    int eq_total = 0;
-    if constexpr (KPL > 0) {
+  int nsel = 0;
+  if constexpr (KPL > 0) {
+    // Keys in registers: every word's masks first (independent ballots),
+    // then the selection as 64-bit mask arithmetic in scalar registers, then
+    // the stores -- no chain of dependent per-word steps.
+    uint64_t vm[KPL], gm[KPL], em[KPL];   // valid, above the threshold, equal to it
 #pragma unroll
-      for (int w = 0; w < KPL; ++w) eq_total += __popcll(__ballot(w * kWave + lane < nc && key[w] == thr));
-    } else {
+    for (int w = 0; w < KPL; ++w) {
+      const bool valid = w * kWave + lane < nc;
+      vm[w] = __ballot(valid);
+      gm[w] = __ballot(valid && key[w] > thr);
+      em[w] = __ballot(valid && key[w] == thr);
+    }
+    int eq_total = 0;
+#pragma unroll
+    for (int w = 0; w < KPL; ++w) eq_total += __popcll(em[w]);
+    uint64_t sm[KPL];
+    int eq_left = rem;   // keys equal to the threshold still to take, lowest indices first
+#pragma unroll
+    for (int w = 0; w < KPL; ++w) {
+      if (take_none) {
+        sm[w] = 0ull;
+      } else if (take_all) {
+        sm[w] = vm[w];
+      } else if (eq_total == rem) {   // every equal key is taken
+        sm[w] = gm[w] | em[w];
+      } else {
+        uint64_t e = em[w];
+        const int c = __popcll(e);
+        if (c > eq_left) {   // keep the lowest eq_left of them
+          uint64_t keep = 0ull;
+          for (int r = 0; r < eq_left; ++r) {
+            const uint64_t low = e & (~e + 1ull);
+            keep |= low;
+            e ^= low;
+          }
+          e = keep;
+        }
+        eq_left -= __popcll(e);
+        sm[w] = gm[w] | e;
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < KPL; ++w) {
+      if (w < nwords) {
+        const int pos = nsel + __popcll(sm[w] & lanes_below(lane));
+        const bool sel = (sm[w] >> lane) & 1ull;
+        for (int x = 0; x < ncopy; ++x) {
+          if (sel && out && pos < k) out[pos + x * k] = lo + w * kWave + lane;
+          if (lane == 0) bits_row[w + x * nwords] = sm[w];
+        }
+        nsel += __popcll(sm[w]);
+      }
+    }
+  } else {
+    int neq = 0;
+    // When every key equal to the threshold is taken, the selection is just
+    // key >= thr and no rank among equal keys is needed.
+    bool simple = take_all || take_none;
+    if (!simple) {
+      int eq_total = 0;
       for (int w = 0; w < nwords; ++w) {
         const int i = w * kWave + lane;
         eq_total += __popcll(__ballot(i < nc && key_at(i) == thr));
       }
+      simple = eq_total == rem;
     }
-    simple = eq_total == rem;
-  }
-  auto word = [&](int w, uint32_t x) {
-    const int i = w * kWave + lane;
-    const bool valid = i < nc;
-    bool sel;
-    if (take_none) {
-      sel = false;
-    } else if (take_all) {
-      sel = valid;
-    } else if (simple) {
-      sel = valid && x >= thr;
-    } else {
-      const bool eq = valid && x == thr;
-      const uint64_t eqm = __ballot(eq);
-      const int eqrank = neq + __popcll(eqm & lanes_below(lane));
-      sel = valid && (x > thr || (eq && eqrank < rem));
-      neq += __popcll(eqm);
-    }
-    const uint64_t sm = __ballot(sel);
-    const int pos = nsel + __popcll(sm & lanes_below(lane));
-    for (int x = 0; x < ncopy; ++x) {
-      if (sel && out && pos < k) out[pos + x * k] = lo + i;
-      if (lane == 0) bits_row[w + x * nwords] = sm;
-    }
-    nsel += __popcll(sm);
-  };
-  if constexpr (KPL > 0) {
-#pragma unroll
-    for (int w = 0; w < KPL; ++w)
-      if (w < nwords) word(w, key[w]);
-  } else {
     for (int w = 0; w < nwords; ++w) {
       const int i = w * kWave + lane;
-      word(w, i < nc ? key_at(i) : 0u);
+      const bool valid = i < nc;
+      const uint32_t x = valid ? key_at(i) : 0u;
+      bool sel;
+      if (take_none) {
+        sel = false;
+      } else if (take_all) {
+        sel = valid;
+      } else if (simple) {
+        sel = valid && x >= thr;
+      } else {
+        const bool eq = valid && x == thr;
+        const uint64_t eqm = __ballot(eq);
+        const int eqrank = neq + __popcll(eqm & lanes_below(lane));
+        sel = valid && (x > thr || (eq && eqrank < rem));
+        neq += __popcll(eqm);
+      }
+      const uint64_t sm = __ballot(sel);
+      const int pos = nsel + __popcll(sm & lanes_below(lane));
+      for (int c = 0; c < ncopy; ++c) {
+        if (sel && out && pos < k) out[pos + c * k] = lo + i;
+        if (lane == 0) bits_row[w + c * nwords] = sm;
+      }
+      nsel += __popcll(sm);
     }
   }
   if (out)
