@@ -51,6 +51,7 @@ constexpr int kAttendWgsTarget = 256;
 constexpr int kCtrStride = 32;       // ints between two pairs' work counters (one 128-byte line each)
 constexpr int kUnitSlices = 4;       // slices per dynamically claimed unit
 constexpr int kMaxDynList = 2048;    // union entries a dynamic attention workgroup holds in LDS
+constexpr int kDeadT0 = 1 << 30;     // first token of a slice whose rows are all invalid
 constexpr int kFusedKplMax = 16;     // keys per lane of the selection fused into the attention prologue: 8 or 16
 constexpr size_t kBtStageBytes = 8 * 1024;      // block-table row staged in LDS up to this size
 
@@ -706,9 +707,9 @@ struct SplitShare {
   int count;   // union size (uniform)
   int ne;      // entries of this split (uniform)
 };
-template <int G, bool FULL, int FK, typename Stage>
+template <int G, bool FULL, int FK, typename Stage, typename Early>
 __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, int b, int g, int split,
-                                  Stage&& stage) {
+                                  Stage&& stage, Early&& early) {
   constexpr int NW = kThreads / kWave;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -773,6 +774,13 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
       for (int u = 0; u < 4; ++u)
         if (base + tid + u * kThreads < nbt) btrow[base + tid + u * kThreads] = w[u];
     }
+  }
+  if constexpr (FULL) {
+    // The blocks past the candidates (window blocks) are in the union
+    // whatever the selection: the caller may start loading them now, so that
+    // they arrive while the selection runs.
+    __syncthreads();   // the block-table row
+    early(nc > 0 ? cr.lo + nc : 0, nb, P.bt_staged ? btrow : bt);
   }
   if (P.fused_sel) {
     // each wavefront selects for its heads; the bitmaps go to LDS and, from
@@ -961,7 +969,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
                ((static_cast<size_t>(b) * P.Hq + g * G + h) * D + lig * 8) * KV::kBytes);
   extern __shared__ uint64_t dyn_lds[];
   const SplitShare share = union_share<G, false, kFusedKplMax>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split,
-                                                               [] {});
+                                                               [] {}, [](int, int, const int32_t*) {});
   const int T = share.T;
   if (split >= share.count) return;
   const int ne = share.ne;
@@ -1302,8 +1310,47 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   auto stage_q = [&] {
     if (q_row < 16) q_lds[q_row][q_col] = qv;
   };
+  const char* kp = reinterpret_cast<const char*>(P.k_pages);
+  const char* vp = reinterpret_cast<const char*>(P.v_pages);
+  const size_t k_lane = (static_cast<size_t>(n16) * D + q4 * (D / 4)) * 2;
+  const size_t v_lane = (static_cast<size_t>(4 * q4) * D + NT * n16) * 2;
+
+  struct Slice {
+    uint4 k[KS];
+    VSlice<NT> v[4];
+    int t0;   // first token (uniform); kDeadT0 for a slice without a page (no row valid)
+    int fm;   // heads that selected the block (uniform)
+  };
+  // Slice `sub` of union entry (ent, page pg); a dead slice re-reads a live
+  // one (an L2 hit) and marks every row invalid.
+  auto load_slice = [&](int ent, int pg, int sub, bool live, Slice& x) __attribute__((always_inline)) {
+    const size_t base = ((static_cast<size_t>(max(pg, 0)) * P.Hkv + g) * B + sub * SL) * D * 2;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) x.k[s] = *reinterpret_cast<const uint4*>(kp + base + k_lane + 16 * s);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x.v[j].load(vp + base + v_lane + static_cast<size_t>(j) * D * 2);
+    x.t0 = (live && pg >= 0) ? (ent & 0xFFFFF) * B + sub * SL : kDeadT0;
+    x.fm = (ent >> 20) & kAll;
+    // keep the loads ahead of the previous slice's arithmetic
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Dynamic split: this wavefront's slice of the window blocks, loaded
+  // before the selection (slice split * NW + wave of the window region, if
+  // there is one; the first npre slices of that region are taken this way).
+  Slice pre;
+  int npre = 0, nwin_sl = 0;
+  auto early = [&](int jw0, int nbk, const int32_t* pages) __attribute__((always_inline)) {
+    nwin_sl = (nbk - jw0) * spb;
+    npre = min(P.max_split * NW, nwin_sl);
+    const int gw = split * NW + wave;
+    const bool live = DYN && gw < npre;
+    const int j = jw0 + (live ? gw : 0) / spb;
+    const int sub = (live ? gw : 0) % spb;
+    load_slice(j, live ? pages[j] : 0, sub, live, pre);
+  };
   extern __shared__ uint64_t dyn_lds[];
-  const SplitShare share = union_share<G, DYN, FK>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, stage_q);
+  const SplitShare share =
+      union_share<G, DYN, FK>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, stage_q, early);
   const int T = share.T;
   const int win0 = T - P.W;
   if (!DYN && split >= share.count) return;
@@ -1325,30 +1372,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) l_acc[mt] = 0.f;
 
-  const char* kp = reinterpret_cast<const char*>(P.k_pages);
-  const char* vp = reinterpret_cast<const char*>(P.v_pages);
-  const size_t k_lane = (static_cast<size_t>(n16) * D + q4 * (D / 4)) * 2;
-  const size_t v_lane = (static_cast<size_t>(4 * q4) * D + NT * n16) * 2;
-
-  struct Slice {
-    uint4 k[KS];
-    VSlice<NT> v[4];
-    int t0;   // first token (uniform); T for a slice without a page (no row valid)
-    int fm;   // heads that selected the block (uniform)
-  };
-  // Slice `sub` of union entry (ent, page pg); a dead slice re-reads a live
-  // one (an L2 hit) and marks every row invalid.
-  auto load_slice = [&](int ent, int pg, int sub, bool live, Slice& x) __attribute__((always_inline)) {
-    const size_t base = ((static_cast<size_t>(max(pg, 0)) * P.Hkv + g) * B + sub * SL) * D * 2;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) x.k[s] = *reinterpret_cast<const uint4*>(kp + base + k_lane + 16 * s);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x.v[j].load(vp + base + v_lane + static_cast<size_t>(j) * D * 2);
-    x.t0 = (live && pg >= 0) ? (ent & 0xFFFFF) * B + sub * SL : T;
-    x.fm = (ent >> 20) & kAll;
-    // keep the loads ahead of the previous slice's arithmetic
-    __builtin_amdgcn_sched_barrier(0);
-  };
   // Static split: slice kk of this wavefront is slice wave + NW kk of the
   // split, whose entries lane e holds.
   auto fetch = [&](int kk, Slice& x) __attribute__((always_inline)) {
@@ -1464,7 +1487,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     const int32_t* uent = reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(dyn_lds) + P.sl.ulist);
     const int32_t* upg = uent + P.umax;
     const int total = share.count * spb;
-    const int nunits = ceil_div(total, kUnitSlices);
+    // the window region is the list's tail; its first npre slices were
+    // prefetched, the rest of the list is claimed
+    const int w0 = total - nwin_sl;
+    const int nclaim = total - npre;
+    const int nunits = ceil_div(nclaim, kUnitSlices);
     int32_t* ctr = P.ctr + static_cast<size_t>(pair) * kCtrStride;
     auto claim = [&]() -> int {   // the claimed unit, in lane 0
       int v = 0;
@@ -1472,26 +1499,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
       return v;
     };
     auto fetch_u = [&](int u, int i, Slice& x) __attribute__((always_inline)) {
-      const int q = u * kUnitSlices + i;
-      const bool live = u < nunits && q < total;
+      const int qc = u * kUnitSlices + i;
+      const bool live = u < nunits && qc < nclaim;
+      const int q = qc < w0 ? qc : qc + npre;
       const int e = (live ? q : 0) / spb;
       const int sub = (live ? q : 0) - e * spb;
       load_slice(__builtin_amdgcn_readfirstlane(uent[e]), __builtin_amdgcn_readfirstlane(upg[e]), sub, live, x);
     };
     static_assert(kUnitSlices == 4, "the loop body processes four slices");
     int ua = __builtin_amdgcn_readfirstlane(claim());
-    fetch_u(ua, 0, sa);
+    fetch_u(ua, 0, sb);
+    process(pre);   // the prefetched window slice (all rows masked if none)
     while (ua < nunits) {
       const int cn = claim();
-      fetch_u(ua, 1, sb);
-      process(sa);
-      fetch_u(ua, 2, sa);
+      fetch_u(ua, 1, sa);
       process(sb);
-      fetch_u(ua, 3, sb);
+      fetch_u(ua, 2, sb);
       process(sa);
+      fetch_u(ua, 3, sa);
+      process(sb);
       ua = __builtin_amdgcn_readfirstlane(cn);
-      fetch_u(ua, 0, sa);
-      process(sb);
+      fetch_u(ua, 0, sb);
+      process(sa);
     }
   } else {
     // Static split.  The loop has a single exit: an odd count ends with a
