@@ -1334,19 +1334,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     // keep the loads ahead of the previous slice's arithmetic
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Dynamic split: this wavefront's slice of the window blocks, loaded
-  // before the selection (slice split * NW + wave of the window region, if
-  // there is one; the first npre slices of that region are taken this way).
-  Slice pre;
+  // Dynamic split: this wavefront's slices of the window blocks, loaded
+  // before the selection: slices r = split * NW + wave + m S NW (m < kPre)
+  // of the window region, so that its first npre slices are taken this way.
+  // One per wavefront measured faster than two.
+  constexpr int kPre = 1;
+  Slice pre[kPre];
   int npre = 0, nwin_sl = 0;
   auto early = [&](int jw0, int nbk, const int32_t* pages) __attribute__((always_inline)) {
     nwin_sl = (nbk - jw0) * spb;
-    npre = min(P.max_split * NW, nwin_sl);
-    const int gw = split * NW + wave;
-    const bool live = DYN && gw < npre;
-    const int j = jw0 + (live ? gw : 0) / spb;
-    const int sub = (live ? gw : 0) % spb;
-    load_slice(j, live ? pages[j] : 0, sub, live, pre);
+    const int span = P.max_split * NW;
+    npre = min(kPre * span, nwin_sl);
+#pragma unroll
+    for (int m = 0; m < kPre; ++m) {
+      const int r = split * NW + wave + m * span;
+      const bool live = DYN && r < npre;
+      const int j = jw0 + (live ? r : 0) / spb;
+      const int sub = (live ? r : 0) % spb;
+      load_slice(j, live ? pages[j] : 0, sub, live, pre[m]);
+    }
   };
   extern __shared__ uint64_t dyn_lds[];
   const SplitShare share =
@@ -1509,7 +1515,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     static_assert(kUnitSlices == 4, "the loop body processes four slices");
     int ua = __builtin_amdgcn_readfirstlane(claim());
     fetch_u(ua, 0, sb);
-    process(pre);   // the prefetched window slice (all rows masked if none)
+#pragma unroll
+    for (int m = 0; m < kPre; ++m) process(pre[m]);   // the prefetched window slices (masked if none)
     while (ua < nunits) {
       const int cn = claim();
       fetch_u(ua, 1, sa);
