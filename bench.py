@@ -1,10 +1,12 @@
 """Decode-step benchmark of hybrid sparse-plus-linear attention on one MI355X.
 
 A step is one pass of the decode hot path for every sequence of the batch:
-hsla_append_token (the new token's k/v into its page, rank-1 update of the
-linear state, statistics of a block that fills) followed by hsla_decode
-(block scores + state readout, top-k, split-K exact attention over sinks,
-window and selected blocks, merge with the subtracted linear residual).
+the append of the new token (its k/v into its page, rank-1 update of the
+linear state, statistics of a block that fills) and the decode at the grown
+length (block scores + state readout, top-k, split-K exact attention over
+sinks, window and selected blocks, merge with the subtracted linear
+residual), as one hsla_append_decode call (--separate-append: the
+hsla_append_token + hsla_decode pair).
 The state/statistics build runs once per cache before the timed region and
 is reported separately under "build".
 
@@ -36,14 +38,17 @@ HBM_PEAK_GBS = 8000.0
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 METRIC = "decode attention µs/step & tokens/s at 32K/128K ctx; % of HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
+STEP_FUSED = "hsla_append_decode (append + decode, one call)"
+STEP_SEPARATE = "hsla_append_token + hsla_decode"
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama8b_32k", choices=["llama8b_32k", "needle_128k", "ragged_paged"])
+    ap.add_argument("--workload", default="llama8b_32k",
+                    choices=["llama8b_32k", "needle_128k", "ragged_paged", "hybrid32_32k"])
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--deterministic", action="store_true",
                     help="fixed split of the attention work (bitwise reproducible) instead of the dynamic one")
@@ -57,7 +62,9 @@ def parse():
                     help="rocprofv3 counter files of two --traffic-run passes -> profiles/attend_traffic.json")
     ap.add_argument("--profile-summary", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="rocprofv3 --stats kernel file -> markdown summary on stdout")
-    return ap.parse_args()
+    ap.add_argument("--separate-append", action="store_true",
+                    help="step = hsla_append_token + hsla_decode instead of one hsla_append_decode call")
+    return ap.parse_args(argv)
 
 
 def workload(name, grouped=False):
@@ -136,9 +143,12 @@ def step_bytes(wl, lens, sel):
 
 
 def append_bytes(wl):
-    d, e = wl.head_dim, wl.elem_bytes
-    per_pair = 2 * d * d * 4 + 2 * 2 * d * 4 + 2 * d * e + 2 * d * e
-    return per_pair * wl.batch * wl.num_kv_heads
+    """Bytes of one append per step, amortised: the new k/v row read and
+    written every step; once per block (every B steps) the completed block
+    read and the state read and written."""
+    d, e, B = wl.head_dim, wl.elem_bytes, wl.block_size
+    per_pair = 2 * (2 * d * e) + (B * 2 * d * e + 2 * (d * d + 2 * d) * 4) / B
+    return int(per_pair * wl.batch * wl.num_kv_heads)
 
 
 def source_sha():
@@ -245,6 +255,25 @@ def profile_summary(stats_csv, command):
         n = re.sub(r"\(.*$", "", n)
         lines.append(f"| `{n[:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    trace = os.path.join(os.path.dirname(stats_csv), os.path.basename(stats_csv).replace("kernel_stats", "kernel_trace"))
+    if os.path.exists(trace):
+        # Attention dispatches in launch order, split into the phases of the
+        # default benchmark run (main() below launches them in this order).
+        import shlex
+        a = parse(shlex.split(command.split(" -- ", 1)[1])[2:]) if " -- " in command else parse([])
+        K, Wm, R = a.steps, a.warmup, max(1, a.replicas)
+        rows = sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"]))
+        us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows if "k_attend" in r["Kernel_Name"]]
+        phases = [("spot check", 1), ("warmup steps", Wm), ("timed steps", K), ("event-timed steps", K),
+                  ("selection reads", R), ("warm decode-only loop", K)]
+        if len(us) == sum(n for _, n in phases):
+            lines += ["", "Attention dispatches by phase of the run (from the kernel trace of the same run):", "",
+                      "| phase | calls | avg us | median us |", "|---|---:|---:|---:|"]
+            at = 0
+            for name, n in phases:
+                seg = us[at:at + n]
+                at += n
+                lines.append(f"| {name} | {n} | {np.mean(seg):.2f} | {np.median(seg):.2f} |")
     return "\n".join(lines)
 
 
@@ -292,12 +321,59 @@ def cpu_baseline(wl, inp_q, gpu_out, gpu_sel, budget_s):
             break
     per_head = t_heads / heads_done
     step_s = per_head * wl.batch * wl.num_q_heads
+    # the same decodes on one thread, for the first group only
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        K, V = W.gen_pair(wl, 0, 0, inp_q)
+        Kf, Vf = O.to_f64(K, wl.kv_dtype), O.to_f64(V, wl.kv_dtype)
+        stats = O.block_statistics(Kf, wl.block_size)
+        state = O.global_state(Kf, Vf)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            shared = (O.group_selection(O.to_f64(inp_q[0, :wl.group], wl.kv_dtype), Kf, p, stats=stats)[3]
+                      if wl.grouped else None)
+            for h in range(wl.group):
+                O.decode_head(O.to_f64(inp_q[0, h], wl.kv_dtype), Kf, Vf, p, stats=stats, state=state,
+                              selected=shared)
+            one = (time.perf_counter() - t0) / wl.group
+        single = round(wl.batch / (one * wl.batch * wl.num_q_heads), 2)
+    except ImportError:  # pragma: no cover
+        pass
     return dict(value=wl.batch / step_s, unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=(f"{heads_done} of {wl.batch * wl.num_q_heads} (sequence, query head) decodes of one "
                         f"step at T={max(wl.seq_lens)}, fp64 subtraction form with statistics and state "
                         f"precomputed{'; grouped selection timed with its heads' if wl.grouped else ''}; "
                         f"step time = mean per head x {wl.batch * wl.num_q_heads}; append not included"),
-                seconds=round(t_heads, 3), ms_per_step=round(step_s * 1e3, 1)), worst
+                seconds=round(t_heads, 3), ms_per_step=round(step_s * 1e3, 1),
+                single_thread_value=single), worst
+
+
+def memory_probe():
+    """The box's plain streaming rates, a second denominator for the
+    roofline: torch's device copy (reads + writes) and sum (reads) of 1 GiB."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    src.sum()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    reps = 10
+    e[0].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e[1].record()
+    for _ in range(reps):
+        src.sum()
+    e[2].record()
+    torch.cuda.synchronize()
+    copy_s = e[0].elapsed_time(e[1]) * 1e-3 / reps
+    sum_s = e[1].elapsed_time(e[2]) * 1e-3 / reps
+    del src, dst
+    return {"copy_GBps": round(2 * 4 * n / copy_s / 1e9, 1), "read_GBps": round(4 * n / sum_s / 1e9, 1),
+            "bytes": 4 * n}
 
 
 def setup(args, extra_steps):
@@ -344,9 +420,166 @@ def setup(args, extra_steps):
         sel = torch.empty((wl.batch, wl.num_q_heads, max(1, wl.top_k)), dtype=torch.int32, device="cuda")
         caches.append(dc)
         qs.append(q)
-        preps.append(PreparedDecodeStep(dc, q, k_tok, v_tok, out, sel))
+        preps.append(PreparedDecodeStep(dc, q, k_tok, v_tok, out, sel, fused=not args.separate_append))
     print(f"[bench] {R} caches built; build {np.mean(build_ms) * 1e3:.1f} us each", file=sys.stderr, flush=True)
     return dict(wl=wl, inp=inp, caches=caches, preps=preps, qs=qs, build_ms=build_ms, hip=hip, stream=stream, R=R)
+
+
+def hybrid_main(args):
+    """Build + 32-layer hybrid decode at 32768 tokens, batch 1: every layer
+    has its own cache, budget and linear-tail switch; a step is one append +
+    decode per layer.  Timed eagerly and as a captured HIP graph of two
+    steps (the lengths ping-pong, so two steps bring the pointers back)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+
+    import workloads as W
+    from hybrid_sparse_linear_block_amd import hsla_profile
+    from hybrid_sparse_linear_block_amd.device import DeviceCache, PreparedDecodeStep, config_for, to_device
+
+    steps, warm = max(2, args.steps - args.steps % 2), args.warmup
+    layers = W.hybrid_layers()
+    appends = warm + 3 * steps + 4
+    room = 1 + -(-appends // layers[0].block_size)
+    layers = [W.dataclasses.replace(wl, append_room=room) for wl in layers]
+    cap = max(layers[0].seq_lens) + appends + 1
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(8) as ex:
+        futs = [ex.submit(W.make_inputs, wl, 0, False) for wl in layers]
+        hip, stream = Hip(), torch.cuda.current_stream().cuda_stream
+        dcs, preps, build_ms, spot = [], [], [], None
+        for wl, f in zip(layers, futs):
+            inp = f.result()
+            cfg = config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k,
+                             wl.num_sink, wl.window, wl.linear_tail, wl.kv_dtype,
+                             deterministic=int(args.deterministic))
+            dc = DeviceCache(cfg, inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"],
+                             capacity_len=cap)
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            dc.build()
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            build_ms.append(hip.ms(e0, e1))
+            q = to_device(inp["q"])
+            if spot is None:   # layer 0 at its prefilled length, for the oracle spot check
+                o, sl = dc.decode(q)
+                torch.cuda.synchronize()
+                spot = (wl, inp["q"], o.cpu().numpy(), sl.cpu().numpy())
+            k_tok, v_tok = (to_device(x) for x in W.gen_token(wl, 0))
+            out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+            sel = torch.empty((wl.batch, wl.num_q_heads, wl.top_k), dtype=torch.int32, device="cuda")
+            dcs.append(dc)
+            preps.append(PreparedDecodeStep(dc, q, k_tok, v_tok, out, sel, fused=not args.separate_append))
+            del inp
+    print(f"[bench] {len(layers)} layers generated and built in {time.perf_counter() - t0:.1f}s; "
+          f"build {np.mean(build_ms) * 1e3:.1f} us per layer", file=sys.stderr, flush=True)
+
+    def step():
+        for p in preps:
+            p()
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    eager_s = (time.perf_counter() - t0) / steps
+
+    # per-kernel event intervals, summed over the layers
+    nev = 8
+    evs = []
+    for _ in preps:
+        pr = hsla_profile()
+        pr.capacity = nev
+        ev = [hip.event(no_fence=True) for _ in range(nev)]
+        for j in range(nev):
+            pr.events[j] = ev[j]
+        evs.append((pr, ev, hip.event(no_fence=True), hip.event(no_fence=True)))
+    sums = {}
+    for _ in range(steps):
+        for p, (pr, ev, a0, a1) in zip(preps, evs):
+            hip.record(a0, stream)
+            p(pr, between=lambda e=a1: hip.record(e, stream))
+        torch.cuda.synchronize()
+        for pr, ev, a0, a1 in evs:
+            names = [pr.names[j].decode() for j in range(pr.recorded - 1)]
+            for j, n in enumerate(names):
+                sums[n] = sums.get(n, 0.0) + hip.ms(ev[j], ev[j + 1]) * 1e3
+            if args.separate_append:
+                sums["append"] = sums.get("append", 0.0) + hip.ms(a0, a1) * 1e3
+    per_kernel = {k: v / steps for k, v in sums.items()}
+
+    # HIP graph of two steps, replayed with the lengths as upper bound
+    gs = torch.cuda.Stream()
+    for p in preps:
+        p.bound, p.stream = cap, gs.cuda_stream
+    saved = [(dc.cur, dc.host_lens.copy()) for dc in dcs]
+    graph = torch.cuda.CUDAGraph()
+    gs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=gs):
+        step()
+        step()
+    for dc, (cur, lens) in zip(dcs, saved):
+        dc.cur, dc.host_lens[:] = cur, lens
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps // 2):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_s = (time.perf_counter() - t0) / steps
+    for dc in dcs:
+        dc.host_lens += steps + 2
+
+    sels = [p.keep[4].cpu().numpy() for p in preps]
+    lens = [dc.host_lens for dc in dcs]
+    by = [step_bytes(wl, ln, sl) for wl, ln, sl in zip(layers, lens, sels)]
+    tot = {k: float(sum(d[k] for d in by)) for k in by[0]}
+    app_b = sum(append_bytes(wl) for wl in layers)
+    attend_us = per_kernel["attend"]
+    value = 1.0 / graph_s
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warm, "ms_per_step": round(graph_s * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "accumulate": "f32", "data": "synthetic",
+        "config": {"workload": "hybrid32_32k", "layers": len(layers), "batch": 1, "ctx": int(max(layers[0].seq_lens)),
+                   "q_heads": 32, "kv_heads": 8, "head_dim": 128, "block": 64,
+                   "top_k": [wl.top_k for wl in layers], "linear_tail": [wl.linear_tail for wl in layers],
+                   "sinks": 4, "window": 512, "attention_split": "fixed" if args.deterministic else "dynamic",
+                   "step": (STEP_SEPARATE if args.separate_append else STEP_FUSED) + " per layer",
+                   "launch": "hip_graph"},
+        "us_per_step": round(graph_s * 1e6, 2),
+        "us_per_step_eager": round(eager_s * 1e6, 2),
+        "kernels_us_sum_over_layers": {k: round(v, 2) for k, v in per_kernel.items()},
+        "roofline": {"bound": "hbm", "kernel": "k_attend", "achieved": round(tot["attend"] / (attend_us * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(tot["attend"] / (attend_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(tot["attend"] / len(layers)), "us_per_launch": round(attend_us / len(layers), 2)},
+        "step_roofline": {"bytes": int(tot["decode"] + app_b), "achieved": round((tot["decode"] + app_b) / graph_s / 1e9, 1),
+                          "frac": round((tot["decode"] + app_b) / graph_s / 1e9 / HBM_PEAK_GBS, 4), "unit": "GB/s"},
+        "bytes_split": {k: int(v) for k, v in tot.items()},
+        "build": {"us_per_layer": round(float(np.mean(build_ms)) * 1e3, 1),
+                  "bytes_per_layer": int(8 * (32768 * 128 * 2 * 2 + (128 ** 2 + 2 * 128) * 4 + 512 * 2 * 128 * 4)),
+                  "flop_per_layer": int(8 * 2 * 32768 * 128 ** 2)},
+    }
+    b = res["build"]
+    b["GB/s"] = round(b["bytes_per_layer"] / (b["us_per_layer"] * 1e-6) / 1e9, 1)
+    b["TFLOP/s"] = round(b["flop_per_layer"] / (b["us_per_layer"] * 1e-6) / 1e12, 1)
+    if not args.no_cpu_baseline:
+        wl0, q0, o0, s0 = spot
+        cb, worst = cpu_baseline(wl0, q0, o0, s0, args.cpu_seconds)
+        # one layer's decode timed; the step is 32 layers (budgets differ, so this is an estimate)
+        cb["value"] = cb["value"] / len(layers)
+        cb["sample"] += f"; layer 0 only (top_k {wl0.top_k}), scaled to {len(layers)} layers"
+        if cb.get("single_thread_value"):
+            cb["single_thread_value"] = round(cb["single_thread_value"] / len(layers), 3)
+        res["cpu_baseline"] = cb
+        res["spot_check_max_row_err"] = float(f"{worst:.3e}")
+    print(json.dumps(res))
 
 
 def main():
@@ -366,6 +599,9 @@ def main():
     from hybrid_sparse_linear_block_amd import hsla_profile
 
     torch.cuda.set_device(0)
+    if args.workload == "hybrid32_32k":
+        hybrid_main(args)
+        return
     if args.traffic_run:
         traffic_run(args)
         return
@@ -396,7 +632,8 @@ def main():
     # (events without the system-scope fence, so the kernels run as in the
     # timed loop); reported separately, never folded into `value`.
     # hsla_profile records an event before each decode kernel and one after
-    # the last; the append call is bracketed by two events of its own.  An
+    # the last; with --separate-append the append call is bracketed by two
+    # events of its own.  An
     # interval between events includes the dispatch of its kernel, so it
     # reads a few percent above the kernel's own duration in rocprofv3.
     nev = 8
@@ -418,7 +655,8 @@ def main():
     names = [profs[0].names[j].decode() for j in range(nrec - 1)]
     per_kernel = {n: float(np.mean([hip.ms(evs[i][j], evs[i][j + 1]) for i in range(steps)]) * 1e3)
                   for j, n in enumerate(names)}
-    per_kernel["append"] = float(np.mean([hip.ms(ev_app[i][0], ev_app[i][1]) for i in range(steps)]) * 1e3)
+    if args.separate_append:
+        per_kernel["append"] = float(np.mean([hip.ms(ev_app[i][0], ev_app[i][1]) for i in range(steps)]) * 1e3)
     gpu_step_us = float(np.mean([hip.ms(ev_app[i][0], evs[i][nrec - 1]) for i in range(steps)]) * 1e3)
 
     # Algorithmic bytes from each replica's selections at its final length.
@@ -429,6 +667,17 @@ def main():
         per_rep.append(step_bytes(wl, caches[r].host_lens, s.cpu().numpy()))
     avg = {k: float(np.mean([d[k] for d in per_rep])) for k in per_rep[0]}
     app_b = append_bytes(wl)
+
+    # Warm decode: replica 0 decoded again and again with the same inputs,
+    # so its working set stays in the 256 MB Infinity Cache (MALL); the
+    # timed loop above rotates over R replicas and runs cold.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        preps[0].decode_only()
+    torch.cuda.synchronize()
+    decode_warm_us = (time.perf_counter() - t0) / steps * 1e6
+    mem = memory_probe()
 
     attend_us = per_kernel["attend"]
     ms_per_step = wall / steps * 1e3
@@ -447,7 +696,8 @@ def main():
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block": wl.block_size,
                    "top_k": wl.top_k, "sinks": wl.num_sink, "window": wl.window, "replicas": R,
                    "selection": "grouped" if wl.grouped else "per_head",
-                   "attention_split": "fixed" if args.deterministic else "dynamic", "step": "append + decode"},
+                   "attention_split": "fixed" if args.deterministic else "dynamic",
+                   "step": STEP_SEPARATE if args.separate_append else STEP_FUSED},
         "us_per_step": round(ms_per_step * 1e3, 2),
         "gpu_us_per_step": round(gpu_step_us, 2),
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
@@ -456,6 +706,8 @@ def main():
                           "frac": round(step_bytes_total / (gpu_step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                           "unit": "GB/s"},
         "bytes_split": {k: int(v) for k, v in avg.items()},
+        "decode_only_us_warm": round(decode_warm_us, 2),
+        "memory_probe": mem,
         "build": {"us": round(float(np.mean(build_ms)) * 1e3, 1),
                   "bytes": int(wl.batch * wl.num_kv_heads * (max(wl.seq_lens) * wl.head_dim * 2 * wl.elem_bytes
                                                               + (wl.head_dim ** 2 + 2 * wl.head_dim) * 4

@@ -29,7 +29,7 @@ HSLA_SEL_GROUPED = 1
 HSLA_MAX_PROFILE_EVENTS = 8
 
 EXPORTED = ("hsla_status_string", "hsla_version", "hsla_build_workspace_size", "hsla_build_state",
-            "hsla_append_token", "hsla_decode_workspace_size", "hsla_decode")
+            "hsla_append_token", "hsla_decode_workspace_size", "hsla_decode", "hsla_append_decode")
 
 
 class hsla_config(ctypes.Structure):
@@ -82,7 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     except ImportError:
         pass
     if not os.path.exists(path):
-        raise ImportError(f"{path} is missing: build it with `python -m hybrid_sparse_linear_block_amd.build`")
+        raise ImportError(f"{path} is missing: build it with `python hybrid_sparse_linear_block_amd/build.py`")
     lib = ctypes.CDLL(path)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     P = ctypes.POINTER
@@ -101,6 +101,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsla_decode.argtypes = [P(hsla_config), P(hsla_kv_pool), P(hsla_state), vp, vp, i32, i32, vp, vp, vp,
                                 sz, vp, P(hsla_profile)]
     lib.hsla_decode.restype = ctypes.c_int
+    lib.hsla_append_decode.argtypes = [P(hsla_config), P(hsla_kv_pool), P(hsla_state), vp, vp, vp, vp, vp, i32,
+                                       i32, vp, vp, vp, sz, vp, P(hsla_profile)]
+    lib.hsla_append_decode.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -218,6 +221,17 @@ def hsla_decode(cfg: Config, pool: Pool, state: Optional[State], q, seq_lens, ba
         ctypes.byref(cfg.c()), ctypes.byref(pool.c()), st, _ptr(q), _ptr(seq_lens), batch, max_seq_len,
         _ptr(out), _ptr(sel_idx), _ptr(workspace), nbytes, _stream(stream),
         ctypes.byref(prof) if prof is not None else None))
+
+
+
+def hsla_append_decode(cfg: Config, pool: Pool, state: State, k_new, v_new, seq_lens_before, seq_lens_after, q,
+                       batch: int, max_seq_len: int, out, sel_idx, workspace, workspace_bytes: Optional[int] = None,
+                       stream=None, prof: Optional[hsla_profile] = None) -> None:
+    nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check("hsla_append_decode", load().hsla_append_decode(
+        ctypes.byref(cfg.c()), ctypes.byref(pool.c()), ctypes.byref(state.c()), _ptr(k_new), _ptr(v_new),
+        _ptr(seq_lens_before), _ptr(seq_lens_after), _ptr(q), batch, max_seq_len, _ptr(out), _ptr(sel_idx),
+        _ptr(workspace), nbytes, _stream(stream), ctypes.byref(prof) if prof is not None else None))
 
 
 load()

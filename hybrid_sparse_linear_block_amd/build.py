@@ -1,6 +1,9 @@
 """Build libhsla.so for gfx950 with hipcc (in-tree, next to this file).
 
-    python -m hybrid_sparse_linear_block_amd.build
+    python hybrid_sparse_linear_block_amd/build.py
+
+(run by path: importing the package first would load the library that is
+being rebuilt).
 """
 from __future__ import annotations
 

@@ -1,0 +1,177 @@
+// Pieces of the token append ("SPLA: Block Sparse Plus Linear Attention for
+// Long Context Modeling", section "Recurrence") shared by the stand-alone
+// append kernel and the decode kernel that takes the append in with its
+// state readout: element access in either storage format, and the
+// statistics of a block the new token completes.
+#pragma once
+
+#include "common.h"
+
+namespace hsla {
+
+template <typename KV>
+__device__ __forceinline__ float kv_elem(const void* p, size_t i) {
+  if constexpr (KV::kBytes == 2) {
+    return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(p)[i]) << 16);
+  } else {
+    return reinterpret_cast<const float*>(p)[i];
+  }
+}
+
+template <typename KV>
+__device__ __forceinline__ void kv_put(void* p, size_t i, const void* src, size_t j) {
+  if constexpr (KV::kBytes == 2) {
+    reinterpret_cast<uint16_t*>(p)[i] = reinterpret_cast<const uint16_t*>(src)[j];
+  } else {
+    reinterpret_cast<float*>(p)[i] = reinterpret_cast<const float*>(src)[j];
+  }
+}
+
+// Four consecutive elements widened to fp32.
+template <typename KV>
+__device__ __forceinline__ float4 kv_load4(const void* p, size_t i) {
+  if constexpr (KV::kBytes == 2) {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + i);
+    return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+  } else {
+    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+  }
+}
+
+// LDS of filled_block_stats for NT threads and head dim D.
+template <int NT, int D>
+struct BlockStatsLds {
+  float part[NT / (D / 8) * D];
+  float mean[D];
+};
+
+// Statistics of the block the new token fills (SPLA, section "Method": the
+// mean and the per-channel variance of the block's keys): rows [0, B) of
+// the page-head tile at row0 of k_pages, row `last` taken from k_new at
+// nbase (its page write may not have landed).  NT threads = D/8 channel
+// groups x (NT / (D/8)) row groups; each thread loads its rows as
+// 8-channel vectors, four rows in flight, and the partial sums meet in LDS.
+// The second pass re-reads the rows (cache hits) for the squared deviations
+// from the mean.  Every thread of the workgroup must call it.
+template <typename KV, int D, int NT>
+__device__ void filled_block_stats(const void* k_pages, const void* k_new, size_t row0, int last, size_t nbase,
+                                   int B, float* mean_out, float* var_out, BlockStatsLds<NT, D>& s) {
+  constexpr int CG = D / 8;      // channel groups of 8
+  constexpr int RG = NT / CG;    // row groups
+  const int tid = threadIdx.x;
+  const int cg = tid % CG;
+  const int rg = tid / CG;
+  auto load_row = [&](int r, float (&x)[8]) __attribute__((always_inline)) {
+    Row8<KV> row;
+    if (r == last)
+      row.load(reinterpret_cast<const char*>(k_new) + (nbase + cg * 8) * KV::kBytes);
+    else
+      row.load(reinterpret_cast<const char*>(k_pages) + ((row0 + r) * D + cg * 8) * KV::kBytes);
+    row.to_f32(x);
+  };
+  auto pass = [&](bool second) __attribute__((always_inline)) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float mu[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mu[j] = second ? s.mean[cg * 8 + j] : 0.f;
+    for (int r0 = rg; r0 < B; r0 += 4 * RG) {
+      float x[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load_row(min(r0 + u * RG, B - 1), x[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = r0 + u * RG < B ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float dl = x[u][j] - mu[j];
+          acc[j] = fmaf(w, second ? dl * dl : x[u][j], acc[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s.part[rg * D + cg * 8 + j] = acc[j];
+    __syncthreads();
+    float t = 0.f;
+    if (tid < D)
+      for (int r = 0; r < RG; ++r) t += s.part[r * D + tid];
+    return t;
+  };
+  const float sum = pass(false);
+  if (tid < D) s.mean[tid] = sum / static_cast<float>(B);
+  __syncthreads();
+  const float m2 = pass(true);
+  if (tid < D) {
+    mean_out[tid] = s.mean[tid];
+    var_out[tid] = m2 / static_cast<float>(B);
+  }
+}
+
+// The block a new token completes: rows [0, B) of the page-head tiles at
+// row0 of the key and value pages, row `last` (the new token) read from
+// k_new / v_new at nbase instead, since its page write may not have landed.
+struct CompletedBlock {
+  const void* k_pages;
+  const void* v_pages;
+  const void* k_new;
+  const void* v_new;
+  size_t row0;
+  size_t nbase;
+  int last;
+  int B;
+};
+
+template <typename KV, int D>
+__device__ __forceinline__ const char* block_row(const void* pages, const void* nw, const CompletedBlock& cb, int j) {
+  return j == cb.last ? reinterpret_cast<const char*>(nw) + cb.nbase * KV::kBytes
+                      : reinterpret_cast<const char*>(pages) + (cb.row0 + j) * D * KV::kBytes;
+}
+
+// The linear state takes a block's tokens when the block completes (tokens
+// of the incomplete last block always lie inside the window, so they are
+// exact and never enter the linear part): rows r_first + RG i (i < NR),
+// columns 4 col4 .. 4 col4 + 3 of S gain sum_j k_j[r] v_j[c] over the
+// block's rows, summed in row order and added once.
+template <typename KV, int D, int NR, int RG>
+__device__ __forceinline__ void fold_block_rows(float4 (&srow)[NR], const CompletedBlock& cb, int r_first, int col4) {
+  float4 acc[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < cb.B; j0 += 4) {   // B is a multiple of 4
+    float4 v[4];
+    float kr[4][NR];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = kv_load4<KV>(block_row<KV, D>(cb.v_pages, cb.v_new, cb, j0 + u), col4 * 4);
+      const char* krow = block_row<KV, D>(cb.k_pages, cb.k_new, cb, j0 + u);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) kr[u][i] = kv_elem<KV>(krow, r_first + i * RG);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        acc[i].x = fmaf(kr[u][i], v[u].x, acc[i].x);
+        acc[i].y = fmaf(kr[u][i], v[u].y, acc[i].y);
+        acc[i].z = fmaf(kr[u][i], v[u].z, acc[i].z);
+        acc[i].w = fmaf(kr[u][i], v[u].w, acc[i].w);
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    srow[i].x += acc[i].x;
+    srow[i].y += acc[i].y;
+    srow[i].z += acc[i].z;
+    srow[i].w += acc[i].w;
+  }
+}
+
+// Channel c summed over the completed block's rows (z for keys, sv for
+// values), in row order.
+template <typename KV, int D>
+__device__ __forceinline__ float fold_block_channel(const void* pages, const void* nw, const CompletedBlock& cb, int c) {
+  float acc = 0.f;
+  for (int j = 0; j < cb.B; ++j) acc += kv_elem<KV>(block_row<KV, D>(pages, nw, cb, j), c);
+  return acc;
+}
+
+}  // namespace hsla

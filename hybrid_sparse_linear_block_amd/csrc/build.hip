@@ -2,7 +2,8 @@
 // ("SPLA: Block Sparse Plus Linear Attention for Long Context Modeling",
 // TL;DR / Abstract: selection from block statistics, residual linear
 // attention from a compact state; "SLAKE ..." abstract: first-order Taylor
-// kernel, whose state is S = sum_t k_t v_t^T, z = sum_t k_t, sv = sum_t v_t).
+// kernel, whose state is S = sum_t k_t v_t^T, z = sum_t k_t, sv = sum_t v_t,
+// here over the tokens of complete blocks).
 //
 // k_build_*: one workgroup per (sequence, kv head, chunk of tokens).  Tiles of
 // the chunk are staged in LDS; the workgroup writes the statistics of every
@@ -44,6 +45,7 @@ struct BuildParams {
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ int clamp_len(int T, int max_len) { return min(max(T, 0), max_len); }
+__device__ __forceinline__ int full_blocks_len(int T, int B) { return T - T % B; }
 
 // ---------------------------------------------------------------------------
 // bf16: MFMA
@@ -83,7 +85,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_build_bf16(BuildParams P) {
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
   const int chunk = blockIdx.x;
-  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
+  // the state holds the tokens of complete blocks; the incomplete last
+  // block's tokens lie inside the window and are attended exactly
+  const int T = full_blocks_len(clamp_len(P.seq_lens[b], P.max_seq_len), P.B);
   const int c_begin = chunk * P.chunk;
   const int c_end = min(c_begin + P.chunk, T);
   if (c_begin >= c_end) {
@@ -305,7 +309,9 @@ __global__ __launch_bounds__(kThreads) void k_build_f32(BuildParams P) {
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
   const int chunk = blockIdx.x;
-  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
+  // the state holds the tokens of complete blocks; the incomplete last
+  // block's tokens lie inside the window and are attended exactly
+  const int T = full_blocks_len(clamp_len(P.seq_lens[b], P.max_seq_len), P.B);
   const int c_begin = chunk * P.chunk;
   const int c_end = min(c_begin + P.chunk, T);
   const int tid = threadIdx.x;

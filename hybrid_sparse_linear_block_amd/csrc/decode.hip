@@ -30,7 +30,7 @@
 #include <type_traits>
 #include <utility>
 
-#include "common.h"
+#include "append_parts.h"
 #include "internal.h"
 
 namespace hsla {
@@ -54,6 +54,22 @@ constexpr int kMaxDynList = 2048;    // union entries a dynamic attention workgr
 constexpr int kDeadT0 = 1 << 30;     // first token of a slice whose rows are all invalid
 constexpr int kFusedKplMax = 16;     // keys per lane of the selection fused into the attention prologue: 8 or 16
 constexpr size_t kBtStageBytes = 8 * 1024;      // block-table row staged in LDS up to this size
+
+// The token append taken in by the scoring / readout kernel
+// (hsla_append_decode); k_new == nullptr: none.
+struct DecodeAppend {
+  void* k_pages;
+  void* v_pages;
+  float* blk_mean;
+  float* blk_var;
+  float* S;
+  float* z;
+  float* sv;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* lens_before;
+  int32_t* lens_after;
+};
 
 struct DecodeParams {
   const void* k_pages;
@@ -83,10 +99,22 @@ struct DecodeParams {
   int dyn;          // attention workgroups of a pair claim its slices dynamically
   int fused_sel;    // per-head selection inside the attention prologue (no selection kernel)
   SelLayout sl;
+  DecodeAppend app;
   float sigma;
 };
 
 __device__ __forceinline__ int clamp_len(int T, int max_len) { return min(max(T, 1), max_len); }
+
+// Position of the appended token (the append's own clamp).
+__device__ __forceinline__ int append_pos(const DecodeParams& P, int b) {
+  return min(max(P.app.lens_before[b], 0), P.max_seq_len - 1);
+}
+
+// Length of sequence b in the first decode kernel: with the append taken in,
+// seq_lens is written by that same kernel, so the length comes from before.
+__device__ __forceinline__ int first_kernel_len(const DecodeParams& P, int b) {
+  return P.app.k_new ? append_pos(P, b) + 1 : clamp_len(P.seq_lens[b], P.max_seq_len);
+}
 
 // Query of one head, 8 channels per lane.
 template <typename KV>
@@ -165,7 +193,7 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
   int page[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) page[it] = bt[lo + min(c_begin + slot + it * CPP, P.nc_max - 1)];
-  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
+  const int T = first_kernel_len(P, b);
   const int nc = min(candidate_range(T, P.B, P.ns, P.W).count, P.nc_max);
   if (c_begin >= nc) return;
 #pragma unroll
@@ -220,6 +248,14 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
   }
 }
 
+// Rows [rc*32, rc*32 + 32) of the state readout: partial S^T q and q . z
+// of the pair's G heads (SPLA, section "Method": the linear part reads the
+// global state).  With the append taken in, row chunk 0 writes the new
+// token's page slot and length, and when the token completes its block
+// every chunk first adds the block to its rows of S and z (chunk 0 to sv,
+// the last chunk computes the block's statistics) and writes them back, so
+// that the readout sees the state the stand-alone append would leave.
+// Without the linear tail only the append's part runs.
 template <typename KV, int D, int G>
 __device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g, int rc) {
   constexpr int C4 = D / 4;            // float4 columns per row
@@ -227,23 +263,78 @@ __device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g
   constexpr int NR = kRoRows / RG;     // rows per thread
   static_assert(kRoRows % RG == 0, "rows per readout workgroup");
   __shared__ float red[kThreads / kWave][C4][G][4];
+  __shared__ float zs[kRoRows];
   const int tid = threadIdx.x;
   const int col4 = tid % C4;
   const int rg = tid / C4;
   const int pair = b * P.Hkv + g;
   const int r0 = rc * kRoRows;
-  const float* Sp = P.S + static_cast<size_t>(pair) * D * D;
+  const bool app = P.app.k_new != nullptr;
+  const bool lin = P.linear_tail != 0;
   const size_t qbase = (static_cast<size_t>(b) * P.Hq + g * G) * D;
+  const size_t nbase = static_cast<size_t>(pair) * D;   // k_new / v_new row of the pair
 
+  const float* Sp = (app ? P.app.S : P.S) + static_cast<size_t>(pair) * D * D;
+  const float* zp = (app ? P.app.z : P.z) + nbase + r0;
   float4 srow[NR];
   float qv[NR][G];
+  float zr = 0.f;
+  auto load_rows = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int r = r0 + rg + i * RG;
-    srow[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(r) * D + col4 * 4);
+    for (int i = 0; i < NR; ++i)
+      srow[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(r0 + rg + i * RG) * D + col4 * 4);
+    if (tid < kRoRows) zr = zp[tid];
+  };
+  // The readout's loads go first; the append's position and page take two
+  // dependent round trips behind them.
+  if (lin) {
+    load_rows();
 #pragma unroll
-    for (int h = 0; h < G; ++h) qv[i][h] = q_elem<KV>(P.q, qbase + static_cast<size_t>(h) * D + r);
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) qv[i][h] = q_elem<KV>(P.q, qbase + static_cast<size_t>(h) * D + r0 + rg + i * RG);
   }
+  int T = 0;
+  size_t row0 = 0, page = 0;
+  bool completes = false;
+  if (app) {
+    T = append_pos(P, b);
+    page = static_cast<size_t>(P.block_table[static_cast<size_t>(b) * P.max_blocks + T / P.B]);
+    row0 = (page * P.Hkv + g) * P.B;   // first row of the page-head tile
+    completes = (T + 1) % P.B == 0;    // uniform
+    if (rc == 0) {
+      if (tid < D) {
+        kv_put<KV>(P.app.k_pages, (row0 + T % P.B) * D + tid, P.app.k_new, nbase + tid);
+        kv_put<KV>(P.app.v_pages, (row0 + T % P.B) * D + tid, P.app.v_new, nbase + tid);
+      }
+      if (g == 0 && tid == 0 && P.app.lens_after) P.app.lens_after[b] = T + 1;
+    }
+  }
+  if (!lin) {
+    if (!completes) return;
+    load_rows();
+  }
+  if (completes) {
+    const CompletedBlock cb{P.app.k_pages, P.app.v_pages, P.app.k_new, P.app.v_new, row0, nbase, T % P.B, P.B};
+    fold_block_rows<KV, D, NR, RG>(srow, cb, r0 + rg, col4);
+    float* Sw = P.app.S + static_cast<size_t>(pair) * D * D;
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      *reinterpret_cast<float4*>(Sw + static_cast<size_t>(r0 + rg + i * RG) * D + col4 * 4) = srow[i];
+    if (tid < kRoRows) {
+      zr += fold_block_channel<KV, D>(P.app.k_pages, P.app.k_new, cb, r0 + tid);
+      P.app.z[nbase + r0 + tid] = zr;
+    }
+    if (rc == 0 && tid < D) P.app.sv[nbase + tid] += fold_block_channel<KV, D>(P.app.v_pages, P.app.v_new, cb, tid);
+    if (rc == D / kRoRows - 1) {
+      __shared__ BlockStatsLds<kThreads, D> lds;
+      const size_t so = (page * P.Hkv + g) * D;
+      filled_block_stats<KV, D, kThreads>(P.app.k_pages, P.app.k_new, row0, T % P.B, nbase, P.B,
+                                          P.app.blk_mean + so, P.app.blk_var + so, lds);
+    }
+  }
+  if (!lin) return;
+  if (tid < kRoRows) zs[tid] = zr;
   float acc[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -284,16 +375,12 @@ __device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g
   }
   if (tid < G) {
     const int h = tid;
-    const float* zp = P.z + static_cast<size_t>(pair) * D + r0;
-    float zr[kRoRows], qr[kRoRows];
+    float qr[kRoRows];
 #pragma unroll
-    for (int r = 0; r < kRoRows; ++r) {
-      zr[r] = zp[r];
-      qr[r] = q_elem<KV>(P.q, qbase + static_cast<size_t>(h) * D + r0 + r);
-    }
+    for (int r = 0; r < kRoRows; ++r) qr[r] = q_elem<KV>(P.q, qbase + static_cast<size_t>(h) * D + r0 + r);
     float v = 0.f;
 #pragma unroll
-    for (int r = 0; r < kRoRows; ++r) v = fmaf(qr[r], zr[r], v);
+    for (int r = 0; r < kRoRows; ++r) v = fmaf(qr[r], zs[r], v);
     P.roz[(static_cast<size_t>(pair) * P.ro_wgs + rc) * G + h] = v;
   }
 }
@@ -950,6 +1037,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
   static_assert(kUnit == kWave, "softmax pass maps one row to one lane");
   __shared__ float s_lds[G][kUnit];
   __shared__ float2 pw_lds[G][kUnit];
+  __shared__ bool lin_lds[kUnit];
   __shared__ float scale_lds[G];
   __shared__ float red[NW][G][2 * D];
   __shared__ float mll[G][4];
@@ -971,6 +1059,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
   const SplitShare share = union_share<G, false, kFusedKplMax>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split,
                                                                [] {}, [](int, int, const int32_t*) {});
   const int T = share.T;
+  const int Ts = T - T % P.B;   // tokens the linear state holds
   if (split >= share.count) return;
   const int ne = share.ne;
   const int my_ent = share.ent;
@@ -1095,6 +1184,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
         if (lig == 0) s_lds[h][grp + NGRP * i] = inc ? d : kNegInf;
       }
     }
+    // subtraction terms only for tokens the state holds (complete blocks)
+    if (lig == 0) {
+#pragma unroll
+      for (int i = 0; i < U; ++i) lin_lds[grp + NGRP * i] = valid[i] && x.tok[i] < Ts;
+    }
     __syncthreads();
     // ---- softmax pass: wavefront w owns heads w, w + NW, ...
 #pragma unroll
@@ -1106,7 +1200,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
       const float mnew = fmaxf(m_run[o], wave_max(sv));
       const float c = (m_run[o] == kNegInf) ? 0.f : (mnew == m_run[o] ? 1.f : fast_exp(m_run[o] - mnew));
       const float pv = inc ? fast_exp(sv - mnew) : 0.f;
-      const float wv = inc ? 1.f + sv : 0.f;
+      const float wv = (inc && lin_lds[lane]) ? 1.f + sv : 0.f;
       pw_lds[h][lane] = make_float2(pv, wv);
       l_lane[o] = fmaf(l_lane[o], c, pv);
       ld_lane[o] += wv;
@@ -1358,6 +1452,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   const SplitShare share =
       union_share<G, DYN, FK>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, stage_q, early);
   const int T = share.T;
+  const int Ts = T - T % P.B;           // tokens the linear state holds
   const int win0 = T - P.W;
   if (!DYN && split >= share.count) return;
   const int ne = share.ne;
@@ -1446,7 +1541,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
       for (int j = 0; j < 4; ++j) {
         const bool inc = sj[j] != kNegInf;
         const float pv = inc ? fast_exp(sj[j] - mh) : 0.f;
-        const float wv = inc ? 1.f + sj[j] : 0.f;
+        // subtraction terms only for tokens the state holds (complete blocks)
+        const float wv = (inc && x.t0 + 4 * q4 + j < Ts) ? 1.f + sj[j] : 0.f;
         float val = typ < 2 ? pv : wv;
         val = typ < 4 ? val : 0.f;
         rs += val;
@@ -1718,7 +1814,7 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
       rz += rz_p[rc];
     }
     const float num_u = svc + P.sigma * ro - lnum;
-    const float den_u = static_cast<float>(T) + P.sigma * rz - lden;
+    const float den_u = static_cast<float>(T - T % P.B) + P.sigma * rz - lden;   // n: tokens the state holds
     const float em = __expf(-M);
     num = fmaf(em, num_u, num);
     den = fmaf(em, den_u, den);
@@ -1731,9 +1827,12 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
                         hipStream_t stream, RecordFn rec, void* ctx) {
   const int pairs = p.batch * p.Hkv;
   int ev = 0;   // profiling events: one before each launched kernel, one after the last
-  if (rec) rec(ctx, ev++, "score_readout");
-  if (L.score_wgs + L.ro_wgs > 0) {   // neither candidates nor a linear tail: nothing to score or read out
-    dim3 grid(L.score_wgs + L.ro_wgs, pairs);
+  // with the append taken in, the row-chunk workgroups run whatever the
+  // linear tail (they apply the state update)
+  const int ro_launch = P.app.k_new ? D / kRoRows : L.ro_wgs;
+  if (rec) rec(ctx, ev++, P.app.k_new ? "append_score_readout" : "score_readout");
+  if (L.score_wgs + ro_launch > 0) {   // neither candidates nor a linear tail: nothing to score or read out
+    dim3 grid(L.score_wgs + ro_launch, pairs);
     hipLaunchKernelGGL((k_score_readout<KV, D, G>), grid, dim3(kThreads), 0, stream, P);
     hipError_t e = launch_status("k_score_readout");
     if (e != hipSuccess) return e;
@@ -1929,6 +2028,8 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.nwords = L.nwords;
   P.bt_staged = L.bt_staged;
   P.sl = L.sl;
+  P.app = DecodeAppend{a.app.k_pages, a.app.v_pages, a.app.blk_mean, a.app.blk_var, a.app.S, a.app.z, a.app.sv,
+                       a.app.k_new, a.app.v_new, a.app.seq_lens_before, a.app.seq_lens_after};
   P.umax = L.umax;
   P.bps = L.bps;
   P.max_split = L.max_split;

@@ -177,15 +177,20 @@ size_t hsla_decode_workspace_size(const hsla_config* cfg, int32_t batch, int32_t
   return hsla::decode_layout(p).total;
 }
 
-hsla_status hsla_decode(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
-                        const void* q, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
-                        float* out, int32_t* sel_idx, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, hsla_profile* prof) {
+}  // extern "C"
+
+namespace {
+
+// hsla_decode, with the token append taken in when `app` is given.
+hsla_status decode_impl(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state, const void* q,
+                        const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float* out, int32_t* sel_idx,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream, hsla_profile* prof,
+                        const hsla::AppendArgs* app) {
   Problem p;
   hsla_status st = resolve(cfg, batch, max_seq_len, pool ? pool->max_blocks_per_seq : 0, &p);
   if (st != HSLA_OK) return st;
   if ((st = check_pool(pool, true)) != HSLA_OK) return st;
-  if (p.linear_tail && (st = check_state(state)) != HSLA_OK) return st;
+  if ((p.linear_tail || app) && (st = check_state(state)) != HSLA_OK) return st;
   if (!q || !aligned(q, 16) || !out || !aligned(out, 16)) return HSLA_ERR_INVALID_ARG;
   if (!seq_lens || !aligned(seq_lens, 4)) return HSLA_ERR_INVALID_ARG;
   if (sel_idx && !aligned(sel_idx, 4)) return HSLA_ERR_INVALID_ARG;
@@ -206,12 +211,53 @@ hsla_status hsla_decode(const hsla_config* cfg, const hsla_kv_pool* pool, const 
   a.out = out;
   a.sel_idx = sel_idx;
   a.ws = static_cast<char*>(workspace);
+  if (app) a.app = *app;
   ProfileCtx ctx{prof, stream, false};
   if (prof) prof->recorded = 0;
   (void)hipGetLastError();
   const hipError_t e = hsla::launch_decode(p, L, a, stream, prof ? record_event : nullptr, &ctx);
   if (e != hipSuccess || ctx.failed) return HSLA_ERR_HIP;
   return HSLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hsla_status hsla_decode(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
+                        const void* q, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                        float* out, int32_t* sel_idx, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, hsla_profile* prof) {
+  return decode_impl(cfg, pool, state, q, seq_lens, batch, max_seq_len, out, sel_idx, workspace, workspace_bytes,
+                     stream, prof, nullptr);
+}
+
+hsla_status hsla_append_decode(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
+                               const void* k_new, const void* v_new, const int32_t* seq_lens_before,
+                               int32_t* seq_lens_after, const void* q, int32_t batch, int32_t max_seq_len,
+                               float* out, int32_t* sel_idx, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, hsla_profile* prof) {
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return HSLA_ERR_INVALID_ARG;
+  if (!seq_lens_before || !aligned(seq_lens_before, 4)) return HSLA_ERR_INVALID_ARG;
+  if (!seq_lens_after || !aligned(seq_lens_after, 4) || seq_lens_after == seq_lens_before)
+    return HSLA_ERR_INVALID_ARG;
+  if (!state) return HSLA_ERR_INVALID_ARG;
+  if (!pool) return HSLA_ERR_INVALID_ARG;
+  hsla::AppendArgs a{};
+  a.k_pages = pool->k_pages;
+  a.v_pages = pool->v_pages;
+  a.blk_mean = pool->blk_mean;
+  a.blk_var = pool->blk_var;
+  a.block_table = pool->block_table;
+  a.S = state->S;
+  a.z = state->z;
+  a.sv = state->sv;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.seq_lens_before = seq_lens_before;
+  a.seq_lens_after = seq_lens_after;
+  return decode_impl(cfg, pool, state, q, seq_lens_after, batch, max_seq_len, out, sel_idx, workspace,
+                     workspace_bytes, stream, prof, &a);
 }
 
 }  // extern "C"

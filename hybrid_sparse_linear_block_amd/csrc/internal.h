@@ -61,6 +61,24 @@ struct DecodeLayout {
 };
 DecodeLayout decode_layout(const Problem& p);
 
+// ---------------------------------------------------------------- append
+struct AppendArgs {
+  void* k_pages;
+  void* v_pages;
+  float* blk_mean;
+  float* blk_var;
+  const int32_t* block_table;
+  float* S;
+  float* z;
+  float* sv;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* seq_lens_before;
+  int32_t* seq_lens_after;
+};
+
+// A decode; app.k_new != nullptr: the token append is taken in by the first
+// kernel (hsla_append_decode), seq_lens is then app.seq_lens_after.
 struct DecodeArgs {
   const void* k_pages;
   const void* v_pages;
@@ -75,6 +93,7 @@ struct DecodeArgs {
   float* out;
   int32_t* sel_idx;
   char* ws;
+  AppendArgs app;
 };
 
 // Launches score+readout, select, attend, merge.  `record` is called with the
@@ -109,20 +128,6 @@ hipError_t launch_build(const Problem& p, const BuildLayout& L, const BuildArgs&
                         hipStream_t stream);
 
 // ---------------------------------------------------------------- append
-struct AppendArgs {
-  void* k_pages;
-  void* v_pages;
-  float* blk_mean;
-  float* blk_var;
-  const int32_t* block_table;
-  float* S;
-  float* z;
-  float* sv;
-  const void* k_new;
-  const void* v_new;
-  const int32_t* seq_lens_before;
-  int32_t* seq_lens_after;
-};
 hipError_t launch_append(const Problem& p, const AppendArgs& a, hipStream_t stream);
 
 }  // namespace hsla

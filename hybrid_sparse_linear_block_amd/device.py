@@ -11,8 +11,9 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (HSLA_BF16, HSLA_F32, HSLA_SEL_GROUPED, HSLA_SEL_PER_HEAD, Config, Pool, State, hsla_append_token, hsla_build_state,
-               hsla_build_workspace_size, hsla_decode, hsla_decode_workspace_size)
+from . import (HSLA_BF16, HSLA_F32, HSLA_SEL_GROUPED, HSLA_SEL_PER_HEAD, Config, Pool, State, hsla_append_decode,
+               hsla_append_token, hsla_build_state, hsla_build_workspace_size, hsla_decode,
+               hsla_decode_workspace_size)
 
 
 def to_device(x: np.ndarray, device="cuda") -> torch.Tensor:
@@ -83,6 +84,23 @@ class DeviceCache:
         self.cur = nxt
         self.host_lens += 1
 
+    def append_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                      out: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None, stream=None, prof=None):
+        """Append one token per (sequence, kv head), then decode at the grown
+        lengths, in one call."""
+        cfg = self.cfg
+        assert self.max_seq_len + 1 <= self.capacity_len, "no room mapped for the appended token"
+        if out is None:
+            out = torch.empty((self.batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=self.device)
+        if sel is None and cfg.top_k > 0:
+            sel = torch.empty((self.batch, cfg.num_q_heads, cfg.top_k), dtype=torch.int32, device=self.device)
+        nxt = 1 - self.cur
+        hsla_append_decode(cfg, self.pool, self.state, k_new, v_new, self.lens[self.cur], self.lens[nxt], q,
+                           self.batch, self.max_seq_len + 1, out, sel, self.decode_ws, stream=stream, prof=prof)
+        self.cur = nxt
+        self.host_lens += 1
+        return out, sel
+
     def decode(self, q: torch.Tensor, out: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None,
                want_sel: bool = True, stream=None, prof=None):
         cfg = self.cfg
@@ -106,10 +124,18 @@ class PreparedDecodeStep:
     """One decode step (append + decode) of a DeviceCache with every C
     argument marshalled once, so that repeated calls cost one ctypes call per
     entry point.  Lengths ping-pong between the cache's two length buffers;
-    each call advances the cache by one token."""
+    each call advances the cache by one token.
+
+    `fused` makes the step one hsla_append_decode call instead of
+    hsla_append_token + hsla_decode.
+
+    `bound`, if set, is passed as max_seq_len to both calls in place of the
+    current length: an upper bound that stays valid while the cache grows,
+    which a captured HIP graph needs since it replays its arguments as
+    captured.  `stream` (a HIP stream handle) may be changed between calls."""
 
     def __init__(self, dc: DeviceCache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
-                 out: torch.Tensor, sel: Optional[torch.Tensor], stream=None):
+                 out: torch.Tensor, sel: Optional[torch.Tensor], stream=None, fused: bool = False):
         import ctypes
 
         from . import hsla_profile, load
@@ -128,6 +154,8 @@ class PreparedDecodeStep:
         self.lens = [dc.lens[0].data_ptr(), dc.lens[1].data_ptr()]
         self.byref = ctypes.byref
         self.prof_type = hsla_profile
+        self.bound: Optional[int] = None
+        self.fused = fused
 
     def __call__(self, prof=None, between=None) -> None:
         """One step; `between`, if given, is called after the append was
@@ -136,8 +164,21 @@ class PreparedDecodeStep:
         assert dc.max_seq_len + 1 <= dc.capacity_len
         cur, nxt = dc.cur, 1 - dc.cur
         br = self.byref
+        bound = self.bound
+        if self.fused:
+            st = self.lib.hsla_append_decode(br(self.cfg), br(self.pool), br(self.state), self.k, self.v,
+                                             self.lens[cur], self.lens[nxt], self.q, dc.batch,
+                                             dc.max_seq_len + 1 if bound is None else bound, self.out, self.sel,
+                                             self.ws, self.ws_bytes, self.stream,
+                                             br(prof) if prof is not None else None)
+            if st != 0:
+                raise RuntimeError(f"hsla_append_decode failed: {st}")
+            dc.cur = nxt
+            dc.host_lens += 1
+            return
         st = self.lib.hsla_append_token(br(self.cfg), br(self.pool), br(self.state), self.k, self.v,
-                                        self.lens[cur], self.lens[nxt], dc.batch, dc.max_seq_len + 1, self.stream)
+                                        self.lens[cur], self.lens[nxt], dc.batch,
+                                        dc.max_seq_len + 1 if bound is None else bound, self.stream)
         if st != 0:
             raise RuntimeError(f"hsla_append_token failed: {st}")
         dc.cur = nxt
@@ -145,7 +186,18 @@ class PreparedDecodeStep:
         if between is not None:
             between()
         st = self.lib.hsla_decode(br(self.cfg), br(self.pool), br(self.state), self.q, self.lens[nxt], dc.batch,
-                                  dc.max_seq_len, self.out, self.sel, self.ws, self.ws_bytes, self.stream,
+                                  dc.max_seq_len if bound is None else bound, self.out, self.sel, self.ws,
+                                  self.ws_bytes, self.stream,
                                   br(prof) if prof is not None else None)
+        if st != 0:
+            raise RuntimeError(f"hsla_decode failed: {st}")
+
+    def decode_only(self) -> None:
+        """The decode of the current length, without an append (the cache
+        does not change)."""
+        dc = self.dc
+        st = self.lib.hsla_decode(self.byref(self.cfg), self.byref(self.pool), self.byref(self.state), self.q,
+                                  self.lens[dc.cur], dc.batch, dc.max_seq_len, self.out, self.sel, self.ws,
+                                  self.ws_bytes, self.stream, None)
         if st != 0:
             raise RuntimeError(f"hsla_decode failed: {st}")

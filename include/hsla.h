@@ -28,14 +28,18 @@
  *     averaged over the block) [SPLA, "Principled Block Selection ..."];
  *   - each query head keeps its top_k candidates by (score desc, index asc);
  *     exact set E = sinks U window U selected blocks, residual U = rest;
- *   - global linear state over all T tokens with phi(q).phi(k) = 1 + sigma q.k
- *     [SLAKE]: S = sum_t k_t v_t^T (d x d, S[i][j] = sum k_t,i v_t,j),
- *     z = sum k_t, sv = sum v_t, n = T;
+ *   - global linear state with phi(q).phi(k) = 1 + sigma q.k [SLAKE]:
+ *     S = sum_t k_t v_t^T (d x d, S[i][j] = sum k_t,i v_t,j), z = sum k_t,
+ *     sv = sum v_t, n = number of tokens summed, taken over the tokens of
+ *     complete blocks, t < Ts = T - T % B.  The incomplete last block lies
+ *     inside the window (window >= B), so its tokens are always exact and
+ *     never part of U; the state takes a block when it completes;
  *   - out = (sum_E e^{s_t} v_t + num_U) / (sum_E e^{s_t} + den_U), s_t =
- *     sigma q.k_t, with num_U = sv + sigma S^T q - sum_E (1+s_t) v_t and
- *     den_U = n + sigma q.z - sum_E (1+s_t) (global minus selected, so U is
- *     never read) [SPLA Abstract]; num_U = den_U = 0 when U is empty or the
- *     linear tail is off.
+ *     sigma q.k_t, with num_U = sv + sigma S^T q - sum_{E, t<Ts} (1+s_t) v_t
+ *     and den_U = n + sigma q.z - sum_{E, t<Ts} (1+s_t) (global minus
+ *     selected, so U is never read) [SPLA Abstract]; num_U = den_U = 0 when
+ *     U is empty or the linear tail is off.  This equals the sum over U of
+ *     the state built over all T tokens.
  *
  * Conventions for every entry point:
  *   - Memory: every pointer is a device pointer unless stated otherwise and
@@ -142,7 +146,8 @@ typedef struct hsla_kv_pool {
 
 /* Global linear state per (sequence, kv head) [SPLA, "Residual Linear
  * Attention (RLA)", "Recurrence"]: S [batch, Hkv, d, d], z and sv
- * [batch, Hkv, d], all float32.  n is the sequence length itself. */
+ * [batch, Hkv, d], all float32, over the tokens of the sequence's complete
+ * blocks; n = T - T % B follows from the length. */
 typedef struct hsla_state {
   float* S;
   float* z;
@@ -177,7 +182,7 @@ size_t hsla_build_workspace_size(const hsla_config* cfg, int32_t batch, int32_t 
  * seq_lens: device [batch] int32, T_b <= max_seq_len (host value, sizes the
  *   launch; >= 1).
  * Writes pool->blk_mean / blk_var for the pages of full blocks, and
- * state->S, z, sv for every (b, g).  The sums are reduced in a fixed order,
+ * state->S, z, sv for every (b, g) over the tokens of full blocks.  The sums are reduced in a fixed order,
  * so repeated builds are bitwise identical.
  * workspace: device scratch of at least hsla_build_workspace_size() bytes;
  *   contents on entry are ignored. */
@@ -193,8 +198,9 @@ hsla_status hsla_build_state(const hsla_config* cfg, const hsla_kv_pool* pool,
  *   which the caller must have mapped.  T_b + 1 <= max_seq_len.
  * seq_lens_after: device [batch] or NULL; receives T_b + 1.  Must not alias
  *   seq_lens_before.
- * Updates S += k v^T, z += k, sv += v and, when position T_b completes its
- * block, that block's statistics. */
+ * Writes the token's page slot.  When position T_b completes its block, the
+ * state takes the block (S += K_b^T V_b, z += sum k, sv += sum v over its B
+ * tokens) and the block's statistics are computed. */
 hsla_status hsla_append_token(const hsla_config* cfg, const hsla_kv_pool* pool,
                               const hsla_state* state, const void* k_new, const void* v_new,
                               const int32_t* seq_lens_before, int32_t* seq_lens_after,
@@ -222,6 +228,24 @@ hsla_status hsla_decode(const hsla_config* cfg, const hsla_kv_pool* pool, const 
                         const void* q, const int32_t* seq_lens, int32_t batch,
                         int32_t max_seq_len, float* out, int32_t* sel_idx, void* workspace,
                         size_t workspace_bytes, hipStream_t stream, hsla_profile* prof);
+
+/* The token append and the decode of the grown sequences in one call
+ * [SPLA, "Recurrence", Abstract, Figure 1]: the same results as
+ * hsla_append_token(k_new, v_new, seq_lens_before, seq_lens_after) followed by
+ * hsla_decode(seq_lens_after), with one launch fewer.  The first decode
+ * kernel applies the append (page slot, seq_lens_after and, when the token
+ * completes its block, the block into the state and its statistics) while
+ * it reads the state, so the state's rows are read once.  Arguments as in the two
+ * calls: the token goes to position T_b = seq_lens_before[b] (page mapped by
+ * the caller), the decode runs at T_b + 1 <= max_seq_len.  seq_lens_after is
+ * required and must not alias seq_lens_before; state is required whatever
+ * linear_tail says (the append maintains it).  Workspace as for hsla_decode
+ * (hsla_decode_workspace_size). */
+hsla_status hsla_append_decode(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
+                               const void* k_new, const void* v_new, const int32_t* seq_lens_before,
+                               int32_t* seq_lens_after, const void* q, int32_t batch, int32_t max_seq_len,
+                               float* out, int32_t* sel_idx, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, hsla_profile* prof);
 
 #ifdef __cplusplus
 }

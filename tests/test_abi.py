@@ -137,3 +137,33 @@ def test_build_rejects_small_workspace():
     c = cfg()
     assert lib.hsla_build_state(ctypes.byref(c.c()), ctypes.byref(pool()), ctypes.byref(state()), FAKE, 8, 32768,
                                 FAKE, 64, None) == H.HSLA_ERR_WORKSPACE
+
+
+def call_append_decode(c, p=None, st=None, k=FAKE, v=FAKE, before=FAKE, after=FAKE + 256, q=FAKE, batch=8,
+                       max_len=32768, out=FAKE, sel=FAKE, ws=FAKE, ws_bytes=1 << 40, null_state=False):
+    lib = H.load()
+    sp = None if null_state else ctypes.byref(st or state())
+    return lib.hsla_append_decode(ctypes.byref(c.c()), ctypes.byref(p or pool()), sp, k, v, before, after, q,
+                                  batch, max_len, out, sel, ws, ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("bad,code", BAD_CONFIGS)
+def test_append_decode_rejects_bad_configs(bad, code):
+    assert call_append_decode(cfg(**bad)) == code
+
+
+def test_append_decode_rejects_bad_pointers_and_sizes():
+    c = cfg()
+    E = H.HSLA_ERR_INVALID_ARG
+    assert call_append_decode(c, after=FAKE) == E          # aliases seq_lens_before
+    assert call_append_decode(c, after=0) == E             # the decode reads the grown lengths
+    assert call_append_decode(c, before=0) == E
+    assert call_append_decode(c, k=0) == E
+    assert call_append_decode(c, v=FAKE + 2) == E
+    assert call_append_decode(c, q=0) == E
+    assert call_append_decode(c, out=FAKE + 4) == E
+    assert call_append_decode(c, null_state=True) == E
+    # the append keeps the state whatever linear_tail says
+    assert call_append_decode(cfg(linear_tail=0), st=state(S=0)) == E
+    assert call_append_decode(c, p=pool(max_blocks_per_seq=100)) == E
+    assert call_append_decode(c, ws_bytes=16) == H.HSLA_ERR_WORKSPACE

@@ -84,9 +84,12 @@ def check_case(wl, inp, dc, out, sel, heads=None, check_build=True, pair_data=No
             nb = T // B
             pages = table[b, :nb]
             assert_stats_close(mean_g[pages, g], var_g[pages, g], stats[0], stats[1], Kf, B, f"pair {(b, g)}")
+            # the library's state holds the tokens of complete blocks
+            Ts = nb * B
             gs = O.LinearState(S_g[b, g].astype(np.float64), z_g[b, g].astype(np.float64),
-                               sv_g[b, g].astype(np.float64), T)
-            assert_state_close(gs, state, Kf, Vf, state_depth(T), f"pair {(b, g)}")
+                               sv_g[b, g].astype(np.float64), Ts)
+            assert_state_close(gs, O.global_state(Kf[:Ts], Vf[:Ts]), Kf[:Ts], Vf[:Ts], state_depth(Ts),
+                               f"pair {(b, g)}")
     worst, flips = 0.0, 0
     shared = {}   # grouped selection: (candidates, group weights, selection) per pair
     for b, h in heads:
@@ -301,10 +304,12 @@ def test_fixed_split_workloads(name):
     print(f"  worst row error {worst:.3e}, near-tie flips {flips}")
 
 
-@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
-def test_append_matches_rebuild(dtype):
+@pytest.mark.parametrize("dtype,fused", [(W.BF16, False), (W.F32, False), (W.BF16, True), (W.F32, True)])
+def test_append_matches_rebuild(dtype, fused):
     """Decode after N appends (crossing block boundaries) equals the oracle on
-    the full sequence, and the appended state matches a rebuild."""
+    the full sequence, and the appended state matches a rebuild.  `fused`:
+    every append goes through hsla_append_decode (the last call's output is
+    the decode checked)."""
     N = 70
     full = _wl("append_full", 60, kv_dtype=dtype, seq_lens=(1400, 1250), append_room=3)
     start = dataclasses.replace(full, name="append_start", seq_lens=tuple(t - N for t in full.seq_lens))
@@ -319,13 +324,18 @@ def test_append_matches_rebuild(dtype):
     dc = DeviceCache(cfg_of(full), kp, vp, table, np.asarray(start.seq_lens, np.int32),
                      capacity_len=max(full.seq_lens))
     dc.build()
+    q_dev = to_device(inp_full["q"])
     for i in range(N):
         kn = np.stack([np.stack([inp_full["pairs"][(b, g)][0][start.seq_lens[b] + i]
                                  for g in range(full.num_kv_heads)]) for b in range(full.batch)])
         vn = np.stack([np.stack([inp_full["pairs"][(b, g)][1][start.seq_lens[b] + i]
                                  for g in range(full.num_kv_heads)]) for b in range(full.batch)])
-        dc.append(to_device(kn), to_device(vn))
-    out, sel = dc.decode(to_device(inp_full["q"]))
+        if fused:
+            out, sel = dc.append_decode(to_device(kn), to_device(vn), q_dev)
+        else:
+            dc.append(to_device(kn), to_device(vn))
+    if not fused:
+        out, sel = dc.decode(q_dev)
     torch.cuda.synchronize()
     assert dc.seq_lens.cpu().numpy().tolist() == list(full.seq_lens)
     inp_check = dict(inp_full)
@@ -334,10 +344,11 @@ def test_append_matches_rebuild(dtype):
     mean_g, var_g = dc.blk_mean.cpu().numpy(), dc.blk_var.cpu().numpy()
     for (b, g), (K, V) in inp_full["pairs"].items():
         Kf, Vf = O.to_f64(K, dtype), O.to_f64(V, dtype)
-        st = O.global_state(Kf, Vf)
+        Ts = Kf.shape[0] - Kf.shape[0] % full.block_size   # the state holds complete blocks
+        st = O.global_state(Kf[:Ts], Vf[:Ts])
         gs = O.LinearState(dc.S[b, g].cpu().numpy().astype(np.float64), dc.z[b, g].cpu().numpy().astype(np.float64),
-                           dc.sv[b, g].cpu().numpy().astype(np.float64), Kf.shape[0])
-        assert_state_close(gs, st, Kf, Vf, state_depth(Kf.shape[0]) + N)
+                           dc.sv[b, g].cpu().numpy().astype(np.float64), Ts)
+        assert_state_close(gs, st, Kf[:Ts], Vf[:Ts], state_depth(Ts) + N)
         m, v = O.block_statistics(Kf, full.block_size)
         pages = table[b, :Kf.shape[0] // full.block_size]
         assert_stats_close(mean_g[pages, g], var_g[pages, g], m, v, Kf, full.block_size)
