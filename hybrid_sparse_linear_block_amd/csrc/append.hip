@@ -8,12 +8,12 @@
 // never needs them; folding them in at completion gives the same outputs as
 // a per-token update while the per-step work shrinks to one row write.
 //
-// Grid: (row chunks of 32 rows of S, sequence x kv head).  Row chunk 0
+// Grid: (row chunks of 32 rows of S + 1, sequence x kv head).  Row chunk 0
 // writes the page slot and the new length; on a completing step every chunk
-// adds the block to its rows of S and z, chunk 0 to sv, and the last chunk
-// computes the statistics (the whole workgroup reads the block's rows as
-// 16-byte vectors and reduces per channel through LDS, mean first, then the
-// variance around it).
+// stages the block through LDS and adds it to its rows of S and z (chunk 0
+// also to sv), while the extra workgroup computes the block's statistics
+// (it reads the block's rows as 16-byte vectors and reduces per channel
+// through LDS, mean first, then the variance around it).
 #include "append_parts.h"
 #include "internal.h"
 
@@ -64,6 +64,13 @@ __global__ __launch_bounds__(kThreads) void k_append(AppendParams P) {
     if (g == 0 && tid == 0 && P.seq_lens_after) P.seq_lens_after[b] = T + 1;
   }
   if ((T + 1) % B != 0) return;   // uniform: the block is still incomplete
+  __shared__ uint4 lds[kFoldStageBytes / 16];   // block stage, or the statistics' sums
+  if (rc == D / kFoldRows) {      // the statistics workgroup
+    const size_t so = (page * P.Hkv + g) * D;
+    filled_block_stats<KV, D, kThreads>(P.k_pages, P.k_new, row0, T % B, nbase, B, P.blk_mean + so, P.blk_var + so,
+                                        *reinterpret_cast<BlockStatsLds<kThreads, D>*>(lds));
+    return;
+  }
   const CompletedBlock cb{P.k_pages, P.v_pages, P.k_new, P.v_new, row0, nbase, T % B, B};
   const int col4 = tid % C4;
   const int r_first = rc * kFoldRows + tid / C4;
@@ -72,25 +79,21 @@ __global__ __launch_bounds__(kThreads) void k_append(AppendParams P) {
 #pragma unroll
   for (int i = 0; i < NR; ++i)
     srow[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(r_first + i * RG) * D + col4 * 4);
-  fold_block_rows<KV, D, NR, RG>(srow, cb, r_first, col4);
+  const int zrow = tid < kFoldRows ? rc * kFoldRows + tid : -1;
+  const int svcol = rc == 0 && tid < D ? tid : -1;
+  float z = zrow >= 0 ? P.z[nbase + zrow] : 0.f;
+  float sv = svcol >= 0 ? P.sv[nbase + svcol] : 0.f;
+  fold_completed_block<KV, D, kThreads, NR, RG>(cb, lds, srow, r_first, col4, zrow, z, svcol, sv);
 #pragma unroll
   for (int i = 0; i < NR; ++i)
     *reinterpret_cast<float4*>(Sp + static_cast<size_t>(r_first + i * RG) * D + col4 * 4) = srow[i];
-  if (tid < kFoldRows) {
-    const int r = rc * kFoldRows + tid;
-    P.z[nbase + r] += fold_block_channel<KV, D>(P.k_pages, P.k_new, cb, r);
-  }
-  if (rc == 0 && tid < D) P.sv[nbase + tid] += fold_block_channel<KV, D>(P.v_pages, P.v_new, cb, tid);
-  if (rc == D / kFoldRows - 1) {
-    __shared__ BlockStatsLds<kThreads, D> lds;
-    const size_t so = (page * P.Hkv + g) * D;
-    filled_block_stats<KV, D, kThreads>(P.k_pages, P.k_new, row0, T % B, nbase, B, P.blk_mean + so, P.blk_var + so, lds);
-  }
+  if (zrow >= 0) P.z[nbase + zrow] = z;
+  if (svcol >= 0) P.sv[nbase + svcol] = sv;
 }
 
 template <typename KV, int D>
 hipError_t launch_t(const Problem& p, const AppendParams& P, hipStream_t s) {
-  dim3 grid(D / kFoldRows, p.batch * p.Hkv);
+  dim3 grid(D / kFoldRows + 1, p.batch * p.Hkv);   // row chunks + the statistics workgroup
   hipLaunchKernelGGL((k_append<KV, D>), grid, dim3(kThreads), 0, s, P);
   return launch_status("k_append");
 }

@@ -126,35 +126,88 @@ __device__ __forceinline__ const char* block_row(const void* pages, const void* 
                       : reinterpret_cast<const char*>(pages) + (cb.row0 + j) * D * KV::kBytes;
 }
 
+// Staging of a completed block's rows in LDS for the fold: up to 64 rows of
+// keys and values per stage, within kFoldStageBytes.
+constexpr int kFoldStageBytes = 32768;
+
+template <typename KV, int D>
+struct FoldStage {
+  static constexpr int kRowBytes = D * KV::kBytes;
+  static constexpr int kFit = kFoldStageBytes / (2 * kRowBytes);
+  static constexpr int kRows = kFit < 64 ? kFit : 64;   // rows per stage
+  static constexpr int kVec = kRowBytes / 16;           // 16-byte vectors per row
+};
+
+// Rows [j0, j0 + n) of the block's keys and then values into LDS (`lds`:
+// keys [kRows][D], values [kRows][D], in kv_dtype), every load issued before
+// the first LDS store.  NT threads, 16-byte vectors.
+template <typename KV, int D, int NT>
+__device__ __forceinline__ void stage_block_rows(const CompletedBlock& cb, int j0, int n, uint4* lds) {
+  using F = FoldStage<KV, D>;
+  constexpr int PER = (2 * F::kRows * F::kVec + NT - 1) / NT;
+  const int per_kv = n * F::kVec;
+  uint4 buf[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int idx = static_cast<int>(threadIdx.x) + p * NT;
+    const int kv = idx < per_kv ? 0 : 1;
+    const int rem = idx - kv * per_kv;
+    const int j = rem / F::kVec;
+    const int c16 = rem % F::kVec;
+    if (idx < 2 * per_kv) {
+      const char* row = kv ? block_row<KV, D>(cb.v_pages, cb.v_new, cb, j0 + j)
+                           : block_row<KV, D>(cb.k_pages, cb.k_new, cb, j0 + j);
+      buf[p] = reinterpret_cast<const uint4*>(row)[c16];
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int idx = static_cast<int>(threadIdx.x) + p * NT;
+    const int kv = idx < per_kv ? 0 : 1;
+    const int rem = idx - kv * per_kv;
+    if (idx < 2 * per_kv) lds[kv * F::kRows * F::kVec + rem] = buf[p];
+  }
+}
+
 // The linear state takes a block's tokens when the block completes (tokens
 // of the incomplete last block always lie inside the window, so they are
-// exact and never enter the linear part): rows r_first + RG i (i < NR),
-// columns 4 col4 .. 4 col4 + 3 of S gain sum_j k_j[r] v_j[c] over the
-// block's rows, summed in row order and added once.
-template <typename KV, int D, int NR, int RG>
-__device__ __forceinline__ void fold_block_rows(float4 (&srow)[NR], const CompletedBlock& cb, int r_first, int col4) {
+// exact and never enter the linear part).  This adds the completed block to
+// one workgroup's rows: rows r_first + RG i (i < NR), columns 4 col4 ..
+// 4 col4 + 3 of S (srow) gain sum_j k_j[r] v_j[c]; the thread's z row
+// (zrow >= 0) gains sum_j k_j[zrow] and its sv channel (svcol >= 0) sum_j
+// v_j[svcol].  The block is staged through `lds` (kFoldStageBytes) and every
+// sum runs in row order, then is added once.  Every thread of the
+// workgroup must call it.
+template <typename KV, int D, int NT, int NR, int RG>
+__device__ void fold_completed_block(const CompletedBlock& cb, uint4* lds, float4 (&srow)[NR], int r_first, int col4,
+                                     int zrow, float& z, int svcol, float& sv) {
+  using F = FoldStage<KV, D>;
   float4 acc[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j0 = 0; j0 < cb.B; j0 += 4) {   // B is a multiple of 4
-    float4 v[4];
-    float kr[4][NR];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      v[u] = kv_load4<KV>(block_row<KV, D>(cb.v_pages, cb.v_new, cb, j0 + u), col4 * 4);
-      const char* krow = block_row<KV, D>(cb.k_pages, cb.k_new, cb, j0 + u);
-#pragma unroll
-      for (int i = 0; i < NR; ++i) kr[u][i] = kv_elem<KV>(krow, r_first + i * RG);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
+  float zacc = 0.f, svacc = 0.f;
+  const char* ks = reinterpret_cast<const char*>(lds);
+  const char* vs = ks + F::kRows * F::kRowBytes;
+  for (int j0 = 0; j0 < cb.B; j0 += F::kRows) {
+    const int n = min(F::kRows, cb.B - j0);
+    if (j0 > 0) __syncthreads();   // the previous stage is consumed
+    stage_block_rows<KV, D, NT>(cb, j0, n, lds);
+    __syncthreads();
+    for (int j = 0; j < n; ++j) {
+      const float4 v = kv_load4<KV>(vs + j * F::kRowBytes, col4 * 4);
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
-        acc[i].x = fmaf(kr[u][i], v[u].x, acc[i].x);
-        acc[i].y = fmaf(kr[u][i], v[u].y, acc[i].y);
-        acc[i].z = fmaf(kr[u][i], v[u].z, acc[i].z);
-        acc[i].w = fmaf(kr[u][i], v[u].w, acc[i].w);
+        const float kr = kv_elem<KV>(ks + j * F::kRowBytes, r_first + i * RG);
+        acc[i].x = fmaf(kr, v.x, acc[i].x);
+        acc[i].y = fmaf(kr, v.y, acc[i].y);
+        acc[i].z = fmaf(kr, v.z, acc[i].z);
+        acc[i].w = fmaf(kr, v.w, acc[i].w);
       }
+    }
+    if (zrow >= 0)
+      for (int j = 0; j < n; ++j) zacc += kv_elem<KV>(ks + j * F::kRowBytes, zrow);
+    if (svcol >= 0)
+      for (int j = 0; j < n; ++j) svacc += kv_elem<KV>(vs + j * F::kRowBytes, svcol);
   }
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
@@ -163,15 +216,8 @@ __device__ __forceinline__ void fold_block_rows(float4 (&srow)[NR], const Comple
     srow[i].z += acc[i].z;
     srow[i].w += acc[i].w;
   }
-}
-
-// Channel c summed over the completed block's rows (z for keys, sv for
-// values), in row order.
-template <typename KV, int D>
-__device__ __forceinline__ float fold_block_channel(const void* pages, const void* nw, const CompletedBlock& cb, int c) {
-  float acc = 0.f;
-  for (int j = 0; j < cb.B; ++j) acc += kv_elem<KV>(block_row<KV, D>(pages, nw, cb, j), c);
-  return acc;
+  z += zacc;
+  sv += svacc;
 }
 
 }  // namespace hsla

@@ -252,10 +252,11 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
 // of the pair's G heads (SPLA, section "Method": the linear part reads the
 // global state).  With the append taken in, row chunk 0 writes the new
 // token's page slot and length, and when the token completes its block
-// every chunk first adds the block to its rows of S and z (chunk 0 to sv,
-// the last chunk computes the block's statistics) and writes them back, so
-// that the readout sees the state the stand-alone append would leave.
-// Without the linear tail only the append's part runs.
+// every chunk first adds the block to its rows of S and z (chunk 0 also to
+// sv) and writes them back, so that the readout sees the state the
+// stand-alone append would leave; one more workgroup per pair (rc = d/32)
+// computes the block's statistics.  Without the linear tail only the
+// append's part runs.
 template <typename KV, int D, int G>
 __device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g, int rc) {
   constexpr int C4 = D / 4;            // float4 columns per row
@@ -273,6 +274,17 @@ __device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g
   const bool lin = P.linear_tail != 0;
   const size_t qbase = (static_cast<size_t>(b) * P.Hq + g * G) * D;
   const size_t nbase = static_cast<size_t>(pair) * D;   // k_new / v_new row of the pair
+  __shared__ uint4 fold_lds[kFoldStageBytes / 16];      // block stage, or the statistics' sums
+  if (app && rc == D / kRoRows) {   // the statistics workgroup of the append
+    const int T = append_pos(P, b);
+    if ((T + 1) % P.B != 0) return;
+    const size_t page = static_cast<size_t>(P.block_table[static_cast<size_t>(b) * P.max_blocks + T / P.B]);
+    const size_t so = (page * P.Hkv + g) * D;
+    filled_block_stats<KV, D, kThreads>(P.app.k_pages, P.app.k_new, (page * P.Hkv + g) * P.B, T % P.B, nbase, P.B,
+                                        P.app.blk_mean + so, P.app.blk_var + so,
+                                        *reinterpret_cast<BlockStatsLds<kThreads, D>*>(fold_lds));
+    return;
+  }
 
   const float* Sp = (app ? P.app.S : P.S) + static_cast<size_t>(pair) * D * D;
   const float* zp = (app ? P.app.z : P.z) + nbase + r0;
@@ -316,22 +328,16 @@ __device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g
   }
   if (completes) {
     const CompletedBlock cb{P.app.k_pages, P.app.v_pages, P.app.k_new, P.app.v_new, row0, nbase, T % P.B, P.B};
-    fold_block_rows<KV, D, NR, RG>(srow, cb, r0 + rg, col4);
+    const int zrow = tid < kRoRows ? r0 + tid : -1;
+    const int svcol = rc == 0 && tid < D ? tid : -1;
+    float sv = svcol >= 0 ? P.app.sv[nbase + svcol] : 0.f;
+    fold_completed_block<KV, D, kThreads, NR, RG>(cb, fold_lds, srow, r0 + rg, col4, zrow, zr, svcol, sv);
     float* Sw = P.app.S + static_cast<size_t>(pair) * D * D;
 #pragma unroll
     for (int i = 0; i < NR; ++i)
       *reinterpret_cast<float4*>(Sw + static_cast<size_t>(r0 + rg + i * RG) * D + col4 * 4) = srow[i];
-    if (tid < kRoRows) {
-      zr += fold_block_channel<KV, D>(P.app.k_pages, P.app.k_new, cb, r0 + tid);
-      P.app.z[nbase + r0 + tid] = zr;
-    }
-    if (rc == 0 && tid < D) P.app.sv[nbase + tid] += fold_block_channel<KV, D>(P.app.v_pages, P.app.v_new, cb, tid);
-    if (rc == D / kRoRows - 1) {
-      __shared__ BlockStatsLds<kThreads, D> lds;
-      const size_t so = (page * P.Hkv + g) * D;
-      filled_block_stats<KV, D, kThreads>(P.app.k_pages, P.app.k_new, row0, T % P.B, nbase, P.B,
-                                          P.app.blk_mean + so, P.app.blk_var + so, lds);
-    }
+    if (zrow >= 0) P.app.z[nbase + zrow] = zr;
+    if (svcol >= 0) P.app.sv[nbase + svcol] = sv;
   }
   if (!lin) return;
   if (tid < kRoRows) zs[tid] = zr;
@@ -1829,7 +1835,7 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
   int ev = 0;   // profiling events: one before each launched kernel, one after the last
   // with the append taken in, the row-chunk workgroups run whatever the
   // linear tail (they apply the state update)
-  const int ro_launch = P.app.k_new ? D / kRoRows : L.ro_wgs;
+  const int ro_launch = P.app.k_new ? D / kRoRows + 1 : L.ro_wgs;   // + the statistics workgroup
   if (rec) rec(ctx, ev++, P.app.k_new ? "append_score_readout" : "score_readout");
   if (L.score_wgs + ro_launch > 0) {   // neither candidates nor a linear tail: nothing to score or read out
     dim3 grid(L.score_wgs + ro_launch, pairs);
