@@ -409,7 +409,9 @@ def setup(args, extra_steps):
         # independent caches with the same contents at other addresses
         dc = base if r == 0 else DeviceCache(cfg, inp["k_pages"], inp["v_pages"], inp["block_table"],
                                              inp["seq_lens"], capacity_len=cap)
-        e0, e1 = hip.event(), hip.event()
+        if r == 0:   # the first launch of the build loads its code; untimed
+            dc.build()
+        e0, e1 = hip.event(no_fence=True), hip.event(no_fence=True)
         hip.record(e0, stream)
         dc.build()
         hip.record(e1, stream)
@@ -456,7 +458,9 @@ def hybrid_main(args):
                              deterministic=int(args.deterministic))
             dc = DeviceCache(cfg, inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"],
                              capacity_len=cap)
-            e0, e1 = hip.event(), hip.event()
+            if not dcs:   # the first launch of the build loads its code; untimed
+                dc.build()
+            e0, e1 = hip.event(no_fence=True), hip.event(no_fence=True)
             hip.record(e0, stream)
             dc.build()
             hip.record(e1, stream)

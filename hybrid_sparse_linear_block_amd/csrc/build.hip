@@ -408,12 +408,21 @@ __global__ __launch_bounds__(kThreads) void k_build_reduce(BuildParams P) {
   if (e4 >= N4) return;
   const float* src = P.ws + static_cast<size_t>(pair) * P.nchunk * P.part_stride + e4 * 4;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = 0; c < P.nchunk; ++c) {
-    const float4 v = *reinterpret_cast<const float4*>(src + static_cast<size_t>(c) * P.part_stride);
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
+  // eight partials in flight, summed in chunk order
+  constexpr int U = 8;
+  for (int c0 = 0; c0 < P.nchunk; c0 += U) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = c0 + u < P.nchunk ? *reinterpret_cast<const float4*>(src + static_cast<size_t>(c0 + u) * P.part_stride)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      s.x += v[u].x;
+      s.y += v[u].y;
+      s.z += v[u].z;
+      s.w += v[u].w;
+    }
   }
   const int e = e4 * 4;
   float* dst;
