@@ -49,6 +49,13 @@ constexpr int kUnit = 64;        // tokens per attention work unit
 // younger workgroup of a CU starts its loop late).
 constexpr int kAttendWgsTarget = 256;
 constexpr int kCtrStride = 32;       // ints between two pairs' work counters (one 128-byte line each)
+constexpr int kDoneSlot = 16;        // a pair's count of finished attention workgroups (fused merge)
+// The last attention workgroup of a pair merges when the pair has at most
+// this many splits.  Its tail (partial stores completing, the count, the
+// partial loads: three round trips) costs about what the merge kernel does
+// at 4 splits per pair, and wins where the merge kernel has many small
+// workgroups of its own (one split per pair for large batches).
+constexpr int kFusedMergeSplits = 2;
 constexpr int kUnitSlices = 4;       // slices per dynamically claimed unit
 constexpr int kMaxDynList = 2048;    // union entries a dynamic attention workgroup holds in LDS
 constexpr int kDeadT0 = 1 << 30;     // first token of a slice whose rows are all invalid
@@ -98,6 +105,7 @@ struct DecodeParams {
   int sstride, nwords, bt_staged;
   int dyn;          // attention workgroups of a pair claim its slices dynamically
   int fused_sel;    // per-head selection inside the attention prologue (no selection kernel)
+  int fused_merge;  // the last attention workgroup of a pair merges its splits (no merge kernel)
   SelLayout sl;
   DecodeAppend app;
   float sigma;
@@ -397,8 +405,13 @@ __global__ __launch_bounds__(kThreads) void k_score_readout(DecodeParams P) {
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
   const int x = blockIdx.x;
-  if (P.dyn && P.fused_sel && x == 0 && threadIdx.x == 0)   // the pair's work counter for the attention kernel
-    __hip_atomic_store(P.ctr + static_cast<size_t>(pair) * kCtrStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (x == 0 && threadIdx.x == 0) {   // the pair's counters for the attention kernel
+    if (P.dyn && P.fused_sel)
+      __hip_atomic_store(P.ctr + static_cast<size_t>(pair) * kCtrStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (P.fused_merge)
+      __hip_atomic_store(P.ctr + static_cast<size_t>(pair) * kCtrStride + kDoneSlot, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (x < P.score_wgs) {
     score_part<KV, D, G>(P, b, g, x);
   } else {
@@ -1363,6 +1376,82 @@ struct VSlice<4> {   // D = 64: 4 channels of a row per lane
   __device__ __forceinline__ void zero() { r = make_uint2(0, 0); }
 };
 
+// Partials shared between the attention workgroups of a pair go through
+// agent-scope atomic stores and loads: each access is coherent across the
+// XCDs' L2 caches on its own, so no cache-wide release (an L2 writeback,
+// which costs microseconds per workgroup) is needed.  A writer waits for its
+// stores to complete before it counts itself done.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// The merge of one pair's nsplit split partials and its residual linear part
+// (SPLA Abstract: global state minus the exact tokens' share), done by the
+// pair's last attention workgroup: thread entries (head, channel) walk the
+// splits with a running maximum, every split's loads issued together.
+template <int D, int G>
+__device__ void merge_pair(const DecodeParams& P, int pair, int b, int g, int nsplit, int T) {
+  constexpr int RO = D / kRoRows;
+  const float* pb = P.part + static_cast<size_t>(pair) * P.max_split * G * P.pstride;
+  const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
+  const bool tail = P.linear_tail && P.top_k < min(cr.count, P.nc_max);
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int hh = idx / D;
+    const int c = idx % D;
+    float ms[kFusedMergeSplits], ls[kFusedMergeSplits], lw[kFusedMergeSplits], a[kFusedMergeSplits],
+        la[kFusedMergeSplits];
+#pragma unroll
+    for (int s = 0; s < kFusedMergeSplits; ++s) {
+      const float* ps = pb + (static_cast<size_t>(min(s, nsplit - 1)) * G + hh) * P.pstride;
+      ms[s] = load_agent(ps);
+      ls[s] = load_agent(ps + 1);
+      lw[s] = load_agent(ps + 2);
+      a[s] = load_agent(ps + 4 + c);
+      la[s] = load_agent(ps + 4 + D + c);
+    }
+    float ro = 0.f, rz = 0.f, svc = 0.f;
+    if (tail) {
+#pragma unroll
+      for (int rc = 0; rc < RO; ++rc) {
+        ro += P.ro[((static_cast<size_t>(pair) * RO + rc) * G + hh) * D + c];
+        rz += P.roz[(static_cast<size_t>(pair) * RO + rc) * G + hh];
+      }
+      svc = P.sv[static_cast<size_t>(pair) * D + c];
+    }
+    float M = 0.f;   // the linear part is in unshifted units (log-scale 0)
+    float num = 0.f, den = 0.f, lnum = 0.f, lden = 0.f;
+#pragma unroll
+    for (int s = 0; s < kFusedMergeSplits; ++s) {
+      if (s >= nsplit) break;
+      lnum += la[s];
+      lden += lw[s];
+      if (ms[s] != kNegInf) {
+        if (ms[s] > M) {
+          const float r = __expf(M - ms[s]);
+          num *= r;
+          den *= r;
+          M = ms[s];
+        }
+        const float f = __expf(ms[s] - M);
+        num = fmaf(f, a[s], num);
+        den = fmaf(f, ls[s], den);
+      }
+    }
+    if (tail) {
+      const float num_u = svc + P.sigma * ro - lnum;
+      const float den_u = static_cast<float>(T - T % P.B) + P.sigma * rz - lden;   // n: tokens the state holds
+      const float em = __expf(-M);
+      num = fmaf(em, num_u, num);
+      den = fmaf(em, den_u, den);
+    }
+    P.out[(static_cast<size_t>(b) * P.Hq + g * G + hh) * D + c] = num / den;
+  }
+}
+
 template <int D, int G, bool DYN, int FK>
 __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   constexpr int NW = kThreads / kWave;
@@ -1706,14 +1795,39 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
       ld += wst[w][h][2];
     }
     float* o = outp + static_cast<size_t>(h) * P.pstride;
-    o[4 + c] = a;
-    o[4 + D + c] = la;
-    if (c == 0) {
-      o[0] = M;
-      o[1] = l;
-      o[2] = ld;
-      o[3] = 0.f;
+    if (P.fused_merge) {
+      store_agent(o + 4 + c, a);
+      store_agent(o + 4 + D + c, la);
+      if (c == 0) {
+        store_agent(o, M);
+        store_agent(o + 1, l);
+        store_agent(o + 2, ld);
+      }
+    } else {
+      o[4 + c] = a;
+      o[4 + D + c] = la;
+      if (c == 0) {
+        o[0] = M;
+        o[1] = l;
+        o[2] = ld;
+        o[3] = 0.f;
+      }
     }
+  }
+  if (P.fused_merge) {
+    // The pair's last workgroup to finish merges: every thread's partial
+    // stores complete first, then one thread counts the workgroup done.
+    __shared__ int is_last;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    const int writers = DYN ? P.max_split : min(share.count, P.max_split);
+    if (tid == 0)
+      is_last = __hip_atomic_fetch_add(P.ctr + static_cast<size_t>(pair) * kCtrStride + kDoneSlot, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) == writers - 1;
+    __syncthreads();
+    if (is_last) merge_pair<D, G>(P, pair, b, g, writers, T);
   }
 }
 
@@ -1837,8 +1951,10 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
   // linear tail (they apply the state update)
   const int ro_launch = P.app.k_new ? D / kRoRows + 1 : L.ro_wgs;   // + the statistics workgroup
   if (rec) rec(ctx, ev++, P.app.k_new ? "append_score_readout" : "score_readout");
-  if (L.score_wgs + ro_launch > 0) {   // neither candidates nor a linear tail: nothing to score or read out
-    dim3 grid(L.score_wgs + ro_launch, pairs);
+  // neither candidates nor a linear tail: nothing to score or read out, and
+  // the launch only runs when a counter of the attention kernel needs zeroing
+  if (L.score_wgs + ro_launch > 0 || P.fused_merge) {
+    dim3 grid(std::max(1, L.score_wgs + ro_launch), pairs);
     hipLaunchKernelGGL((k_score_readout<KV, D, G>), grid, dim3(kThreads), 0, stream, P);
     hipError_t e = launch_status("k_score_readout");
     if (e != hipSuccess) return e;
@@ -1900,8 +2016,8 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
     hipError_t e = launch_status("k_attend");
     if (e != hipSuccess) return e;
   }
-  if (rec) rec(ctx, ev++, "merge");
-  {
+  if (!P.fused_merge) {   // else the last attention workgroup of each pair merged it
+    if (rec) rec(ctx, ev++, "merge");
     hipLaunchKernelGGL((k_merge<D, G>), dim3(p.batch * p.Hq), dim3(kThreads), 0, stream, P);
     hipError_t e = launch_status("k_merge");
     if (e != hipSuccess) return e;
@@ -1955,6 +2071,8 @@ DecodeLayout decode_layout(const Problem& p) {
       L.max_split = ceil_div(L.umax, L.bps);
     }
   }
+  // bf16 attention with few splits per pair: its last workgroup merges
+  L.fused_merge = (p.bf16 && L.max_split <= kFusedMergeSplits) ? 1 : 0;
   L.pstride = 2 * p.D + 4;
   L.sstride = std::max(4, (p.nc_max + 3) / 4 * 4);
   L.nwords = std::max(1, (p.nc_max + 63) / 64);
@@ -2016,6 +2134,7 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.ctr = reinterpret_cast<int32_t*>(a.ws + L.off_ctr);
   P.dyn = L.dyn;
   P.fused_sel = L.fused_sel;
+  P.fused_merge = L.fused_merge;
   P.part = reinterpret_cast<float*>(a.ws + L.off_part);
   P.Hq = p.Hq;
   P.Hkv = p.Hkv;

@@ -56,6 +56,7 @@ struct DecodeLayout {
   int bt_staged;       // block-table row staged in LDS
   int dyn;             // attention workgroups of a pair claim its slices dynamically
   int fused_sel;       // per-head selection in the attention prologue
+  int fused_merge;     // the last attention workgroup of a pair merges (no merge kernel)
   SelLayout sl;
   size_t off_scores, off_ro, off_roz, off_bits, off_ucount, off_ctr, off_part, total;
 };

@@ -415,3 +415,42 @@ def test_long_candidate_rows(case):
     dc, out, sel = run_gpu(wl, inp)
     worst, flips = check_case(wl, inp, dc, out, sel, check_build=False)
     print(f"  worst row error {worst:.3e}, near-tie flips {flips}")
+
+
+# ----------------------------------------------------------------------------
+# Merge by the last attention workgroup of each pair
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("deterministic", [1, 0])
+def test_merge_in_last_workgroup(deterministic):
+    """128 pairs, so two splits per pair: the attention kernel's last
+    workgroup of each pair merges.  Outputs against the oracle, then
+    alternating queries on the same cache: every call must match the first
+    call with the same queries (a merge reading another call's partials
+    would not)."""
+    wl = _wl("merge_fused", 81, batch=16, num_q_heads=32, num_kv_heads=8,
+             seq_lens=(2100, 1900, 2047, 1500, 1300, 1800, 2200, 1717, 1600, 2000, 1999, 1450, 2050, 1650, 1900, 1333),
+             deterministic=deterministic)
+    _announce(wl, "merge in the attention kernel")
+    inp = W.make_inputs(wl)
+    dc, out, sel = run_gpu(wl, inp)
+    worst, _ = check_case(wl, inp, dc, out, sel, check_build=False)
+    print(f"  worst row error {worst:.3e}")
+    qs = [to_device(inp["q"]), to_device(W.gen_queries(wl, variant=1))]
+    first = []
+    for i in range(2):
+        o, s = dc.decode(qs[i])
+        torch.cuda.synchronize()
+        first.append((o.cpu().numpy(), s.cpu().numpy()))
+    assert not np.array_equal(first[0][0], first[1][0])
+    for it in range(40):
+        o, s = dc.decode(qs[it % 2])
+        o, s = o.cpu().numpy(), s.cpu().numpy()
+        ref_o, ref_s = first[it % 2]
+        assert np.array_equal(s, ref_s), it
+        if deterministic:
+            assert np.array_equal(o, ref_o), it
+        else:
+            for b in range(wl.batch):
+                for h in range(wl.num_q_heads):
+                    assert row_rel_err(o[b, h], ref_o[b, h]) < 1e-5, (it, b, h)
