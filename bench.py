@@ -60,6 +60,11 @@ def parse(argv=None):
                     help="only the work profiled for HBM traffic: a device copy of known size, then a few steps")
     ap.add_argument("--traffic-collect", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="rocprofv3 counter files of two --traffic-run passes -> profiles/attend_traffic.json")
+    ap.add_argument("--build-run", action="store_true",
+                    help="only the work profiled for the build's counters: a device copy of known size, then "
+                         "BUILD_RUNS builds of the workload's cache")
+    ap.add_argument("--build-collect", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "MFMA_CSV"),
+                    help="rocprofv3 counter files of three --build-run passes -> summary on stdout")
     ap.add_argument("--profile-summary", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="rocprofv3 --stats kernel file -> markdown summary on stdout")
     ap.add_argument("--separate-append", action="store_true",
@@ -195,6 +200,59 @@ def traffic_run(args):
         preps[i % R]()
     torch.cuda.synchronize()
     print(f"[traffic] {TRAFFIC_STEPS} steps done", file=sys.stderr)
+
+
+BUILD_RUNS = 4
+
+
+def build_run(args):
+    """The profiled program of the build's counter passes: the calibration
+    copy, then BUILD_RUNS builds of one cache of the workload."""
+    import torch
+
+    import workloads as W
+    from hybrid_sparse_linear_block_amd.device import DeviceCache, config_for
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    wl = workload(args.workload)
+    inp = W.make_inputs(wl, keep_pairs=False)
+    cfg = config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
+                     wl.window, wl.linear_tail, wl.kv_dtype)
+    dc = DeviceCache(cfg, inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"])
+    for _ in range(BUILD_RUNS):
+        dc.build()
+    torch.cuda.synchronize()
+    print(f"[build-run] {BUILD_RUNS} builds done", file=sys.stderr)
+
+
+def build_collect(fetch_csv, write_csv, mfma_csv):
+    """HBM bytes (scaled as for the attention kernel) and MFMA counters per
+    dispatch of the bf16 build kernel."""
+    wl = workload(parse_known_workload())
+    T = max(wl.seq_lens)
+    pairs = wl.batch * wl.num_kv_heads
+    res = {"workload": wl.name}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, counter)
+        copy = [v for n, v in rows if "k_" not in n and v * 1024 > COPY_BYTES / 4]
+        build = [v for n, v in rows if "k_build_bf16" in n]
+        if not copy or not build:
+            raise SystemExit(f"{path}: no copy or build dispatches for {counter}")
+        scale = COPY_BYTES / (max(copy) * 1024.0)
+        res[counter.lower() + "_bytes"] = int(np.mean(build) * 1024.0 * scale)
+        res[counter.lower() + "_scale"] = round(scale, 4)
+    for counter in ("MfmaUtil", "MfmaFlopsBF16"):
+        v = [x for n, x in _counter_rows(mfma_csv, counter) if "k_build_bf16" in n]
+        res[counter] = float(np.mean(v)) if v else None
+    # K and V read, block statistics and the state written (chunk partials are overhead)
+    res["algorithmic_bytes"] = int(pairs * (T * wl.head_dim * 2 * wl.elem_bytes + T // wl.block_size * 2 * wl.head_dim * 4
+                                            + (wl.head_dim ** 2 + 2 * wl.head_dim) * 4))
+    res["algorithmic_flop"] = int(pairs * 2 * T * wl.head_dim ** 2)
+    print(json.dumps(res))
 
 
 def _counter_rows(path, counter):
@@ -591,6 +649,9 @@ def main():
     if args.traffic_collect:
         traffic_collect(*args.traffic_collect)
         return
+    if args.build_collect:
+        build_collect(*args.build_collect)
+        return
     if args.profile_summary:
         print(profile_summary(*args.profile_summary))
         return
@@ -608,6 +669,9 @@ def main():
         return
     if args.traffic_run:
         traffic_run(args)
+        return
+    if args.build_run:
+        build_run(args)
         return
     steps, warm = args.steps, args.warmup
     env = setup(args, 2 * steps)   # timed and profiled steps
