@@ -53,7 +53,11 @@ __device__ __forceinline__ int full_blocks_len(int T, int B) { return T - T % B;
 // One workgroup per (sequence, kv head, chunk of tokens); tiles of 64 tokens.
 // Thread task = 8 tokens x 8 channels of K or V (eight 16-byte row loads of
 // one page); the 8 x 8 block is transposed in registers and stored
-// channel-major in LDS, so that
+// channel-major in LDS.  Lanes take the token groups fastest, so that the
+// 16 lanes of one 16-byte LDS store hit 16 distinct bank quads (with the
+// channel groups fastest, lanes 8 channels apart share banks: 8-way
+// conflicts that dominated the kernel), while each global load still reads
+// whole 128-byte lines.  The layout serves two readers:
 //   * the MFMA operands (8 consecutive tokens of one channel) are single
 //     16-byte LDS reads: S += K^T V with v_mfma_f32_32x32x16_bf16, wave
 //     (wi, wj) owning a D/2 x D/2 quarter of S;
@@ -129,8 +133,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_build_bf16(BuildParams P) {
       if (kPartial && task >= TASKS) break;
       const int tensor = task / ((kTile / 8) * (D / 8));
       const int rem = task % ((kTile / 8) * (D / 8));
-      const int tg = rem / (D / 8);
-      const int cg = rem % (D / 8);
+      const int tg = rem % (kTile / 8);
+      const int cg = rem / (kTile / 8);
       // first token of the group, clamped to the last group that holds a
       // token (a multiple of 8, so the 8 rows stay inside one page)
       const int t8 = min(tile0 + tg * 8, (c_end - 1) & ~7);
@@ -149,8 +153,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_build_bf16(BuildParams P) {
       if (kPartial && task >= TASKS) break;
       const int tensor = task / ((kTile / 8) * (D / 8));
       const int rem = task % ((kTile / 8) * (D / 8));
-      const int tg = rem / (D / 8);
-      const int cg = rem % (D / 8);
+      const int tg = rem % (kTile / 8);
+      const int cg = rem / (kTile / 8);
       uint16_t* dst = tensor ? Vt : Kt;
       uint32_t w[8][4];
 #pragma unroll
