@@ -121,6 +121,12 @@ def test_decode_rejects_bad_pointers_and_sizes():
     assert call_decode(c, ws=0) == H.HSLA_ERR_WORKSPACE
     assert call_decode(c, ws_bytes=16) == H.HSLA_ERR_WORKSPACE
     assert call_decode(c, max_len=(1 << 20) * 64) == H.HSLA_ERR_UNSUPPORTED
+    # one block past the largest candidate row whose selection bitmaps fit
+    # the attention workgroup's 16 KB (8 heads x 256 words at 16384 blocks)
+    big = cfg(num_q_heads=8, num_kv_heads=1, head_dim=64, block_size=16, window=64)
+    assert call_decode(big, max_len=262208 + 16, p=pool(max_blocks_per_seq=1 << 15)) == H.HSLA_ERR_UNSUPPORTED
+    assert H.hsla_decode_workspace_size(big, 1, 262208 + 16) == 0
+    assert H.hsla_decode_workspace_size(big, 1, 262208) > 0
 
 
 def test_append_rejects_aliased_lengths():

@@ -403,6 +403,10 @@ LONG_ROWS = [
     ("B16_20k", dict(block_size=16, window=256, top_k=20, seq_lens=(20011, 17000))),
     ("B16_40k", dict(block_size=16, window=256, top_k=24, seq_lens=(40000, 36999))),
     ("B16_70k", dict(batch=1, block_size=16, window=512, top_k=9, seq_lens=(70001,))),
+    # the largest candidate row the attention prologue takes: 8 heads x
+    # 256 bitmap words = 16 KB of LDS (16384 candidate blocks of 16 tokens)
+    ("max_bitmap_G8", dict(batch=1, num_q_heads=8, num_kv_heads=1, head_dim=64, block_size=16, window=64, top_k=16,
+                           seq_lens=(262208,), spare_pages=0)),
 ]
 
 
@@ -428,7 +432,7 @@ def test_merge_in_last_workgroup(deterministic):
     alternating queries on the same cache: every call must match the first
     call with the same queries (a merge reading another call's partials
     would not)."""
-    wl = _wl("merge_fused", 81, batch=16, num_q_heads=32, num_kv_heads=8,
+    wl = _wl("merge_fused", 90, batch=16, num_q_heads=32, num_kv_heads=8,
              seq_lens=(2100, 1900, 2047, 1500, 1300, 1800, 2200, 1717, 1600, 2000, 1999, 1450, 2050, 1650, 1900, 1333),
              deterministic=deterministic)
     _announce(wl, "merge in the attention kernel")
