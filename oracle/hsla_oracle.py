@@ -64,6 +64,7 @@ class Params:
     linear_tail: int = 1
     scale: float = 0.0
     grouped: int = 0   # 1: one selection shared by the G query heads of a kv head
+    tokens: int = 0    # 1: top_k counts single tokens, scored by their own keys (token-level variant)
 
     @property
     def group(self) -> int:
@@ -145,6 +146,27 @@ def candidate_blocks(T: int, p: Params) -> np.ndarray:
                      if b * B < hi and (b + 1) * B > lo and lo < hi], dtype=np.int64)
 
 
+# ----------------------------------------------------------------------------
+# Token-level variant.  ["SALS: Sparse Attention in Latent Space for KV
+# Cache Compression", summary, Approach: top-k critical tokens picked by a
+# score against each key; SALSA abstract: a sparse cache of selected tokens
+# beside the window and the linear state.]
+# Here the score is taken on the plain key (no latent projection):
+# candidates are the tokens of [ns, T - W), a token's score is sigma q.k_t,
+# and the top_k tokens by (score descending, index ascending) join the
+# exact set; everything else is unchanged.
+# ----------------------------------------------------------------------------
+
+def candidate_tokens(T: int, p: Params) -> np.ndarray:
+    """Token indices of [ns, T - W), ascending (empty when W covers the rest)."""
+    lo, hi = p.num_sink, T - p.window
+    return np.arange(lo, hi, dtype=np.int64) if lo < hi else np.zeros(0, np.int64)
+
+
+def token_scores(q: np.ndarray, K: np.ndarray, cands: np.ndarray, sigma: float) -> np.ndarray:
+    return sigma * (K[cands] @ q)
+
+
 def select_top_k(cands: np.ndarray, scores: np.ndarray, k: int) -> np.ndarray:
     """The min(k, n) best candidates by (score descending, block index ascending),
     returned in ascending block order."""
@@ -212,7 +234,7 @@ def exact_token_mask(T: int, selected: Sequence[int], p: Params) -> np.ndarray:
     E[s0:s1] = True
     w0, w1 = window_range(T, p)
     E[w0:w1] = True
-    B = p.block_size
+    B = 1 if p.tokens else p.block_size   # token-level: the selection holds token indices
     for b in selected:
         E[b * B:min((b + 1) * B, T)] = True
     return E
@@ -300,14 +322,18 @@ def decode_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, p: Params, *,
     T, d = K.shape
     sig = p.sigma
     B = p.block_size
-    cands = candidate_blocks(T, p)
-    if stats is None:
-        stats = block_statistics(K, B)
-    mean, var = stats
-    if len(cands):
-        scores = block_score(q, mean[cands], var[cands], sig)
+    if p.tokens:
+        cands = candidate_tokens(T, p)
+        scores = token_scores(q, K, cands, sig)
     else:
-        scores = np.zeros(0)
+        cands = candidate_blocks(T, p)
+        if stats is None:
+            stats = block_statistics(K, B)
+        mean, var = stats
+        if len(cands):
+            scores = block_score(q, mean[cands], var[cands], sig)
+        else:
+            scores = np.zeros(0)
     if selected is None:
         sel = select_top_k(cands, scores, p.top_k)
     else:

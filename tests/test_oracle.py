@@ -496,3 +496,86 @@ def test_group_selection_scores_every_head_of_the_group():
     cands, scores, w, sel = O.group_selection(qs, K, pg)
     assert sel.tolist() == want.tolist()
     np.testing.assert_array_equal(scores, np.stack([r.scores for r in per_head]))
+
+
+# ----------------------------------------------------------------------------
+# Token-level variant: top_k single tokens scored by their own keys
+# ----------------------------------------------------------------------------
+
+def _brute_force_tokens(q, K, V, p):
+    """Pure-Python per-token evaluation of the token-level step on a tiny input:
+    candidates [ns, T - W), score sigma q.k, top-k by rank counting."""
+    T, d = len(K), len(q)
+    sig = p.sigma
+    Kl, Vl, ql = K.tolist(), V.tolist(), q.tolist()
+    sc = {t: sig * sum(ql[c] * Kl[t][c] for c in range(d)) for t in range(p.num_sink, T - p.window)}
+    sel = [t for t in sc if sum(1 for o in sc if sc[o] > sc[t] or (sc[o] == sc[t] and o < t)) < p.top_k]
+    num = [0.0] * d
+    den = 0.0
+    for t in range(T):
+        s = sig * sum(ql[c] * Kl[t][c] for c in range(d))
+        if t < p.num_sink or t >= T - p.window or t in sel:
+            w = math.exp(s)
+        elif p.linear_tail:
+            w = 1.0 + s
+        else:
+            continue
+        den += w
+        for c in range(d):
+            num[c] += w * Vl[t][c]
+    return np.array([x / den for x in num]), sel
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_token_level_against_per_token_brute_force(seed):
+    rng = np.random.default_rng(700 + seed)
+    B = int(rng.choice([2, 4, 8]))
+    d = int(rng.integers(1, 6))
+    Wn = int(rng.integers(B, 3 * B))
+    ns = int(rng.integers(0, B + 2))
+    T = int(rng.integers(Wn + ns + 1, Wn + ns + 40))
+    k = int(rng.integers(0, 9))
+    lt = int(rng.integers(0, 2))
+    q, K, V = _rand_case(rng, T, d, scale_k=0.5)
+    p = _params(head_dim=d, block_size=B, num_sink=ns, window=Wn, top_k=k, linear_tail=lt, tokens=1)
+    want, sel = _brute_force_tokens(q, K, V, p)
+    for form in ("definition", "subtraction"):
+        r = O.decode_head(q, K, V, p, form=form)
+        assert r.selected.tolist() == sel
+        np.testing.assert_allclose(r.out, want, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_token_level_is_block_level_with_blocks_of_one_token(seed):
+    """A one-token block has its key as mean and zero variance, so its block
+    score is sigma q.k and its candidates are the tokens of [ns, T - W): the
+    token-level step equals the block-level step at block size 1."""
+    rng = np.random.default_rng(800 + seed)
+    T, d = 300, 8
+    q, K, V = _rand_case(rng, T, d)
+    for k in (0, 7, 50):
+        pt = _params(head_dim=d, block_size=16, num_sink=3, window=32, top_k=k, tokens=1)
+        pb = _params(head_dim=d, block_size=1, num_sink=3, window=32, top_k=k)
+        rt, rb = O.decode_head(q, K, V, pt), O.decode_head(q, K, V, pb)
+        assert rt.selected.tolist() == rb.selected.tolist()
+        assert (rt.exact == rb.exact).all()
+        np.testing.assert_allclose(rt.out, rb.out, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("form", ["definition", "subtraction"])
+def test_token_level_dense_when_budget_covers_all_candidates(form):
+    rng = np.random.default_rng(901)
+    T, d = 120, 8
+    q, K, V = _rand_case(rng, T, d)
+    p = _params(head_dim=d, block_size=8, num_sink=4, window=16, top_k=T, tokens=1)
+    r = O.decode_head(q, K, V, p, form=form)
+    assert r.exact.all() and r.den_u == 0.0
+    np.testing.assert_allclose(r.out, _sdpa(q, K, V, p.sigma), rtol=1e-12, atol=1e-13)
+
+
+def test_token_level_candidates_and_ties():
+    p = _params(head_dim=2, block_size=4, num_sink=2, window=3, top_k=2, tokens=1)
+    assert O.candidate_tokens(10, p).tolist() == [2, 3, 4, 5, 6]
+    assert O.candidate_tokens(5, p).tolist() == []
+    # equal scores go to the lower token index
+    assert O.select_top_k(np.array([2, 3, 4, 5, 6]), np.array([0.5, 1.0, 1.0, 1.0, 0.2]), 2).tolist() == [3, 4]
