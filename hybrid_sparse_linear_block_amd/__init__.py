@@ -26,6 +26,7 @@ HSLA_F32 = 0
 HSLA_BF16 = 1
 HSLA_SEL_PER_HEAD = 0
 HSLA_SEL_GROUPED = 1
+HSLA_SEL_TOKEN = 2
 HSLA_MAX_PROFILE_EVENTS = 8
 
 EXPORTED = ("hsla_status_string", "hsla_version", "hsla_build_workspace_size", "hsla_build_state",

@@ -56,6 +56,7 @@ constexpr int kDoneSlot = 16;        // a pair's count of finished attention wor
 // at 4 splits per pair, and wins where the merge kernel has many small
 // workgroups of its own (one split per pair for large batches).
 constexpr int kFusedMergeSplits = 2;
+constexpr int kTokensPerSplit = 256;  // token-level variant: list entries per attention workgroup
 constexpr int kUnitSlices = 4;       // slices per dynamically claimed unit
 constexpr int kMaxDynList = 2048;    // union entries a dynamic attention workgroup holds in LDS
 constexpr int kDeadT0 = 1 << 30;     // first token of a slice whose rows are all invalid
@@ -106,6 +107,9 @@ struct DecodeParams {
   int dyn;          // attention workgroups of a pair claim its slices dynamically
   int fused_sel;    // per-head selection inside the attention prologue (no selection kernel)
   int fused_merge;  // the last attention workgroup of a pair merges its splits (no merge kernel)
+  int tokens;       // token-level variant: candidates are single tokens, scored by their keys
+  int bsel;         // candidate granularity: the block size, or 1 for the token-level variant
+  int32_t* tlist;   // token-level variant: each pair's exact token list [pairs, umax] (token | heads << 20)
   SelLayout sl;
   DecodeAppend app;
   float sigma;
@@ -265,6 +269,53 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
 // stand-alone append would leave; one more workgroup per pair (rc = d/32)
 // computes the block's statistics.  Without the linear tail only the
 // append's part runs.
+// Token-level variant ("SALS: Sparse Attention in Latent Space for KV Cache
+// Compression", Approach, here on the plain keys): the scores sigma q.k_t of
+// 64 candidate tokens of one (sequence, kv head) for its G query heads, as
+// order keys.  D/8 lanes share a token (8 channels each); a pass covers 256 /
+// (D/8) tokens, and every pass's page lookups and key rows are issued before
+// the first dot product.
+template <typename KV, int D, int G>
+__device__ __forceinline__ void score_tokens_part(const DecodeParams& P, int b, int g, int chunk) {
+  constexpr int LPT = D / 8;
+  constexpr int TPP = kThreads / LPT;
+  constexpr int NIT = kScoreChunk / TPP;
+  static_assert(kScoreChunk % TPP == 0 && G <= LPT, "whole passes; one finishing lane per head");
+  const int c_begin = chunk * kScoreChunk;
+  const int tid = threadIdx.x;
+  const int lig = tid % LPT;
+  const int slot = tid / LPT;
+  const int T = first_kernel_len(P, b);
+  const CandRange cr = candidate_range(T, 1, P.ns, P.W);
+  const int nc = min(cr.count, P.nc_max);
+  if (c_begin >= nc) return;
+  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  const char* kp = reinterpret_cast<const char*>(P.k_pages);
+  Row8<KV> kr[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int t = cr.lo + min(c_begin + slot + it * TPP, nc - 1);
+    const size_t page = static_cast<size_t>(bt[t / P.B]);
+    kr[it].load(kp + (((page * P.Hkv + g) * P.B + t % P.B) * D + lig * 8) * KV::kBytes);
+  }
+  QReg<KV> qr[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qr[h].load(reinterpret_cast<const char*>(P.q) + ((static_cast<size_t>(b) * P.Hq + g * G + h) * D + lig * 8) * KV::kBytes);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    float mine = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float a = reduce_sum_lanes<LPT>(qr[h].dot(kr[it]));
+      mine = (h == lig) ? a : mine;
+    }
+    const int c = c_begin + slot + it * TPP;
+    if (lig < G && c < nc)
+      P.keys[(static_cast<size_t>(b) * P.Hq + g * G + lig) * P.sstride + c] = f32_order_key(P.sigma * mine);
+  }
+}
+
 template <typename KV, int D, int G>
 __device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g, int rc) {
   constexpr int C4 = D / 4;            // float4 columns per row
@@ -413,7 +464,11 @@ __global__ __launch_bounds__(kThreads) void k_score_readout(DecodeParams P) {
                          __HIP_MEMORY_SCOPE_AGENT);
   }
   if (x < P.score_wgs) {
-    score_part<KV, D, G>(P, b, g, x);
+    if (P.tokens) {
+      if constexpr (G <= D / 8) score_tokens_part<KV, D, G>(P, b, g, x);
+    } else {
+      score_part<KV, D, G>(P, b, g, x);
+    }
   } else {
     readout_part<KV, D, G>(P, b, g, x - P.score_wgs);
   }
@@ -697,7 +752,7 @@ __global__ __launch_bounds__(kWave) void k_select(DecodeParams P) {
     for (int j = 0; j < KPL; ++j) key[j] = kh[min(lane + kWave * j, P.sstride - 1)];
   }
   const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
-  const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
+  const CandRange cr = candidate_range(T, P.bsel, P.ns, P.W);
   const int nc = min(cr.count, P.nc_max);
   auto key_at = [&](int i) -> uint32_t { return kh[i]; };
   int32_t* out = P.sel_idx ? P.sel_idx + static_cast<size_t>(bh) * P.top_k : nullptr;
@@ -1925,7 +1980,7 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
     lnum += part_lnum[x][c];
     lden += part_lden[x][c];
   }
-  const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
+  const CandRange cr = candidate_range(T, P.bsel, P.ns, P.W);
   if (P.linear_tail && P.top_k < min(cr.count, P.nc_max)) {
     float ro = 0.f, rz = 0.f;
 #pragma unroll
@@ -1940,6 +1995,277 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
     den = fmaf(em, den_u, den);
   }
   P.out[(static_cast<size_t>(b) * P.Hq + h) * D + c] = num / den;
+}
+
+// ---------------------------------------------------------------------------
+// Token-level variant: exact token list and attention over it
+// ---------------------------------------------------------------------------
+// One workgroup per (sequence, kv head) lists the pair's exact tokens in
+// ascending order: the sinks and the window for every head, and between them
+// every candidate token some head selected, with the mask of the heads that
+// selected it (token | heads << 20).  Each thread takes a contiguous run of
+// bitmap words; a workgroup scan of their counts places the runs.
+template <int G>
+__global__ __launch_bounds__(kThreads) void k_token_union(DecodeParams P) {
+  __shared__ int wave_total[kThreads / kWave];
+  const int pair = blockIdx.x;
+  const int b = pair / P.Hkv;
+  const int g = pair % P.Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
+  const CandRange cr = candidate_range(T, 1, P.ns, P.W);
+  const int nc = min(cr.count, P.nc_max);
+  const int nw = ceil_div(nc, kWave);
+  const int nsink = min(P.ns, T);
+  const int w0 = max(T - P.W, nsink);   // first window token that is not a sink
+  constexpr int kAll = (1 << G) - 1;
+  int32_t* list = P.tlist + static_cast<size_t>(pair) * P.umax;
+  const uint64_t* bits = P.bits + (static_cast<size_t>(b) * P.Hq + g * G) * P.nwords;
+
+  const int wpt = ceil_div(nw, kThreads);   // bitmap words per thread
+  const int wb = min(tid * wpt, nw);
+  const int we = min(wb + wpt, nw);
+  int mine = 0;
+  for (int w = wb; w < we; ++w) {
+    uint64_t any = 0ull;
+#pragma unroll
+    for (int h = 0; h < G; ++h) any |= bits[static_cast<size_t>(h) * P.nwords + w];
+    mine += __popcll(any);
+  }
+  const uint32_t incl = wave_scan_incl(static_cast<uint32_t>(mine));
+  if (lane == kWave - 1) wave_total[wave] = static_cast<int>(incl);
+  __syncthreads();
+  int before = static_cast<int>(incl) - mine;
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    before += w < wave ? wave_total[w] : 0;
+    total += wave_total[w];
+  }
+  int at = nsink + before;
+  for (int w = wb; w < we; ++w) {
+    uint64_t hb[G];
+    uint64_t any = 0ull;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      hb[h] = bits[static_cast<size_t>(h) * P.nwords + w];
+      any |= hb[h];
+    }
+    while (any) {
+      const int j = __ffsll(static_cast<unsigned long long>(any)) - 1;
+      any &= any - 1ull;
+      int heads = 0;
+#pragma unroll
+      for (int h = 0; h < G; ++h) heads |= static_cast<int>((hb[h] >> j) & 1ull) << h;
+      list[at++] = (cr.lo + w * kWave + j) | (heads << 20);
+    }
+  }
+  for (int i = tid; i < nsink; i += kThreads) list[i] = i | (kAll << 20);
+  const int nwin = T - w0;
+  for (int i = tid; i < nwin; i += kThreads) list[nsink + total + i] = (w0 + i) | (kAll << 20);
+  if (tid == 0) P.ucount[pair] = nsink + total + nwin;
+}
+
+// Split-K exact attention over a pair's token list (token-level variant):
+// split s takes a contiguous run of the list.  D/8 lanes share a token (8
+// channels of its key and value row each, gathered through the block
+// table); a wavefront takes 64 / (D/8) tokens at a time, U deep, and every
+// token group keeps its own running maximum, sums and first-order sums per
+// head.  The groups are combined inside the wavefront (lane swaps), the
+// wavefronts through LDS, and the split's partial is written in the layout
+// the merge reads.  Subtraction sums take only the tokens the state holds
+// (complete blocks).
+template <typename KV, int D, int G>
+__global__ __launch_bounds__(kThreads) void k_token_attend(DecodeParams P) {
+  constexpr int LPT = D / 8;            // lanes per token
+  constexpr int TPW = kWave / LPT;      // tokens per wavefront at a time
+  constexpr int NW = kThreads / kWave;
+  constexpr int U = 4;                  // tokens in flight per token group
+  __shared__ float red[NW][G][2][D];
+  __shared__ float wst[NW][G][3];
+  const int pair = blockIdx.x / P.max_split;
+  const int split = blockIdx.x % P.max_split;
+  const int b = pair / P.Hkv;
+  const int g = pair % P.Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int tg = lane / LPT;
+  const int lig = lane % LPT;
+  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
+  const int Ts = T - T % P.B;           // tokens the linear state holds
+  const int count = min(P.ucount[pair], P.umax);
+  const int per = ceil_div(count, P.max_split);
+  const int e0 = min(split * per, count);
+  const int e1 = min(e0 + per, count);
+  const int32_t* list = P.tlist + static_cast<size_t>(pair) * P.umax;
+  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  const char* kp = reinterpret_cast<const char*>(P.k_pages);
+  const char* vp = reinterpret_cast<const char*>(P.v_pages);
+
+  QReg<KV> qr[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qr[h].load(reinterpret_cast<const char*>(P.q) + ((static_cast<size_t>(b) * P.Hq + g * G + h) * D + lig * 8) * KV::kBytes);
+  float m[G], l[G], ld[G], acc[G][8], lacc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegInf;
+    l[h] = ld[h] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[h][j] = lacc[h][j] = 0.f;
+  }
+
+  constexpr int STEP = NW * TPW * U;    // list entries per workgroup iteration
+  const int niter = ceil_div(e1 - e0, STEP);
+  for (int it = 0; it < niter; ++it) {
+    int tok[U], heads[U];
+    Row8<KV> kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + it * STEP + (u * NW + wave) * TPW + tg;
+      const bool live = e < e1;
+      const int ent = list[live ? e : e0];
+      tok[u] = ent & 0xFFFFF;
+      heads[u] = live ? (ent >> 20) : 0;
+      const size_t page = static_cast<size_t>(bt[tok[u] / P.B]);
+      const size_t off = (((page * P.Hkv + g) * P.B + tok[u] % P.B) * D + lig * 8) * KV::kBytes;
+      kr[u].load(kp + off);
+      vr[u].load(vp + off);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[8];
+      vr[u].to_f32(vf);
+      const bool held = tok[u] < Ts;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float s = P.sigma * reduce_sum_lanes<LPT>(qr[h].dot(kr[u]));
+        if ((heads[u] >> h) & 1) {
+          const float mn = fmaxf(m[h], s);
+          const float c = m[h] == kNegInf ? 0.f : __expf(m[h] - mn);
+          const float pv = __expf(s - mn);
+          l[h] = fmaf(l[h], c, pv);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(acc[h][j], c, pv * vf[j]);
+          m[h] = mn;
+          if (held) {
+            const float w = 1.f + s;
+            ld[h] += w;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) lacc[h][j] = fmaf(w, vf[j], lacc[h][j]);
+          }
+        }
+      }
+    }
+  }
+
+  // token groups of the wavefront: common maximum, rescale, sum
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float M = m[h];
+    if constexpr (LPT <= 8) M = fmaxf(M, __shfl_xor(M, 8));
+    if constexpr (LPT <= 16) M = fmaxf(M, __shfl_xor(M, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float f = m[h] == kNegInf ? 0.f : __expf(m[h] - M);
+    l[h] *= f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[h][j] *= f;
+    auto gsum = [&](float x) {
+      if constexpr (LPT <= 8) x = pair_sum<8>(x);
+      if constexpr (LPT <= 16) x = pair_sum<16>(x);
+      return pair_sum<32>(x);
+    };
+    l[h] = gsum(l[h]);
+    ld[h] = gsum(ld[h]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[h][j] = gsum(acc[h][j]);
+      lacc[h][j] = gsum(lacc[h][j]);
+    }
+    m[h] = M;
+    if (tg == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        red[wave][h][0][lig * 8 + j] = acc[h][j];
+        red[wave][h][1][lig * 8 + j] = lacc[h][j];
+      }
+    }
+    if (lane == 0) {
+      wst[wave][h][0] = M;
+      wst[wave][h][1] = l[h];
+      wst[wave][h][2] = ld[h];
+    }
+  }
+  __syncthreads();
+  float* outp = P.part + (static_cast<size_t>(pair) * P.max_split + split) * G * P.pstride;
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int h = idx / D;
+    const int c = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wst[w][h][0]);
+    float a = 0.f, la = 0.f, lsum = 0.f, lw = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = wst[w][h][0];
+      const float e = mw == kNegInf ? 0.f : __expf(mw - M);
+      a = fmaf(e, red[w][h][0][c], a);
+      lsum = fmaf(e, wst[w][h][1], lsum);
+      la += red[w][h][1][c];
+      lw += wst[w][h][2];
+    }
+    float* o = outp + static_cast<size_t>(h) * P.pstride;
+    o[4 + c] = a;
+    o[4 + D + c] = la;
+    if (c == 0) {
+      o[0] = M;
+      o[1] = lsum;
+      o[2] = lw;
+      o[3] = 0.f;
+    }
+  }
+}
+
+// The token-level variant after the scoring launch: per-head selection over
+// the candidate tokens, the pairs' exact token lists, attention over them,
+// merge.
+template <typename KV, int D, int G>
+hipError_t launch_tokens(const Problem& p, const DecodeLayout& L, const DecodeParams& P, hipStream_t stream,
+                         RecordFn rec, void* ctx, int ev) {
+  const int pairs = p.batch * p.Hkv;
+  if (rec) rec(ctx, ev++, "select");
+  {
+    const dim3 grid(p.batch * p.Hq);
+    if (p.nc_max <= 4 * kWave)
+      hipLaunchKernelGGL((k_select<4>), grid, dim3(kWave), 0, stream, P);
+    else if (p.nc_max <= 8 * kWave)
+      hipLaunchKernelGGL((k_select<8>), grid, dim3(kWave), 0, stream, P);
+    else if (p.nc_max <= 16 * kWave)
+      hipLaunchKernelGGL((k_select<16>), grid, dim3(kWave), 0, stream, P);
+    else if (p.nc_max <= 32 * kWave)
+      hipLaunchKernelGGL((k_select<32>), grid, dim3(kWave), 0, stream, P);
+    else
+      hipLaunchKernelGGL((k_select<0>), grid, dim3(kWave), 0, stream, P);
+    hipError_t e = launch_status("k_select");
+    if (e != hipSuccess) return e;
+  }
+  if (rec) rec(ctx, ev++, "token_union");
+  hipLaunchKernelGGL((k_token_union<G>), dim3(pairs), dim3(kThreads), 0, stream, P);
+  hipError_t e = launch_status("k_token_union");
+  if (e != hipSuccess) return e;
+  if (rec) rec(ctx, ev++, "attend");
+  hipLaunchKernelGGL((k_token_attend<KV, D, G>), dim3(pairs * L.max_split), dim3(kThreads), 0, stream, P);
+  e = launch_status("k_token_attend");
+  if (e != hipSuccess) return e;
+  if (rec) rec(ctx, ev++, "merge");
+  hipLaunchKernelGGL((k_merge<D, G>), dim3(p.batch * p.Hq), dim3(kThreads), 0, stream, P);
+  e = launch_status("k_merge");
+  if (e != hipSuccess) return e;
+  if (rec) rec(ctx, ev, nullptr);
+  return hipSuccess;
 }
 
 template <typename KV, int D, int G>
@@ -1958,6 +2284,10 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
     hipLaunchKernelGGL((k_score_readout<KV, D, G>), grid, dim3(kThreads), 0, stream, P);
     hipError_t e = launch_status("k_score_readout");
     if (e != hipSuccess) return e;
+  }
+  if (p.tokens) {
+    if constexpr (G <= 4) return launch_tokens<KV, D, G>(p, L, P, stream, rec, ctx, ev);
+    return hipErrorInvalidValue;
   }
   if (L.fused_sel) {
     // selection runs in the attention prologue
@@ -2053,13 +2383,18 @@ DecodeLayout decode_layout(const Problem& p) {
   const long sel_blocks = std::min<long>(static_cast<long>(p.grouped ? 1 : p.G) * p.top_k, p.nc_max);
   const long bound = static_cast<long>(sink_blocks) + sel_blocks + 2 + p.W / p.B + 1;
   L.umax = static_cast<int>(std::max<long>(1, std::min<long>(bound, p.nblk_max)));
+  if (p.tokens)   // the exact token list: sinks, the heads' selected tokens, the window
+    L.umax = static_cast<int>(std::min<long>(static_cast<long>(p.ns) + std::min<long>(static_cast<long>(p.G) * p.top_k,
+                                                                                     p.nc_max) + p.W + 1,
+                                             static_cast<long>(p.max_seq_len) + 1));
   // Dynamic attention (bf16 path): the pair's workgroups share its union
   // list, which the prologue keeps whole in LDS.
-  L.fused_sel = (!p.grouped && p.nc_max <= kFusedKplMax * kWave) ? 1 : 0;
+  L.fused_sel = (!p.grouped && !p.tokens && p.nc_max <= kFusedKplMax * kWave) ? 1 : 0;
   // with the selection fused, the scoring kernel zeroes the work counters,
   // so the dynamic split needs that launch
   const bool scores_launched = (p.nc_max > 0) || p.linear_tail;
-  L.dyn = (p.bf16 && !p.deterministic && L.umax <= kMaxDynList && (!L.fused_sel || scores_launched)) ? 1 : 0;
+  L.dyn = (p.bf16 && !p.tokens && !p.deterministic && L.umax <= kMaxDynList && (!L.fused_sel || scores_launched))
+              ? 1 : 0;
   {
     const int want = std::max(1, (kAttendWgsTarget + pairs / 2) / pairs);
     if (L.dyn) {
@@ -2071,8 +2406,13 @@ DecodeLayout decode_layout(const Problem& p) {
       L.max_split = ceil_div(L.umax, L.bps);
     }
   }
+  if (p.tokens) {   // about kTokensPerSplit list entries per attention workgroup, at least want
+    const int want = std::max(1, (kAttendWgsTarget + pairs / 2) / pairs);
+    L.max_split = std::max(want, ceil_div(L.umax, kTokensPerSplit));
+    L.bps = ceil_div(L.umax, L.max_split);
+  }
   // bf16 attention with few splits per pair: its last workgroup merges
-  L.fused_merge = (p.bf16 && L.max_split <= kFusedMergeSplits) ? 1 : 0;
+  L.fused_merge = (p.bf16 && !p.tokens && L.max_split <= kFusedMergeSplits) ? 1 : 0;
   L.pstride = 2 * p.D + 4;
   L.sstride = std::max(4, (p.nc_max + 3) / 4 * 4);
   L.nwords = std::max(1, (p.nc_max + 63) / 64);
@@ -2107,6 +2447,8 @@ DecodeLayout decode_layout(const Problem& p) {
   off = align_up(off + sizeof(int32_t) * static_cast<size_t>(pairs) * kCtrStride);
   L.off_part = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(pairs) * L.max_split * p.G * L.pstride);
+  L.off_tlist = off;
+  off = align_up(off + (p.tokens ? sizeof(int32_t) * static_cast<size_t>(pairs) * L.umax : 0));
   L.total = off;
   return L;
 }
@@ -2135,6 +2477,9 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.dyn = L.dyn;
   P.fused_sel = L.fused_sel;
   P.fused_merge = L.fused_merge;
+  P.tokens = p.tokens;
+  P.bsel = p.tokens ? 1 : p.B;
+  P.tlist = reinterpret_cast<int32_t*>(a.ws + L.off_tlist);
   P.part = reinterpret_cast<float*>(a.ws + L.off_part);
   P.Hq = p.Hq;
   P.Hkv = p.Hkv;

@@ -22,7 +22,8 @@ hsla_status resolve(const hsla_config* cfg, int32_t batch, int32_t max_seq_len,
     return HSLA_ERR_INVALID_ARG;
   if (cfg->top_k < 0 || cfg->num_sink < 0 || cfg->window < 1) return HSLA_ERR_INVALID_ARG;
   if (cfg->linear_tail != 0 && cfg->linear_tail != 1) return HSLA_ERR_INVALID_ARG;
-  if (cfg->selection != HSLA_SEL_PER_HEAD && cfg->selection != HSLA_SEL_GROUPED) return HSLA_ERR_INVALID_ARG;
+  if (cfg->selection != HSLA_SEL_PER_HEAD && cfg->selection != HSLA_SEL_GROUPED && cfg->selection != HSLA_SEL_TOKEN)
+    return HSLA_ERR_INVALID_ARG;
   if (cfg->deterministic != 0 && cfg->deterministic != 1) return HSLA_ERR_INVALID_ARG;
   if (!(cfg->scale >= 0.0f) || !isfinite(cfg->scale)) return HSLA_ERR_INVALID_ARG;
   if (batch < 1 || max_seq_len < 1) return HSLA_ERR_INVALID_ARG;
@@ -47,6 +48,7 @@ hsla_status resolve(const hsla_config* cfg, int32_t batch, int32_t max_seq_len,
   p.W = cfg->window;
   p.linear_tail = cfg->linear_tail;
   p.grouped = cfg->selection == HSLA_SEL_GROUPED ? 1 : 0;
+  p.tokens = cfg->selection == HSLA_SEL_TOKEN ? 1 : 0;
   p.deterministic = cfg->deterministic;
   p.bf16 = cfg->kv_dtype == HSLA_BF16;
   p.sigma = cfg->scale > 0.0f ? cfg->scale : 1.0f / sqrtf(static_cast<float>(cfg->head_dim));
@@ -54,10 +56,17 @@ hsla_status resolve(const hsla_config* cfg, int32_t batch, int32_t max_seq_len,
   p.max_seq_len = max_seq_len;
   p.max_blocks = max_blocks;
   p.nblk_max = static_cast<int>(nblk);
-  p.nc_max = hsla::candidate_range(max_seq_len, B, p.ns, p.W).count;
-  // Per-head selection bitmaps of an attention workgroup live in LDS.
-  const size_t bitmap = static_cast<size_t>(G) * ((p.nc_max + 63) / 64) * 8;
-  if (bitmap > 16 * 1024) return HSLA_ERR_UNSUPPORTED;
+  if (p.tokens) {
+    // token indices share a 32-bit list entry with the heads' mask; the
+    // attention kernel keeps up to four heads' sums in registers
+    if (max_seq_len >= (1 << 20) || G > 4) return HSLA_ERR_UNSUPPORTED;
+    p.nc_max = hsla::candidate_range(max_seq_len, 1, p.ns, p.W).count;
+  } else {
+    p.nc_max = hsla::candidate_range(max_seq_len, B, p.ns, p.W).count;
+    // Per-head selection bitmaps of an attention workgroup live in LDS.
+    const size_t bitmap = static_cast<size_t>(G) * ((p.nc_max + 63) / 64) * 8;
+    if (bitmap > 16 * 1024) return HSLA_ERR_UNSUPPORTED;
+  }
   *out = p;
   return HSLA_OK;
 }

@@ -23,6 +23,7 @@ struct Problem {
   int Hq, Hkv, G, D, B, top_k, ns, W, linear_tail, bf16;
   int grouped;     // one selection per kv head (HSLA_SEL_GROUPED)
   int deterministic;  // static split-K attention (bitwise reproducible)
+  int tokens;      // token-level variant (HSLA_SEL_TOKEN): candidates are single tokens
   float sigma;
   int batch, max_seq_len;
   int max_blocks;  // block table row stride
@@ -58,7 +59,7 @@ struct DecodeLayout {
   int fused_sel;       // per-head selection in the attention prologue
   int fused_merge;     // the last attention workgroup of a pair merges (no merge kernel)
   SelLayout sl;
-  size_t off_scores, off_ro, off_roz, off_bits, off_ucount, off_ctr, off_part, total;
+  size_t off_scores, off_ro, off_roz, off_bits, off_ucount, off_ctr, off_part, off_tlist, total;
 };
 DecodeLayout decode_layout(const Problem& p);
 

@@ -11,7 +11,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (HSLA_BF16, HSLA_F32, HSLA_SEL_GROUPED, HSLA_SEL_PER_HEAD, Config, Pool, State, hsla_append_decode,
+from . import (HSLA_BF16, HSLA_F32, HSLA_SEL_GROUPED, HSLA_SEL_PER_HEAD, HSLA_SEL_TOKEN, Config, Pool, State,
+               hsla_append_decode,
                hsla_append_token, hsla_build_state, hsla_build_workspace_size, hsla_decode,
                hsla_decode_workspace_size)
 
@@ -114,10 +115,11 @@ class DeviceCache:
 
 
 def config_for(num_q_heads, num_kv_heads, head_dim, block_size, top_k, num_sink, window, linear_tail,
-               kv_dtype: str, scale: float = 0.0, grouped: int = 0, deterministic: int = 0) -> Config:
+               kv_dtype: str, scale: float = 0.0, grouped: int = 0, deterministic: int = 0,
+               tokens: int = 0) -> Config:
+    sel = HSLA_SEL_TOKEN if tokens else (HSLA_SEL_GROUPED if grouped else HSLA_SEL_PER_HEAD)
     return Config(num_q_heads, num_kv_heads, head_dim, block_size, top_k, num_sink, window, linear_tail,
-                  HSLA_BF16 if kv_dtype == "bf16" else HSLA_F32, scale,
-                  HSLA_SEL_GROUPED if grouped else HSLA_SEL_PER_HEAD, int(deterministic))
+                  HSLA_BF16 if kv_dtype == "bf16" else HSLA_F32, scale, sel, int(deterministic))
 
 
 class PreparedDecodeStep:

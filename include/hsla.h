@@ -87,8 +87,19 @@ typedef enum hsla_dtype { HSLA_F32 = 0, HSLA_BF16 = 1 } hsla_dtype;
  *   softmax over its candidates, the G softmaxes are summed per block, and
  *   the top_k blocks by that sum (lower index first on ties) are the
  *   selection of every head of the group.  With G = 1 it equals
- *   HSLA_SEL_PER_HEAD. */
-typedef enum hsla_selection { HSLA_SEL_PER_HEAD = 0, HSLA_SEL_GROUPED = 1 } hsla_selection;
+ *   HSLA_SEL_PER_HEAD.
+ * HSLA_SEL_TOKEN: token-level variant ["SALS: Sparse Attention in Latent
+ *   Space for KV Cache Compression", Approach; here on the plain keys, with
+ *   no latent projection]: the candidates are the tokens of
+ *   [num_sink, T - window), a token's score is sigma q.k_t, each query head
+ *   keeps its top_k tokens (score descending, lower index first), and
+ *   sel_idx receives token indices.  Sinks, window, the linear tail and the
+ *   merge are unchanged.  Supported for G <= 4 and max_seq_len < 2^20. */
+typedef enum hsla_selection {
+  HSLA_SEL_PER_HEAD = 0,
+  HSLA_SEL_GROUPED = 1,
+  HSLA_SEL_TOKEN = 2
+} hsla_selection;
 
 /* The problem statement's parameters.
  * num_q_heads, num_kv_heads: GQA heads; num_q_heads / num_kv_heads must be

@@ -127,6 +127,12 @@ def test_decode_rejects_bad_pointers_and_sizes():
     assert call_decode(big, max_len=262208 + 16, p=pool(max_blocks_per_seq=1 << 15)) == H.HSLA_ERR_UNSUPPORTED
     assert H.hsla_decode_workspace_size(big, 1, 262208 + 16) == 0
     assert H.hsla_decode_workspace_size(big, 1, 262208) > 0
+    # token-level variant: up to four query heads per kv head, lengths below 2^20
+    assert call_decode(cfg(selection=H.HSLA_SEL_TOKEN, num_q_heads=64)) == H.HSLA_ERR_UNSUPPORTED
+    assert call_decode(cfg(selection=H.HSLA_SEL_TOKEN), max_len=1 << 20,
+                       p=pool(max_blocks_per_seq=1 << 15)) == H.HSLA_ERR_UNSUPPORTED
+    assert H.hsla_decode_workspace_size(cfg(selection=H.HSLA_SEL_TOKEN), 8, 32768) > 0
+    assert call_decode(cfg(selection=3)) == H.HSLA_ERR_INVALID_ARG
 
 
 def test_append_rejects_aliased_lengths():

@@ -33,6 +33,7 @@ CASES = {
     "grouped": dict(grouped=1, seq_lens=(1471, 1203)),
     "block16": dict(block_size=16, window=64, top_k=12, seq_lens=(1471, 1202)),
     "no_candidates": dict(seq_lens=(200, 37)),
+    "token_level": dict(tokens=1, top_k=40, seq_lens=(1471, 1203)),
 }
 
 

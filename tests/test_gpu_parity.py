@@ -34,12 +34,12 @@ def _announce(wl, extra=""):
 def cfg_of(wl):
     return config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
                       wl.window, wl.linear_tail, wl.kv_dtype, wl.scale, grouped=wl.grouped,
-                      deterministic=wl.deterministic)
+                      deterministic=wl.deterministic, tokens=wl.tokens)
 
 
 def params_of(wl):
     return O.Params(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
-                    wl.window, wl.linear_tail, wl.scale, grouped=wl.grouped)
+                    wl.window, wl.linear_tail, wl.scale, grouped=wl.grouped, tokens=wl.tokens)
 
 
 def run_gpu(wl, inp, capacity_len=None):
@@ -458,3 +458,31 @@ def test_merge_in_last_workgroup(deterministic):
             for b in range(wl.batch):
                 for h in range(wl.num_q_heads):
                     assert row_rel_err(o[b, h], ref_o[b, h]) < 1e-5, (it, b, h)
+
+
+# ----------------------------------------------------------------------------
+# Token-level variant: top_k single tokens per head, scored by their keys
+# ----------------------------------------------------------------------------
+
+TOKEN_CASES = [
+    ("bf16_g4", dict(top_k=64, window=512, seq_lens=(4133, 3001))),
+    ("bf16_g4_k300", dict(top_k=300, window=256, seq_lens=(2900, 2311), deterministic=1)),
+    ("f32_d64", dict(kv_dtype=W.F32, head_dim=64, top_k=40, seq_lens=(1500, 1203))),
+    ("g1", dict(num_q_heads=2, num_kv_heads=2, top_k=33, seq_lens=(1500, 977))),
+    ("g2_b16", dict(num_q_heads=4, num_kv_heads=2, block_size=16, window=64, top_k=50, seq_lens=(1313, 700))),
+    ("no_tail", dict(linear_tail=0, top_k=25, seq_lens=(1500, 1203))),
+    ("dense", dict(top_k=4000, seq_lens=(1500, 1203))),
+    ("short", dict(top_k=16, seq_lens=(200, 37))),
+    ("batch4", dict(batch=4, top_k=128, seq_lens=(2000, 1999, 1024, 3000))),
+]
+
+
+@pytest.mark.parametrize("case", TOKEN_CASES, ids=lambda c: c[0])
+def test_token_level_selection(case):
+    name, over = case
+    wl = _wl("tokens_" + name, 95 + TOKEN_CASES.index(case), tokens=1, **over)
+    _announce(wl)
+    inp = W.make_inputs(wl)
+    dc, out, sel = run_gpu(wl, inp)
+    worst, flips = check_case(wl, inp, dc, out, sel, check_build=False)
+    print(f"  worst row error {worst:.3e}, near-tie flips {flips}")

@@ -60,6 +60,7 @@ class Workload:
     layer: int = 0
     grouped: int = 0              # one block selection per kv head
     deterministic: int = 0        # fixed split of the attention work (bitwise reproducible)
+    tokens: int = 0               # token-level variant: top_k counts single tokens
 
     @property
     def group(self) -> int:
