@@ -54,6 +54,9 @@ def parse(argv=None):
                     help="fixed split of the attention work (bitwise reproducible) instead of the dynamic one")
     ap.add_argument("--grouped", action="store_true",
                     help="the grouped-selection variant (one block selection per kv head)")
+    ap.add_argument("--tokens", action="store_true",
+                    help="the token-level variant: top_k single tokens per head (top_k x block size of the "
+                         "workload's block budget), scored by their keys")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-run", action="store_true",
@@ -72,14 +75,16 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
-def workload(name, grouped=False):
+def workload(name, grouped=False, tokens=False):
     import workloads as W
     wl = {"llama8b_32k": W.llama8b_32k, "needle_128k": W.needle_128k, "ragged_paged": W.ragged_paged}[name]()
+    if tokens:   # the same number of selected tokens as the block budget
+        return W.dataclasses.replace(wl, tokens=1, top_k=wl.top_k * wl.block_size)
     return W.dataclasses.replace(wl, grouped=1) if grouped else wl
 
 
 def traffic_key(wl):
-    return wl.name + ("+grouped" if wl.grouped else "")
+    return wl.name + ("+grouped" if wl.grouped else "") + ("+tokens" if wl.tokens else "")
 
 
 class Hip:
@@ -109,14 +114,16 @@ class Hip:
 
 
 def n_cand(T, wl):
-    lo = wl.num_sink // wl.block_size
+    """Candidate blocks (or tokens, for the token-level variant) at length T."""
+    B = 1 if wl.tokens else wl.block_size
+    lo = wl.num_sink // B
     hi = T - wl.window
-    return 0 if hi <= wl.num_sink else -(-hi // wl.block_size) - lo
+    return 0 if hi <= wl.num_sink else -(-hi // B) - lo
 
 
 def union_tokens(T, wl, sel_rows):
     """Tokens of sinks U window U every selected block of the group's heads."""
-    B = wl.block_size
+    B = 1 if wl.tokens else wl.block_size   # token-level rows hold token indices
     mask = np.zeros(T, bool)
     mask[:min(wl.num_sink, T)] = True
     mask[max(0, T - wl.window):] = True
@@ -135,7 +142,8 @@ def step_bytes(wl, lens, sel):
     for b in range(wl.batch):
         T = int(lens[b])
         for g in range(wl.num_kv_heads):
-            stats += n_cand(T, wl) * 2 * d * 4
+            # candidate statistics, or every candidate token's key for the token-level variant
+            stats += n_cand(T, wl) * (d * e if wl.tokens else 2 * d * 4)
             state += (d * d + 2 * d) * 4 if wl.linear_tail else 0
             rows = sel[b, g * G:(g + 1) * G] if sel is not None else []
             kv += union_tokens(T, wl, rows) * 2 * d * e
@@ -278,7 +286,7 @@ def traffic_collect(fetch_csv, write_csv):
             raise SystemExit(f"{path}: no copy or attention dispatches for {counter}")
         scales[counter] = COPY_BYTES / (max(copy) * 1024.0)
         per[counter] = float(np.mean(attend)) * 1024.0 * scales[counter]
-    name = traffic_key(workload(parse_known_workload(), "--grouped" in sys.argv))
+    name = traffic_key(workload(parse_known_workload(), "--grouped" in sys.argv, "--tokens" in sys.argv))
     try:
         out = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -347,7 +355,7 @@ def cpu_baseline(wl, inp_q, gpu_out, gpu_sel, budget_s):
     except Exception:  # pragma: no cover
         threads = 1
     p = O.Params(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
-                 wl.window, wl.linear_tail, wl.scale, grouped=wl.grouped)
+                 wl.window, wl.linear_tail, wl.scale, grouped=wl.grouped, tokens=wl.tokens)
     heads_done, t_heads, worst = 0, 0.0, 0.0
     t_start = time.perf_counter()
     for b in range(wl.batch):
@@ -443,7 +451,7 @@ def setup(args, extra_steps):
     from hybrid_sparse_linear_block_amd.device import DeviceCache, PreparedDecodeStep, config_for, to_device
 
     torch.cuda.set_device(0)
-    wl = workload(args.workload, args.grouped)
+    wl = workload(args.workload, args.grouped, args.tokens)
     steps, warm, R = args.steps, args.warmup, max(1, args.replicas)
     appends_per_replica = -(-(extra_steps + warm) // R) + 1
     wl = W.dataclasses.replace(wl, append_room=1 + -(-appends_per_replica // wl.block_size))
@@ -452,7 +460,7 @@ def setup(args, extra_steps):
     t_gen = time.perf_counter() - t0
     print(f"[bench] {wl.name}: inputs generated in {t_gen:.1f}s", file=sys.stderr, flush=True)
     cfg = config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
-                     wl.window, wl.linear_tail, wl.kv_dtype, grouped=wl.grouped,
+                     wl.window, wl.linear_tail, wl.kv_dtype, grouped=wl.grouped, tokens=wl.tokens,
                      deterministic=int(args.deterministic))
     cap = max(wl.seq_lens) + appends_per_replica + 1
     hip = Hip()
@@ -755,6 +763,14 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(avg["attend"] / (attend_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "bytes_per_launch": int(avg["attend"]), "us_per_launch": round(attend_us, 2)}
+    first = "append_score_readout" if "append_score_readout" in per_kernel else "score_readout"
+    if wl.tokens and per_kernel.get(first, 0.0) > attend_us:
+        # the token-level variant reads every candidate token's key in the scoring kernel
+        sr_us = per_kernel[first]
+        roofline = {"bound": "hbm", "kernel": "k_score_readout", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "achieved": round(avg["score_readout"] / (sr_us * 1e-6) / 1e9, 1),
+                    "frac": round(avg["score_readout"] / (sr_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "traffic": None, "bytes_per_launch": int(avg["score_readout"]), "us_per_launch": round(sr_us, 2)}
     step_bytes_total = avg["decode"] + app_b
     res = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
@@ -763,7 +779,7 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "ctx": int(max(wl.seq_lens)), "q_heads": wl.num_q_heads,
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block": wl.block_size,
                    "top_k": wl.top_k, "sinks": wl.num_sink, "window": wl.window, "replicas": R,
-                   "selection": "grouped" if wl.grouped else "per_head",
+                   "selection": "tokens" if wl.tokens else ("grouped" if wl.grouped else "per_head"),
                    "attention_split": "fixed" if args.deterministic else "dynamic",
                    "step": STEP_SEPARATE if args.separate_append else STEP_FUSED},
         "us_per_step": round(ms_per_step * 1e3, 2),

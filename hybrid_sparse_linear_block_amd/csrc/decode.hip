@@ -57,6 +57,7 @@ constexpr int kDoneSlot = 16;        // a pair's count of finished attention wor
 // workgroups of its own (one split per pair for large batches).
 constexpr int kFusedMergeSplits = 2;
 constexpr int kTokensPerSplit = 256;  // token-level variant: list entries per attention workgroup
+constexpr int kTokenChunk = 256;      // token-level variant: candidate tokens per scoring workgroup
 constexpr int kUnitSlices = 4;       // slices per dynamically claimed unit
 constexpr int kMaxDynList = 2048;    // union entries a dynamic attention workgroup holds in LDS
 constexpr int kDeadT0 = 1 << 30;     // first token of a slice whose rows are all invalid
@@ -271,7 +272,7 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
 // append's part runs.
 // Token-level variant ("SALS: Sparse Attention in Latent Space for KV Cache
 // Compression", Approach, here on the plain keys): the scores sigma q.k_t of
-// 64 candidate tokens of one (sequence, kv head) for its G query heads, as
+// 256 candidate tokens of one (sequence, kv head) for its G query heads, as
 // order keys.  D/8 lanes share a token (8 channels each); a pass covers 256 /
 // (D/8) tokens, and every pass's page lookups and key rows are issued before
 // the first dot product.
@@ -279,9 +280,9 @@ template <typename KV, int D, int G>
 __device__ __forceinline__ void score_tokens_part(const DecodeParams& P, int b, int g, int chunk) {
   constexpr int LPT = D / 8;
   constexpr int TPP = kThreads / LPT;
-  constexpr int NIT = kScoreChunk / TPP;
-  static_assert(kScoreChunk % TPP == 0 && G <= LPT, "whole passes; one finishing lane per head");
-  const int c_begin = chunk * kScoreChunk;
+  constexpr int NIT = kTokenChunk / TPP;
+  static_assert(kTokenChunk % TPP == 0 && G <= LPT, "whole passes; one finishing lane per head");
+  const int c_begin = chunk * kTokenChunk;
   const int tid = threadIdx.x;
   const int lig = tid % LPT;
   const int slot = tid / LPT;
@@ -1998,6 +1999,190 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// Token-level variant: per-head top-k over the candidate tokens
+// ---------------------------------------------------------------------------
+// One workgroup of 1024 threads per (sequence, query head).  Rows hold tens
+// of thousands of keys, so the whole workgroup runs the radix select: three passes over
+// 11-, 11- and 10-bit digits, each streaming the row (16 keys per thread in
+// flight) into a 2048-bin LDS histogram of the keys that match the digits
+// found so far, and a suffix scan picks the digit that holds the k-th
+// largest key.  Then each
+// wavefront takes a sixteenth of the row's 64-key words: it counts its keys
+// above and equal to the threshold, the counts are exchanged, and a second
+// walk writes the bitmap words and the ascending indices (keys equal to the
+// threshold are taken lowest index first).
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_incl(uint32_t v, uint32_t* wtot) {
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const uint32_t incl = wave_scan_incl(v);
+  if (lane == kWave - 1) wtot[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) before += w < wave ? wtot[w] : 0u;
+  __syncthreads();
+  return incl + before;
+}
+
+constexpr int kSelThreads = 1024;   // token-level selection: threads per head
+
+__global__ __launch_bounds__(kSelThreads) void k_select_tokens(DecodeParams P) {
+  constexpr int NT = kSelThreads;
+  constexpr int NW = NT / kWave;
+  constexpr int UK = 16;            // keys in flight per thread
+  constexpr int NB = 2048;          // histogram bins (11-bit digits)
+  constexpr int BPT = NB / NT;      // bins per thread
+  __shared__ uint32_t hist[NB];
+  __shared__ uint32_t wtot[NW];
+  __shared__ int pick[2];
+  __shared__ int wcnt[NW][2];
+  const int bh = blockIdx.x;
+  const int b = bh / P.Hq;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const uint32_t* kh = P.keys + static_cast<size_t>(bh) * P.sstride;
+  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
+  const CandRange cr = candidate_range(T, 1, P.ns, P.W);
+  const int nc = min(cr.count, P.nc_max);
+  const int k = P.top_k;
+  const int nw = ceil_div(nc, kWave);
+  uint64_t* bits_row = P.bits + static_cast<size_t>(bh) * P.nwords;
+  int32_t* out = P.sel_idx ? P.sel_idx + static_cast<size_t>(bh) * k : nullptr;
+  const bool take_all = k >= nc;
+  const bool take_none = k <= 0 || nc == 0;
+
+  uint32_t thr = 0u;
+  int rem = k;   // keys equal to thr still to take, lowest indices first
+  if (!take_all && !take_none) {
+    uint32_t prefix = 0u, pmask = 0u;
+    // digits: bits 21..31, 10..20, 0..9
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+      const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) hist[tid * BPT + j] = 0u;
+      __syncthreads();
+      for (int i0 = 0; i0 < nc; i0 += NT * UK) {
+        uint32_t x[UK];
+#pragma unroll
+        for (int u = 0; u < UK; ++u) x[u] = kh[min(i0 + u * NT + tid, nc - 1)];
+#pragma unroll
+        for (int u = 0; u < UK; ++u)
+          if (i0 + u * NT + tid < nc && (x[u] & pmask) == prefix) atomicAdd(&hist[(x[u] >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      // thread tid holds the BPT bins counted from the top: digits
+      // NB-1 - (tid*BPT + j)
+      uint32_t cb[BPT];
+      uint32_t mine = 0u;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        cb[j] = hist[NB - 1 - (tid * BPT + j)];
+        mine += cb[j];
+      }
+      const uint32_t incl = block_scan_incl<NT>(mine, wtot);   // keys whose digit >= the thread's lowest
+      uint32_t above = incl - mine;
+      if (above < static_cast<uint32_t>(rem) && static_cast<uint32_t>(rem) <= incl) {
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+          if (above < static_cast<uint32_t>(rem) && static_cast<uint32_t>(rem) <= above + cb[j]) {
+            pick[0] = NB - 1 - (tid * BPT + j);
+            pick[1] = rem - static_cast<int>(above);
+          }
+          above += cb[j];
+        }
+      }
+      __syncthreads();
+      prefix |= static_cast<uint32_t>(pick[0]) << shift;
+      pmask |= dmask << shift;
+      rem = pick[1];
+      __syncthreads();
+    }
+    thr = prefix;
+  }
+
+  // an equal share of the words per wavefront, UK words in flight
+  const int wpw = ceil_div(nw, NW);
+  const int wb = min(wave * wpw, nw);
+  const int we = min(wb + wpw, nw);
+  auto masks = [&](int w, uint32_t x, uint64_t& gt, uint64_t& eq, uint64_t& valid) __attribute__((always_inline)) {
+    const bool v = w * kWave + lane < nc;
+    valid = __ballot(v);
+    gt = __ballot(v && x > thr);
+    eq = __ballot(v && x == thr);
+  };
+  int n_eq = 0, n_gt = 0;
+  for (int w0 = wb; w0 < we; w0 += UK) {
+    uint32_t x[UK];
+#pragma unroll
+    for (int u = 0; u < UK; ++u) x[u] = kh[min((w0 + u) * kWave + lane, max(nc - 1, 0))];
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+      if (w0 + u >= we) break;
+      uint64_t gt, eq, valid;
+      masks(w0 + u, x[u], gt, eq, valid);
+      n_eq += __popcll(eq);
+      n_gt += __popcll(gt);
+    }
+  }
+  if (lane == 0) {
+    wcnt[wave][0] = n_eq;
+    wcnt[wave][1] = n_gt;
+  }
+  __syncthreads();
+  int eq_before = 0, pos = 0, total = 0, eq_acc = 0;
+  for (int w = 0; w < NW; ++w) {   // keys each wavefront selects, in index order
+    const int e = wcnt[w][0];
+    const int taken = take_all ? e + wcnt[w][1] : take_none ? 0 : wcnt[w][1] + min(max(rem - eq_acc, 0), e);
+    if (w < wave) {
+      pos += taken;
+      eq_before += e;
+    }
+    total += taken;
+    eq_acc += e;
+  }
+  for (int w0 = wb; w0 < we; w0 += UK) {
+    uint32_t x[UK];
+#pragma unroll
+    for (int u = 0; u < UK; ++u) x[u] = kh[min((w0 + u) * kWave + lane, max(nc - 1, 0))];
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+      const int w = w0 + u;
+      if (w >= we) break;
+      uint64_t gt, eq, valid;
+      masks(w, x[u], gt, eq, valid);
+      uint64_t sm;
+      if (take_none) {
+        sm = 0ull;
+      } else if (take_all) {
+        sm = valid;
+      } else {
+        // equal keys of this word whose rank among all equal keys is < rem
+        uint64_t keep = 0ull, e = eq;
+        int r = eq_before;
+        while (e && r < rem) {
+          const uint64_t low = e & (~e + 1ull);
+          keep |= low;
+          e ^= low;
+          ++r;
+        }
+        eq_before += __popcll(eq);
+        sm = gt | keep;
+      }
+      if (lane == 0) bits_row[w] = sm;
+      const bool sel = (sm >> lane) & 1ull;
+      const int at = pos + __popcll(sm & lanes_below(lane));
+      if (sel && out && at < k) out[at] = cr.lo + w * kWave + lane;
+      pos += __popcll(sm);
+    }
+  }
+  if (out)   // padding after the selection
+    for (int j = total + tid; j < k; j += NT) out[j] = -1;
+}
+
+// ---------------------------------------------------------------------------
 // Token-level variant: exact token list and attention over it
 // ---------------------------------------------------------------------------
 // One workgroup per (sequence, kv head) lists the pair's exact tokens in
@@ -2238,17 +2423,15 @@ hipError_t launch_tokens(const Problem& p, const DecodeLayout& L, const DecodePa
   const int pairs = p.batch * p.Hkv;
   if (rec) rec(ctx, ev++, "select");
   {
+    // short rows: one wavefront per head with the keys in registers; long
+    // rows: the whole workgroup
     const dim3 grid(p.batch * p.Hq);
-    if (p.nc_max <= 4 * kWave)
-      hipLaunchKernelGGL((k_select<4>), grid, dim3(kWave), 0, stream, P);
-    else if (p.nc_max <= 8 * kWave)
+    if (p.nc_max <= 8 * kWave)
       hipLaunchKernelGGL((k_select<8>), grid, dim3(kWave), 0, stream, P);
-    else if (p.nc_max <= 16 * kWave)
-      hipLaunchKernelGGL((k_select<16>), grid, dim3(kWave), 0, stream, P);
     else if (p.nc_max <= 32 * kWave)
       hipLaunchKernelGGL((k_select<32>), grid, dim3(kWave), 0, stream, P);
     else
-      hipLaunchKernelGGL((k_select<0>), grid, dim3(kWave), 0, stream, P);
+      hipLaunchKernelGGL(k_select_tokens, grid, dim3(kSelThreads), 0, stream, P);
     hipError_t e = launch_status("k_select");
     if (e != hipSuccess) return e;
   }
@@ -2376,6 +2559,7 @@ DecodeLayout decode_layout(const Problem& p) {
   DecodeLayout L{};
   const int pairs = p.batch * p.Hkv;
   L.score_chunk = kScoreChunk;
+  if (p.tokens) L.score_chunk = kTokenChunk;
   L.score_wgs = p.nc_max > 0 ? ceil_div(p.nc_max, L.score_chunk) : 0;
   L.ro_rows = kRoRows;
   L.ro_wgs = p.linear_tail ? p.D / L.ro_rows : 0;

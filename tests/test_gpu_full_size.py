@@ -27,7 +27,9 @@ if not torch.cuda.is_available():  # collected on CPU hosts, skipped there
 from hybrid_sparse_linear_block_amd.device import DeviceCache, to_device  # noqa: E402
 
 FULL = {"llama8b_32k": W.llama8b_32k, "needle_128k": W.needle_128k, "ragged_paged": W.ragged_paged,
-        "llama8b_32k_grouped": lambda: W.dataclasses.replace(W.llama8b_32k(), grouped=1)}
+        "llama8b_32k_grouped": lambda: W.dataclasses.replace(W.llama8b_32k(), grouped=1),
+        # token-level variant with the block budget's token count (16 x 64)
+        "llama8b_32k_tokens": lambda: W.dataclasses.replace(W.llama8b_32k(), tokens=1, top_k=1024)}
 
 
 def run_full(wl, inp):
@@ -49,7 +51,7 @@ def sampled_pairs(wl):
 
 def check_properties(wl, out, sel):
     assert np.isfinite(out).all(), "non-finite outputs"
-    B, k = wl.block_size, wl.top_k
+    B, k = (1 if wl.tokens else wl.block_size), wl.top_k   # token-level rows hold token indices
     for b in range(wl.batch):
         T = int(wl.seq_lens[b])
         lo = wl.num_sink // B
