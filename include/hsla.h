@@ -107,7 +107,8 @@ typedef enum hsla_selection {
  * head_dim: 64 or 128.
  * block_size: tokens per block and per KV page: 16, 32, 64, 128 or 256
  *   [SPLA, "Page Attention and Selection": selection at page granularity].
- * top_k: selected blocks per query head, >= 0 [SPLA Abstract].
+ * top_k: selected blocks per query head (tokens with HSLA_SEL_TOKEN), >= 0
+ *   [SPLA Abstract].
  * num_sink: initial sink tokens, >= 0; window: sliding-window length
  *   including the current token, >= block_size [SALSA abstract].
  * linear_tail: 1 = residual linear attention over U [SPLA, "Residual Linear
@@ -231,7 +232,8 @@ size_t hsla_decode_workspace_size(const hsla_config* cfg, int32_t batch, int32_t
  *   statistics of every full block and the state must be up to date.
  * out: device [batch, Hq, head_dim] float32.
  * sel_idx: device [batch, Hq, top_k] int32 or NULL; receives each head's
- *   selected block indices in ascending order, padded with -1.
+ *   selected block indices (token indices with HSLA_SEL_TOKEN) in ascending
+ *   order, padded with -1.
  * workspace: device scratch of at least hsla_decode_workspace_size() bytes;
  *   contents on entry are ignored.
  * prof: optional timing hook (NULL for none). */
