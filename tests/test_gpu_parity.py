@@ -486,3 +486,27 @@ def test_token_level_selection(case):
     dc, out, sel = run_gpu(wl, inp)
     worst, flips = check_case(wl, inp, dc, out, sel, check_build=False)
     print(f"  worst row error {worst:.3e}, near-tie flips {flips}")
+
+
+@pytest.mark.parametrize("n", [1500, 2900])   # 1024-candidate register path and the workgroup radix path
+def test_token_level_exact_ties_go_to_the_lower_token(n):
+    """Tokens 40, 41, 700 and 900 hold copies of token 30's key, which is made
+    to score high for the first query head of each group: with k = 3 the
+    five-way tie at the top straddles the cut and must resolve to tokens 30,
+    40, 41."""
+    wl = _wl("token_ties", 110, batch=1, seq_lens=(n,), top_k=3, tokens=1, shuffle_pages=False)
+    _announce(wl)
+    inp = W.make_inputs(wl)
+    rng = np.random.default_rng(8)
+    for g in range(wl.num_kv_heads):
+        K, V = inp["pairs"][(0, g)]
+        qh = W.bf16_to_f32(inp["q"][0, g * wl.group])
+        qhat = qh / np.sqrt((qh.astype(np.float64) ** 2).sum())
+        K[30] = W.bf16_round(6.0 * qhat + 0.1 * rng.standard_normal(wl.head_dim))
+        for dst in (40, 41, 700, 900):
+            K[dst] = K[30]
+        W.scatter_pairs(wl, inp["block_table"], inp["k_pages"], 0, g, K)
+    dc, out, sel = run_gpu(wl, inp)
+    check_case(wl, inp, dc, out, sel, check_build=False)
+    for g in range(wl.num_kv_heads):
+        assert gpu_selection(sel[0, g * wl.group]) == [30, 40, 41]
