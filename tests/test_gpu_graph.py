@@ -28,7 +28,7 @@ from parity import row_rel_err  # noqa: E402
 REPLAYS = 3
 
 
-def _layer_set(layers, inps, cap):
+def _layer_set(layers, inps, cap, fused):
     preps = []
     for wl, inp in zip(layers, inps):
         dc = DeviceCache(cfg_of(wl), inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"],
@@ -37,7 +37,7 @@ def _layer_set(layers, inps, cap):
         k_tok, v_tok = (to_device(x) for x in W.gen_token(wl, 0))
         out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
         sel = torch.empty((wl.batch, wl.num_q_heads, wl.top_k), dtype=torch.int32, device="cuda")
-        preps.append(PreparedDecodeStep(dc, to_device(inp["q"]), k_tok, v_tok, out, sel))
+        preps.append(PreparedDecodeStep(dc, to_device(inp["q"]), k_tok, v_tok, out, sel, fused=fused))
     return preps
 
 
@@ -46,14 +46,18 @@ def _snapshot(preps):
     return [(p.keep[3].cpu().numpy().copy(), p.keep[4].cpu().numpy().copy()) for p in preps]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "append_decode"])
 @pytest.mark.parametrize("deterministic", [1, 0])
-def test_graph_replays_match_eager_steps(deterministic):
-    layers = [dataclasses.replace(wl, append_room=2, deterministic=deterministic) for wl in W.hybrid_small()]
-    _announce(layers[0], f"graph replays, {len(layers)} layers, deterministic={deterministic}")
+def test_graph_replays_match_eager_steps(deterministic, fused):
+    # 4157 tokens: the third step's token completes block 64, so the replays
+    # also fold a block into the state and write its statistics
+    layers = [dataclasses.replace(wl, append_room=2, deterministic=deterministic, seq_lens=(4157,))
+              for wl in W.hybrid_small()]
+    _announce(layers[0], f"graph replays, {len(layers)} layers, deterministic={deterministic}, fused={fused}")
     inps = [W.make_inputs(wl, keep_pairs=False) for wl in layers]
     steps = 2 * REPLAYS
     cap = int(max(layers[0].seq_lens)) + steps + 2
-    eager, graphed = _layer_set(layers, inps, cap), _layer_set(layers, inps, cap)
+    eager, graphed = _layer_set(layers, inps, cap, fused), _layer_set(layers, inps, cap, fused)
     for p in eager:   # the same length bound as the graph (the split of the work depends on it)
         p.bound = cap
 
