@@ -110,7 +110,7 @@ struct DecodeParams {
   int fused_merge;  // the last attention workgroup of a pair merges its splits (no merge kernel)
   int tokens;       // token-level variant: candidates are single tokens, scored by their keys
   int bsel;         // candidate granularity: the block size, or 1 for the token-level variant
-  int32_t* tlist;   // token-level variant: each pair's exact token list [pairs, umax] (token | heads << 20)
+  int32_t* tlist;   // token-level variant: each pair's exact token list [pairs, umax] x (token | heads << 20, page)
   SelLayout sl;
   DecodeAppend app;
   float sigma;
@@ -2026,6 +2026,7 @@ __device__ __forceinline__ uint32_t block_scan_incl(uint32_t v, uint32_t* wtot) 
 }
 
 constexpr int kSelThreads = 1024;   // token-level selection: threads per head
+constexpr int kUnionThreads = 1024; // token-level exact lists: threads per (sequence, kv head)
 
 __global__ __launch_bounds__(kSelThreads) void k_select_tokens(DecodeParams P) {
   constexpr int NT = kSelThreads;
@@ -2188,11 +2189,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select_tokens(DecodeParams P) {
 // One workgroup per (sequence, kv head) lists the pair's exact tokens in
 // ascending order: the sinks and the window for every head, and between them
 // every candidate token some head selected, with the mask of the heads that
-// selected it (token | heads << 20).  Each thread takes a contiguous run of
+// selected it and the token's page (token | heads << 20, page), so that the
+// attention kernel reaches the rows in one round trip.  Each thread takes a contiguous run of
 // bitmap words; a workgroup scan of their counts places the runs.
 template <int G>
-__global__ __launch_bounds__(kThreads) void k_token_union(DecodeParams P) {
-  __shared__ int wave_total[kThreads / kWave];
+__global__ __launch_bounds__(kUnionThreads) void k_token_union(DecodeParams P) {
+  constexpr int NT = kUnionThreads;
+  __shared__ int wave_total[NT / kWave];
   const int pair = blockIdx.x;
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
@@ -2206,10 +2209,11 @@ __global__ __launch_bounds__(kThreads) void k_token_union(DecodeParams P) {
   const int nsink = min(P.ns, T);
   const int w0 = max(T - P.W, nsink);   // first window token that is not a sink
   constexpr int kAll = (1 << G) - 1;
-  int32_t* list = P.tlist + static_cast<size_t>(pair) * P.umax;
+  int2* list = reinterpret_cast<int2*>(P.tlist) + static_cast<size_t>(pair) * P.umax;
+  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
   const uint64_t* bits = P.bits + (static_cast<size_t>(b) * P.Hq + g * G) * P.nwords;
 
-  const int wpt = ceil_div(nw, kThreads);   // bitmap words per thread
+  const int wpt = ceil_div(nw, NT);   // bitmap words per thread
   const int wb = min(tid * wpt, nw);
   const int we = min(wb + wpt, nw);
   int mine = 0;
@@ -2225,7 +2229,7 @@ __global__ __launch_bounds__(kThreads) void k_token_union(DecodeParams P) {
   int before = static_cast<int>(incl) - mine;
   int total = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / kWave; ++w) {
+  for (int w = 0; w < NT / kWave; ++w) {
     before += w < wave ? wave_total[w] : 0;
     total += wave_total[w];
   }
@@ -2238,18 +2242,29 @@ __global__ __launch_bounds__(kThreads) void k_token_union(DecodeParams P) {
       hb[h] = bits[static_cast<size_t>(h) * P.nwords + w];
       any |= hb[h];
     }
+    // the word's 64 tokens span at most 64 / B + 1 <= 5 blocks: their pages
+    // are read together, before the entries are written
+    const int blk0 = (cr.lo + w * kWave) / P.B;
+    const int blk1 = (cr.lo + min(w * kWave + kWave, nc) - 1) / P.B;   // the word's last candidate
+    int pg[5];
+#pragma unroll
+    for (int q = 0; q < 5; ++q) pg[q] = bt[min(blk0 + q, blk1)];
     while (any) {
       const int j = __ffsll(static_cast<unsigned long long>(any)) - 1;
       any &= any - 1ull;
       int heads = 0;
 #pragma unroll
       for (int h = 0; h < G; ++h) heads |= static_cast<int>((hb[h] >> j) & 1ull) << h;
-      list[at++] = (cr.lo + w * kWave + j) | (heads << 20);
+      const int t = cr.lo + w * kWave + j;
+      const int q = t / P.B - blk0;
+      const int page = q == 0 ? pg[0] : q == 1 ? pg[1] : q == 2 ? pg[2] : q == 3 ? pg[3] : pg[4];
+      list[at++] = make_int2(t | (heads << 20), page);
     }
   }
-  for (int i = tid; i < nsink; i += kThreads) list[i] = i | (kAll << 20);
+  for (int i = tid; i < nsink; i += NT) list[i] = make_int2(i | (kAll << 20), bt[i / P.B]);
   const int nwin = T - w0;
-  for (int i = tid; i < nwin; i += kThreads) list[nsink + total + i] = (w0 + i) | (kAll << 20);
+  for (int i = tid; i < nwin; i += NT)
+    list[nsink + total + i] = make_int2((w0 + i) | (kAll << 20), bt[(w0 + i) / P.B]);
   if (tid == 0) P.ucount[pair] = nsink + total + nwin;
 }
 
@@ -2285,8 +2300,7 @@ __global__ __launch_bounds__(kThreads) void k_token_attend(DecodeParams P) {
   const int per = ceil_div(count, P.max_split);
   const int e0 = min(split * per, count);
   const int e1 = min(e0 + per, count);
-  const int32_t* list = P.tlist + static_cast<size_t>(pair) * P.umax;
-  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  const int2* list = reinterpret_cast<const int2*>(P.tlist) + static_cast<size_t>(pair) * P.umax;
   const char* kp = reinterpret_cast<const char*>(P.k_pages);
   const char* vp = reinterpret_cast<const char*>(P.v_pages);
 
@@ -2305,21 +2319,30 @@ __global__ __launch_bounds__(kThreads) void k_token_attend(DecodeParams P) {
 
   constexpr int STEP = NW * TPW * U;    // list entries per workgroup iteration
   const int niter = ceil_div(e1 - e0, STEP);
+  // list entries of iteration it (dead ones repeat the first entry)
+  auto fetch_list = [&](int it, int2 (&en)[U]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + it * STEP + (u * NW + wave) * TPW + tg;
+      en[u] = list[e < e1 ? e : e0];
+      if (e >= e1) en[u].x &= 0xFFFFF;   // no heads
+    }
+  };
+  int2 nxt[U];
+  if (niter > 0) fetch_list(0, nxt);
   for (int it = 0; it < niter; ++it) {
     int tok[U], heads[U];
     Row8<KV> kr[U], vr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = e0 + it * STEP + (u * NW + wave) * TPW + tg;
-      const bool live = e < e1;
-      const int ent = list[live ? e : e0];
-      tok[u] = ent & 0xFFFFF;
-      heads[u] = live ? (ent >> 20) : 0;
-      const size_t page = static_cast<size_t>(bt[tok[u] / P.B]);
-      const size_t off = (((page * P.Hkv + g) * P.B + tok[u] % P.B) * D + lig * 8) * KV::kBytes;
+      tok[u] = nxt[u].x & 0xFFFFF;
+      heads[u] = nxt[u].x >> 20;
+      const size_t off = (((static_cast<size_t>(nxt[u].y) * P.Hkv + g) * P.B + tok[u] % P.B) * D + lig * 8) *
+                         KV::kBytes;
       kr[u].load(kp + off);
       vr[u].load(vp + off);
     }
+    if (it + 1 < niter) fetch_list(it + 1, nxt);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float vf[8];
@@ -2436,7 +2459,7 @@ hipError_t launch_tokens(const Problem& p, const DecodeLayout& L, const DecodePa
     if (e != hipSuccess) return e;
   }
   if (rec) rec(ctx, ev++, "token_union");
-  hipLaunchKernelGGL((k_token_union<G>), dim3(pairs), dim3(kThreads), 0, stream, P);
+  hipLaunchKernelGGL((k_token_union<G>), dim3(pairs), dim3(kUnionThreads), 0, stream, P);
   hipError_t e = launch_status("k_token_union");
   if (e != hipSuccess) return e;
   if (rec) rec(ctx, ev++, "attend");
@@ -2632,7 +2655,7 @@ DecodeLayout decode_layout(const Problem& p) {
   L.off_part = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(pairs) * L.max_split * p.G * L.pstride);
   L.off_tlist = off;
-  off = align_up(off + (p.tokens ? sizeof(int32_t) * static_cast<size_t>(pairs) * L.umax : 0));
+  off = align_up(off + (p.tokens ? 2 * sizeof(int32_t) * static_cast<size_t>(pairs) * L.umax : 0));
   L.total = off;
   return L;
 }
