@@ -2491,10 +2491,7 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
     hipError_t e = launch_status("k_score_readout");
     if (e != hipSuccess) return e;
   }
-  if (p.tokens) {
-    if constexpr (G <= 4) return launch_tokens<KV, D, G>(p, L, P, stream, rec, ctx, ev);
-    return hipErrorInvalidValue;
-  }
+  if (p.tokens) return launch_tokens<KV, D, G>(p, L, P, stream, rec, ctx, ev);
   if (L.fused_sel) {
     // selection runs in the attention prologue
   } else if (p.grouped) {

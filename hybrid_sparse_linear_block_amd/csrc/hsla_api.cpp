@@ -57,9 +57,8 @@ hsla_status resolve(const hsla_config* cfg, int32_t batch, int32_t max_seq_len,
   p.max_blocks = max_blocks;
   p.nblk_max = static_cast<int>(nblk);
   if (p.tokens) {
-    // token indices share a 32-bit list entry with the heads' mask; the
-    // attention kernel keeps up to four heads' sums in registers
-    if (max_seq_len >= (1 << 20) || G > 4) return HSLA_ERR_UNSUPPORTED;
+    // token indices share a 32-bit list entry with the heads' mask
+    if (max_seq_len >= (1 << 20)) return HSLA_ERR_UNSUPPORTED;
     p.nc_max = hsla::candidate_range(max_seq_len, 1, p.ns, p.W).count;
   } else {
     p.nc_max = hsla::candidate_range(max_seq_len, B, p.ns, p.W).count;

@@ -94,7 +94,7 @@ typedef enum hsla_dtype { HSLA_F32 = 0, HSLA_BF16 = 1 } hsla_dtype;
  *   [num_sink, T - window), a token's score is sigma q.k_t, each query head
  *   keeps its top_k tokens (score descending, lower index first), and
  *   sel_idx receives token indices.  Sinks, window, the linear tail and the
- *   merge are unchanged.  Supported for G <= 4 and max_seq_len < 2^20. */
+ *   merge are unchanged.  Supported for max_seq_len < 2^20. */
 typedef enum hsla_selection {
   HSLA_SEL_PER_HEAD = 0,
   HSLA_SEL_GROUPED = 1,

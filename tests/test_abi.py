@@ -127,8 +127,7 @@ def test_decode_rejects_bad_pointers_and_sizes():
     assert call_decode(big, max_len=262208 + 16, p=pool(max_blocks_per_seq=1 << 15)) == H.HSLA_ERR_UNSUPPORTED
     assert H.hsla_decode_workspace_size(big, 1, 262208 + 16) == 0
     assert H.hsla_decode_workspace_size(big, 1, 262208) > 0
-    # token-level variant: up to four query heads per kv head, lengths below 2^20
-    assert call_decode(cfg(selection=H.HSLA_SEL_TOKEN, num_q_heads=64)) == H.HSLA_ERR_UNSUPPORTED
+    # token-level variant: lengths below 2^20 (token index field of the list entries)
     assert call_decode(cfg(selection=H.HSLA_SEL_TOKEN), max_len=1 << 20,
                        p=pool(max_blocks_per_seq=1 << 15)) == H.HSLA_ERR_UNSUPPORTED
     assert H.hsla_decode_workspace_size(cfg(selection=H.HSLA_SEL_TOKEN), 8, 32768) > 0

@@ -470,6 +470,8 @@ TOKEN_CASES = [
     ("f32_d64", dict(kv_dtype=W.F32, head_dim=64, top_k=40, seq_lens=(1500, 1203))),
     ("g1", dict(num_q_heads=2, num_kv_heads=2, top_k=33, seq_lens=(1500, 977))),
     ("g2_b16", dict(num_q_heads=4, num_kv_heads=2, block_size=16, window=64, top_k=50, seq_lens=(1313, 700))),
+    ("g8", dict(num_q_heads=16, num_kv_heads=2, top_k=70, seq_lens=(2600, 1900))),
+    ("g8_f32_d64", dict(num_q_heads=16, num_kv_heads=2, kv_dtype=W.F32, head_dim=64, top_k=30, seq_lens=(1500, 900))),
     ("no_tail", dict(linear_tail=0, top_k=25, seq_lens=(1500, 1203))),
     ("dense", dict(top_k=4000, seq_lens=(1500, 1203))),
     ("short", dict(top_k=16, seq_lens=(200, 37))),
