@@ -2026,9 +2026,12 @@ __device__ __forceinline__ uint32_t block_scan_incl(uint32_t v, uint32_t* wtot) 
 }
 
 constexpr int kSelThreads = 1024;   // token-level selection: threads per head
+constexpr size_t kSelCacheBytes = 128 * 1024;   // token rows up to this size stay in LDS
 constexpr int kUnionThreads = 1024; // token-level exact lists: threads per (sequence, kv head)
 
+template <bool CACHE>
 __global__ __launch_bounds__(kSelThreads) void k_select_tokens(DecodeParams P) {
+  extern __shared__ uint32_t krow[];   // CACHE: the row's keys, filled by the first pass
   constexpr int NT = kSelThreads;
   constexpr int NW = NT / kWave;
   constexpr int UK = 16;            // keys in flight per thread
@@ -2053,6 +2056,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_tokens(DecodeParams P) {
   int32_t* out = P.sel_idx ? P.sel_idx + static_cast<size_t>(bh) * k : nullptr;
   const bool take_all = k >= nc;
   const bool take_none = k <= 0 || nc == 0;
+  const bool cached = CACHE && !take_all && !take_none;   // the radix passes fill krow
 
   uint32_t thr = 0u;
   int rem = k;   // keys equal to thr still to take, lowest indices first
@@ -2068,10 +2072,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select_tokens(DecodeParams P) {
       for (int i0 = 0; i0 < nc; i0 += NT * UK) {
         uint32_t x[UK];
 #pragma unroll
-        for (int u = 0; u < UK; ++u) x[u] = kh[min(i0 + u * NT + tid, nc - 1)];
+        for (int u = 0; u < UK; ++u) {
+          const int i = min(i0 + u * NT + tid, nc - 1);
+          x[u] = (CACHE && pass > 0) ? krow[i] : kh[i];
+        }
 #pragma unroll
-        for (int u = 0; u < UK; ++u)
-          if (i0 + u * NT + tid < nc && (x[u] & pmask) == prefix) atomicAdd(&hist[(x[u] >> shift) & dmask], 1u);
+        for (int u = 0; u < UK; ++u) {
+          if (i0 + u * NT + tid < nc) {
+            if (CACHE && pass == 0) krow[i0 + u * NT + tid] = x[u];
+            if ((x[u] & pmask) == prefix) atomicAdd(&hist[(x[u] >> shift) & dmask], 1u);
+          }
+        }
       }
       __syncthreads();
       // thread tid holds the BPT bins counted from the top: digits
@@ -2118,7 +2129,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select_tokens(DecodeParams P) {
   for (int w0 = wb; w0 < we; w0 += UK) {
     uint32_t x[UK];
 #pragma unroll
-    for (int u = 0; u < UK; ++u) x[u] = kh[min((w0 + u) * kWave + lane, max(nc - 1, 0))];
+    for (int u = 0; u < UK; ++u) {
+      const int i = min((w0 + u) * kWave + lane, max(nc - 1, 0));
+      x[u] = cached ? krow[i] : kh[i];
+    }
 #pragma unroll
     for (int u = 0; u < UK; ++u) {
       if (w0 + u >= we) break;
@@ -2147,7 +2161,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select_tokens(DecodeParams P) {
   for (int w0 = wb; w0 < we; w0 += UK) {
     uint32_t x[UK];
 #pragma unroll
-    for (int u = 0; u < UK; ++u) x[u] = kh[min((w0 + u) * kWave + lane, max(nc - 1, 0))];
+    for (int u = 0; u < UK; ++u) {
+      const int i = min((w0 + u) * kWave + lane, max(nc - 1, 0));
+      x[u] = cached ? krow[i] : kh[i];
+    }
 #pragma unroll
     for (int u = 0; u < UK; ++u) {
       const int w = w0 + u;
@@ -2453,8 +2470,16 @@ hipError_t launch_tokens(const Problem& p, const DecodeLayout& L, const DecodePa
       hipLaunchKernelGGL((k_select<8>), grid, dim3(kWave), 0, stream, P);
     else if (p.nc_max <= 32 * kWave)
       hipLaunchKernelGGL((k_select<32>), grid, dim3(kWave), 0, stream, P);
-    else
-      hipLaunchKernelGGL(k_select_tokens, grid, dim3(kSelThreads), 0, stream, P);
+    else if (static_cast<size_t>(p.nc_max) * sizeof(uint32_t) <= kSelCacheBytes) {
+      // the row fits in LDS: only the first radix pass reads it from memory
+      const size_t lds = static_cast<size_t>(p.nc_max) * sizeof(uint32_t);
+      hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select_tokens<true>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (a != hipSuccess) return a;
+      hipLaunchKernelGGL((k_select_tokens<true>), grid, dim3(kSelThreads), lds, stream, P);
+    } else {
+      hipLaunchKernelGGL((k_select_tokens<false>), grid, dim3(kSelThreads), 0, stream, P);
+    }
     hipError_t e = launch_status("k_select");
     if (e != hipSuccess) return e;
   }
