@@ -19,6 +19,11 @@ Sources (page title, then the part of the page):
 * [SLAKE] "SLAKE: Softmax-Approximated Training-Free Linear Attention with
   KV-Cache Eviction for Long-Sequence LLMs" -- abstract (PTAA: first-order
   Taylor linearisation of the softmax kernel for low-importance tokens).
+* [SALS] "SALS: Sparse Attention in Latent Space for KV Cache Compression"
+  -- summary, Approach (top-k token selection; here on the plain keys).
+
+Every function is pinned by the CPU tests (hand-derived goldens, closed
+forms, brute force on tiny inputs, invariants); none is parity unpinned.
 
 None of the pages prints a formula, so every step below states the reading
 it implements.  Everything is float64; stored inputs (bfloat16 bit patterns
