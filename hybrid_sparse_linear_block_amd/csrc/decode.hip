@@ -11,8 +11,8 @@
 //   2. selection        top-k candidates per query head (score desc, index
 //      asc), ascending index output, as a bitmap per head.  Up to 1024
 //      candidates it runs inside the attention prologue (each wavefront one
-//      head); beyond that, and for the grouped variant, in its own kernel
-//      (k_select / k_select_grouped).
+//      head), and the grouped variant up to 512 candidates on the bf16 path;
+//      beyond that in its own kernel (k_select / k_select_grouped).
 //   3. k_attend         split-K over the union of the group's exact blocks
 //      (sinks, window and selected blocks, SPLA Figure 1(a)), which each
 //      workgroup builds from the bitmaps with a per-block mask of the heads
@@ -62,6 +62,7 @@ constexpr int kUnitSlices = 4;       // slices per dynamically claimed unit
 constexpr int kMaxDynList = 2048;    // union entries a dynamic attention workgroup holds in LDS
 constexpr int kDeadT0 = 1 << 30;     // first token of a slice whose rows are all invalid
 constexpr int kFusedKplMax = 16;     // keys per lane of the selection fused into the attention prologue: 8 or 16
+constexpr int kFusedKplGrouped = 8;  // keys per lane of the fused grouped selection
 constexpr size_t kBtStageBytes = 8 * 1024;      // block-table row staged in LDS up to this size
 
 // The token append taken in by the scoring / readout kernel
@@ -869,7 +870,7 @@ struct SplitShare {
   int count;   // union size (uniform)
   int ne;      // entries of this split (uniform)
 };
-template <int G, bool FULL, int FK, typename Stage, typename Early>
+template <int G, bool FULL, int FK, bool GS, typename Stage, typename Early>
 __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, int b, int g, int split,
                                   Stage&& stage, Early&& early) {
   constexpr int NW = kThreads / kWave;
@@ -944,21 +945,73 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
     __syncthreads();   // the block-table row
     early(nc > 0 ? cr.lo + nc : 0, nb, P.bt_staged ? btrow : bt);
   }
-  if (P.fused_sel) {
-    // each wavefront selects for its heads; the bitmaps go to LDS and, from
-    // the pair's first workgroup, the indices to sel_idx
-    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + P.sl.hist) + wave * 256;
-    auto no_key = [](int) -> uint32_t { return 0u; };   // the keys are all in registers
+  if constexpr (!GS) {
+    if (P.fused_sel) {
+      // each wavefront selects for its heads; the bitmaps go to LDS and, from
+      // the pair's first workgroup, the indices to sel_idx
+      uint32_t* hist = reinterpret_cast<uint32_t*>(smem + P.sl.hist) + wave * 256;
+      auto no_key = [](int) -> uint32_t { return 0u; };   // the keys are all in registers
+#pragma unroll
+      for (int i = 0; i < HPW; ++i) {
+        const int h = wave + NW * i;
+        if (h < G) {
+          int32_t* out = (P.sel_idx && split == 0)
+                             ? P.sel_idx + (static_cast<size_t>(b) * P.Hq + g * G + h) * P.top_k
+                             : nullptr;
+          head_select<FK>(no_key, kr[i], nc, P.top_k, nwords, lane, hist, bits + h * nwords, out, cr.lo);
+        }
+      }
+    }
+  } else if (nc > 0) {
+    // grouped selection, as k_select_grouped computes it: each wavefront
+    // turns its heads' scores into shares of the head's candidate mass (a
+    // softmax over the candidates); wavefront 0 sums the G shares per block
+    // and selects once for every head of the group
+    const int ncr = ceil_div(P.nc_max, kWave) * kWave;
+    float* gw = reinterpret_cast<float*>(smem + P.sl.gw);
 #pragma unroll
     for (int i = 0; i < HPW; ++i) {
       const int h = wave + NW * i;
       if (h < G) {
-        int32_t* out = (P.sel_idx && split == 0)
-                           ? P.sel_idx + (static_cast<size_t>(b) * P.Hq + g * G + h) * P.top_k
-                           : nullptr;
-        head_select<FK>(no_key, kr[i], nc, P.top_k, nwords, lane, hist, bits + h * nwords, out, cr.lo);
+        uint32_t kmax = 0u;
+#pragma unroll
+        for (int j = 0; j < FK; ++j)
+          if (lane + kWave * j < nc) kmax = max(kmax, kr[i][j]);
+        const float m = f32_from_order_key(wave_max_u32(kmax));
+        float e[FK], sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < FK; ++j) {
+          e[j] = lane + kWave * j < nc ? fast_exp(f32_from_order_key(kr[i][j]) - m) : 0.f;
+          sum += e[j];
+        }
+        const float inv = 1.f / wave_sum(sum);
+#pragma unroll
+        for (int j = 0; j < FK; ++j)
+          if (lane + kWave * j < nc) gw[h * ncr + lane + kWave * j] = e[j] * inv;   // nc <= ncr
       }
     }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t agg[FK];
+#pragma unroll
+      for (int j = 0; j < FK; ++j) {
+        float w = 0.f;
+        if (lane + kWave * j < nc) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) w += gw[h * ncr + lane + kWave * j];
+        }
+        agg[j] = f32_order_key(w);
+      }
+      uint32_t* hist = reinterpret_cast<uint32_t*>(smem + P.sl.hist);
+      int32_t* out = (P.sel_idx && split == 0) ? P.sel_idx + (static_cast<size_t>(b) * P.Hq + g * G) * P.top_k
+                                               : nullptr;
+      auto no_key = [](int) -> uint32_t { return 0u; };
+      head_select<FK>(no_key, agg, nc, P.top_k, nwords, lane, hist, bits, out, cr.lo, G);
+    }
+  } else {   // grouped, no candidates: every head's bitmap is empty
+    for (int x = tid; x < G * nwords; x += kThreads) bits[x] = 0ull;
+    if (P.sel_idx && split == 0)
+      for (int x = tid; x < G * P.top_k; x += kThreads) P.sel_idx[(static_cast<size_t>(b) * P.Hq + g * G) * P.top_k + x] = -1;
   }
   __syncthreads();
 
@@ -1131,7 +1184,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
     qr[h].load(reinterpret_cast<const char*>(P.q) +
                ((static_cast<size_t>(b) * P.Hq + g * G + h) * D + lig * 8) * KV::kBytes);
   extern __shared__ uint64_t dyn_lds[];
-  const SplitShare share = union_share<G, false, kFusedKplMax>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split,
+  const SplitShare share = union_share<G, false, kFusedKplMax, false>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split,
                                                                [] {}, [](int, int, const int32_t*) {});
   const int T = share.T;
   const int Ts = T - T % P.B;   // tokens the linear state holds
@@ -1508,7 +1561,7 @@ __device__ void merge_pair(const DecodeParams& P, int pair, int b, int g, int ns
   }
 }
 
-template <int D, int G, bool DYN, int FK>
+template <int D, int G, bool DYN, int FK, bool GS>
 __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   constexpr int NW = kThreads / kWave;
   constexpr int KS = D / 32;            // score MFMAs per slice (32 channels each)
@@ -1601,7 +1654,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   };
   extern __shared__ uint64_t dyn_lds[];
   const SplitShare share =
-      union_share<G, DYN, FK>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, stage_q, early);
+      union_share<G, DYN, FK, GS>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, stage_q, early);
   const int T = share.T;
   const int Ts = T - T % P.B;           // tokens the linear state holds
   const int win0 = T - P.W;
@@ -2558,14 +2611,18 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
     if constexpr (KV::kBytes == 2) {
       // keys per lane of the fused selection: 8 up to 512 candidates
       const bool fk8 = p.nc_max <= 8 * kWave;
-      if (P.dyn && fk8)
-        hipLaunchKernelGGL((k_attend_mfma<D, G, true, 8>), grid, dim3(kThreads), lds, stream, P);
+      if (L.fused_sel && p.grouped && P.dyn)   // fused grouped selection: up to 512 candidates
+        hipLaunchKernelGGL((k_attend_mfma<D, G, true, 8, true>), grid, dim3(kThreads), lds, stream, P);
+      else if (L.fused_sel && p.grouped)
+        hipLaunchKernelGGL((k_attend_mfma<D, G, false, 8, true>), grid, dim3(kThreads), lds, stream, P);
+      else if (P.dyn && fk8)
+        hipLaunchKernelGGL((k_attend_mfma<D, G, true, 8, false>), grid, dim3(kThreads), lds, stream, P);
       else if (P.dyn)
-        hipLaunchKernelGGL((k_attend_mfma<D, G, true, 16>), grid, dim3(kThreads), lds, stream, P);
+        hipLaunchKernelGGL((k_attend_mfma<D, G, true, 16, false>), grid, dim3(kThreads), lds, stream, P);
       else if (fk8)
-        hipLaunchKernelGGL((k_attend_mfma<D, G, false, 8>), grid, dim3(kThreads), lds, stream, P);
+        hipLaunchKernelGGL((k_attend_mfma<D, G, false, 8, false>), grid, dim3(kThreads), lds, stream, P);
       else
-        hipLaunchKernelGGL((k_attend_mfma<D, G, false, 16>), grid, dim3(kThreads), lds, stream, P);
+        hipLaunchKernelGGL((k_attend_mfma<D, G, false, 16, false>), grid, dim3(kThreads), lds, stream, P);
     }
     else if (p.B >= kUnit)
       hipLaunchKernelGGL((k_attend<KV, D, G, true>), grid, dim3(kThreads), lds, stream, P);
@@ -2618,7 +2675,10 @@ DecodeLayout decode_layout(const Problem& p) {
                                              static_cast<long>(p.max_seq_len) + 1));
   // Dynamic attention (bf16 path): the pair's workgroups share its union
   // list, which the prologue keeps whole in LDS.
-  L.fused_sel = (!p.grouped && !p.tokens && p.nc_max <= kFusedKplMax * kWave) ? 1 : 0;
+  // The grouped selection is fused on the bf16 path up to 512 candidates
+  // (eight keys per lane); past that its registers spill.
+  L.fused_sel = (!p.tokens && (p.grouped ? (p.bf16 && p.nc_max <= kFusedKplGrouped * kWave)
+                                         : p.nc_max <= kFusedKplMax * kWave)) ? 1 : 0;
   // with the selection fused, the scoring kernel zeroes the work counters,
   // so the dynamic split needs that launch
   const bool scores_launched = (p.nc_max > 0) || p.linear_tail;
@@ -2659,6 +2719,9 @@ DecodeLayout decode_layout(const Problem& p) {
     L.sl.btrow = take(L.bt_staged ? static_cast<uint32_t>(p.nblk_max * sizeof(int32_t)) : 0u);
     L.sl.ulist = take(L.dyn ? static_cast<uint32_t>(2 * L.umax * sizeof(int32_t)) : 0u);
     L.sl.hist = take(L.fused_sel ? static_cast<uint32_t>((kThreads / kWave) * 256 * sizeof(uint32_t)) : 0u);
+    L.sl.gw = take(L.fused_sel && p.grouped
+                       ? static_cast<uint32_t>(p.G * ((p.nc_max + kWave - 1) / kWave) * kWave * sizeof(float))
+                       : 0u);
     L.sl.total = o;
   }
   size_t off = 0;

@@ -37,10 +37,11 @@ struct Problem {
 // (uint64), wavefront-private union chunk masks [4][64] (uint64) and chunk
 // prefixes [4][64] (int32), when staged the sequence's block-table row
 // [nblk_max] (int32), for dynamic attention the whole union list: entries
-// [umax] and pages [umax] (int32), and for the fused selection the
-// wavefronts' radix histograms [4][256] (uint32).
+// [umax] and pages [umax] (int32), for the fused selection the
+// wavefronts' radix histograms [4][256] (uint32), and for the fused grouped
+// selection the heads' candidate shares [G][round64(nc_max)] (float).
 struct SelLayout {
-  uint32_t bits, umask, upre, btrow, ulist, hist, total;
+  uint32_t bits, umask, upre, btrow, ulist, hist, gw, total;
 };
 
 struct DecodeLayout {
