@@ -384,6 +384,30 @@ def dense_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, sigma: float) -
     return (w @ V) / w.sum()
 
 
+def decode_chunk_head(qc: np.ndarray, K: np.ndarray, V: np.ndarray, T0: int, p: Params, *,
+                      selected: Optional[Sequence[Optional[Sequence[int]]]] = None,
+                      form: str = "subtraction") -> list:
+    """A chunk of Q consecutive queries of one head: the multi-query form of
+    the decode step (SALSA abstract, training-consistent form over a tile of
+    queries; SPLA Figure 1(a) partition per query).
+
+    qc [Q, d]; K/V [T0 + Q, d] hold the cache's T0 tokens followed by the
+    chunk's Q tokens.  Reading: query i sits at position T0 + i and sees the
+    tokens 0 .. T0 + i (causal), so its output is the decode step at length
+    T0 + i + 1 with its own candidates, selection, window, exact set and
+    linear tail.  Returns one HeadResult per query.  `selected` may force a
+    row's selection (near-ties), as in decode_head.
+    """
+    Q = qc.shape[0]
+    assert K.shape[0] >= T0 + Q and V.shape[0] >= T0 + Q
+    rows = []
+    for i in range(Q):
+        L = T0 + i + 1
+        sel = None if selected is None else selected[i]
+        rows.append(decode_head(qc[i], K[:L], V[:L], p, selected=sel, form=form))
+    return rows
+
+
 # ----------------------------------------------------------------------------
 # Whole batch
 # ----------------------------------------------------------------------------

@@ -579,3 +579,74 @@ def test_token_level_candidates_and_ties():
     assert O.candidate_tokens(5, p).tolist() == []
     # equal scores go to the lower token index
     assert O.select_top_k(np.array([2, 3, 4, 5, 6]), np.array([0.5, 1.0, 1.0, 1.0, 0.2]), 2).tolist() == [3, 4]
+
+
+# ----------------------------------------------------------------------------
+# Multi-query (chunk) form: Q consecutive queries, each causal at its position
+# ----------------------------------------------------------------------------
+
+def _chunk_case(seed, T0, Q, d=8, B=4, **kw):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((T0 + Q, d))
+    V = rng.standard_normal((T0 + Q, d))
+    qc = rng.standard_normal((Q, d))
+    p = _params(head_dim=d, block_size=B, **kw)
+    return qc, K, V, p
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_chunk_all_exact_is_causal_dense_attention(seed):
+    # budget covering every candidate: each query is plain softmax attention
+    # over the tokens up to its own position; computed here as one masked
+    # score matrix (rows = queries, columns = tokens) through torch
+    T0, Q = 37, 6
+    qc, K, V, p = _chunk_case(seed, T0, Q, top_k=64)
+    rows = O.decode_chunk_head(qc, K, V, T0, p)
+    q_t, k_t, v_t = (torch.from_numpy(x) for x in (qc, K, V))
+    s = p.sigma * (q_t @ k_t.T)
+    mask = torch.arange(T0 + Q)[None, :] <= (T0 + torch.arange(Q))[:, None]
+    ref = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=1) @ v_t
+    for i, r in enumerate(rows):
+        np.testing.assert_allclose(r.out, ref[i].numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_chunk_rows_do_not_see_later_tokens(seed):
+    # causality: row i is unchanged when every key and value after its
+    # position is replaced; the rows after it change
+    T0, Q = 45, 5
+    qc, K, V, p = _chunk_case(seed, T0, Q, top_k=2, window=8)
+    base = O.decode_chunk_head(qc, K, V, T0, p)
+    for i in range(Q - 1):
+        K2, V2 = K.copy(), V.copy()
+        K2[T0 + i + 1:] += 3.0
+        V2[T0 + i + 1:] -= 2.0
+        alt = O.decode_chunk_head(qc, K2, V2, T0, p)
+        for j in range(Q):
+            if j <= i:
+                np.testing.assert_array_equal(alt[j].out, base[j].out)
+            else:
+                assert not np.allclose(alt[j].out, base[j].out)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_chunk_rows_against_per_token_brute_force(seed):
+    # each row by direct per-token sums over its own exact and residual sets
+    # (first-order Taylor weight 1 + s on the residual tokens), with the
+    # chunk crossing a block boundary (T0 = 42, B = 4)
+    T0, Q = 42, 6
+    qc, K, V, p = _chunk_case(seed, T0, Q, top_k=2, window=8, num_sink=2)
+    rows = O.decode_chunk_head(qc, K, V, T0, p)
+    for i, r in enumerate(rows):
+        L = T0 + i + 1
+        assert r.exact[L - 1] and len(r.exact) == L          # the row's own token is exact
+        num = np.zeros(K.shape[1])
+        den = 0.0
+        for t in range(L):
+            st = p.sigma * float(K[t] @ qc[i])
+            w = math.exp(st) if r.exact[t] else 1.0 + st
+            num += w * V[t]
+            den += w
+        np.testing.assert_allclose(r.out, num / den, rtol=1e-11, atol=1e-12)
+        # the window of row i starts at its own length minus W
+        assert r.exact[L - p.window:].all()
