@@ -30,7 +30,8 @@ HSLA_SEL_TOKEN = 2
 HSLA_MAX_PROFILE_EVENTS = 8
 
 EXPORTED = ("hsla_status_string", "hsla_version", "hsla_build_workspace_size", "hsla_build_state",
-            "hsla_append_token", "hsla_decode_workspace_size", "hsla_decode", "hsla_append_decode")
+            "hsla_append_token", "hsla_decode_workspace_size", "hsla_decode", "hsla_append_decode",
+            "hsla_prefill_chunk_workspace_size", "hsla_prefill_chunk")
 
 
 class hsla_config(ctypes.Structure):
@@ -105,6 +106,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsla_append_decode.argtypes = [P(hsla_config), P(hsla_kv_pool), P(hsla_state), vp, vp, vp, vp, vp, i32,
                                        i32, vp, vp, vp, sz, vp, P(hsla_profile)]
     lib.hsla_append_decode.restype = ctypes.c_int
+    lib.hsla_prefill_chunk_workspace_size.argtypes = [P(hsla_config), i32, i32, i32]
+    lib.hsla_prefill_chunk_workspace_size.restype = sz
+    lib.hsla_prefill_chunk.argtypes = [P(hsla_config), P(hsla_kv_pool), P(hsla_state), vp, vp, vp, vp, vp, i32,
+                                       i32, i32, vp, vp, vp, sz, vp]
+    lib.hsla_prefill_chunk.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -233,6 +239,20 @@ def hsla_append_decode(cfg: Config, pool: Pool, state: State, k_new, v_new, seq_
         ctypes.byref(cfg.c()), ctypes.byref(pool.c()), ctypes.byref(state.c()), _ptr(k_new), _ptr(v_new),
         _ptr(seq_lens_before), _ptr(seq_lens_after), _ptr(q), batch, max_seq_len, _ptr(out), _ptr(sel_idx),
         _ptr(workspace), nbytes, _stream(stream), ctypes.byref(prof) if prof is not None else None))
+
+
+def hsla_prefill_chunk_workspace_size(cfg: Config, batch: int, q_len: int, max_seq_len: int) -> int:
+    return int(load().hsla_prefill_chunk_workspace_size(ctypes.byref(cfg.c()), batch, q_len, max_seq_len))
+
+
+def hsla_prefill_chunk(cfg: Config, pool: Pool, state: State, k_chunk, v_chunk, seq_lens_before, seq_lens_after,
+                       q, batch: int, q_len: int, max_seq_len: int, out, sel_idx, workspace,
+                       workspace_bytes: Optional[int] = None, stream=None) -> None:
+    nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check("hsla_prefill_chunk", load().hsla_prefill_chunk(
+        ctypes.byref(cfg.c()), ctypes.byref(pool.c()), ctypes.byref(state.c()), _ptr(k_chunk), _ptr(v_chunk),
+        _ptr(seq_lens_before), _ptr(seq_lens_after), _ptr(q), batch, q_len, max_seq_len, _ptr(out), _ptr(sel_idx),
+        _ptr(workspace), nbytes, _stream(stream)))
 
 
 load()

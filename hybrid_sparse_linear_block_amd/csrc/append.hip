@@ -8,8 +8,14 @@
 // never needs them; folding them in at completion gives the same outputs as
 // a per-token update while the per-step work shrinks to one row write.
 //
+// A chunk of Q tokens (the multi-query form) goes in two launches around
+// the chunk's attention: the first writes the Q page slots (and each query
+// row's length for the decode), the second, once every query has read the
+// state as it stood before the chunk, folds the block the chunk completed (at
+// most one, Q <= B) and sets the new length.
+//
 // Grid: (row chunks of 32 rows of S + 1, sequence x kv head).  Row chunk 0
-// writes the page slot and the new length; on a completing step every chunk
+// writes the page slots and the new length; on a completing step every chunk
 // stages the block through LDS and adds it to its rows of S and z (chunk 0
 // also to sv), while the extra workgroup computes the block's statistics
 // (it reads the block's rows as 16-byte vectors and reduces per channel
@@ -37,8 +43,13 @@ struct AppendParams {
   const void* v_new;
   const int32_t* seq_lens_before;
   int32_t* seq_lens_after;
+  int32_t* row_lens;   // chunk writes: each query row's length [batch x count] (or null)
   int Hkv, B, max_blocks, max_seq_len;
+  int count;           // tokens per sequence: 1, or the chunk length
+  int mode;            // kWriteRows | kFold
 };
+constexpr int kWriteRows = kAppendWriteRows;
+constexpr int kFold = kAppendFold;
 
 template <typename KV, int D>
 __global__ __launch_bounds__(kThreads) void k_append(AppendParams P) {
@@ -51,27 +62,41 @@ __global__ __launch_bounds__(kThreads) void k_append(AppendParams P) {
   const int g = pair % P.Hkv;
   const int rc = blockIdx.x;
   const int tid = threadIdx.x;
-  const int T = min(max(P.seq_lens_before[b], 0), P.max_seq_len - 1);  // new token's position
-  const size_t nbase = static_cast<size_t>(pair) * D;
+  const int Q = P.count;
+  const int T0 = min(max(P.seq_lens_before[b], 0), P.max_seq_len - Q);  // first new token's position
+  const size_t nbase = static_cast<size_t>(pair) * D;   // the pair's state rows
   const int B = P.B;
-  const size_t page = static_cast<size_t>(P.block_table[static_cast<size_t>(b) * P.max_blocks + T / B]);
-  const size_t row0 = (page * P.Hkv + g) * B;  // first row of this page-head tile
+  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  // new token i of the pair: k_new / v_new row ((b Q + i) Hkv + g)
+  auto new_row = [&](int i) { return ((static_cast<size_t>(b) * Q + i) * P.Hkv + g) * D; };
   if (rc == 0) {
-    if (tid < D) {
-      kv_put<KV>(P.k_pages, (row0 + T % B) * D + tid, P.k_new, nbase + tid);
-      kv_put<KV>(P.v_pages, (row0 + T % B) * D + tid, P.v_new, nbase + tid);
+    if (P.mode & kWriteRows) {
+      for (int i = 0; i < Q; ++i) {
+        const int t = T0 + i;
+        const size_t r = (static_cast<size_t>(bt[t / B]) * P.Hkv + g) * B + t % B;
+        if (tid < D) {
+          kv_put<KV>(P.k_pages, r * D + tid, P.k_new, new_row(i) + tid);
+          kv_put<KV>(P.v_pages, r * D + tid, P.v_new, new_row(i) + tid);
+        }
+      }
+      if (P.row_lens && g == 0 && tid < Q) P.row_lens[static_cast<size_t>(b) * Q + tid] = T0 + 1 + tid;
     }
-    if (g == 0 && tid == 0 && P.seq_lens_after) P.seq_lens_after[b] = T + 1;
+    if ((P.mode & kFold) && g == 0 && tid == 0 && P.seq_lens_after) P.seq_lens_after[b] = T0 + Q;
   }
-  if ((T + 1) % B != 0) return;   // uniform: the block is still incomplete
+  if (!(P.mode & kFold)) return;
+  const int ic = B - 1 - T0 % B;   // the new token that completes a block, if ic < Q
+  if (ic >= Q) return;              // uniform: no block completes
+  const int T = T0 + ic;
+  const size_t page = static_cast<size_t>(bt[T / B]);
+  const size_t row0 = (page * P.Hkv + g) * B;  // first row of this page-head tile
   __shared__ uint4 lds[kFoldStageBytes / 16];   // block stage, or the statistics' sums
   if (rc == D / kFoldRows) {      // the statistics workgroup
     const size_t so = (page * P.Hkv + g) * D;
-    filled_block_stats<KV, D, kThreads>(P.k_pages, P.k_new, row0, T % B, nbase, B, P.blk_mean + so, P.blk_var + so,
+    filled_block_stats<KV, D, kThreads>(P.k_pages, P.k_new, row0, T % B, new_row(ic), B, P.blk_mean + so, P.blk_var + so,
                                         *reinterpret_cast<BlockStatsLds<kThreads, D>*>(lds));
     return;
   }
-  const CompletedBlock cb{P.k_pages, P.v_pages, P.k_new, P.v_new, row0, nbase, T % B, B};
+  const CompletedBlock cb{P.k_pages, P.v_pages, P.k_new, P.v_new, row0, new_row(ic), T % B, B};
   const int col4 = tid % C4;
   const int r_first = rc * kFoldRows + tid / C4;
   float* Sp = P.S + static_cast<size_t>(pair) * D * D;
@@ -100,8 +125,12 @@ hipError_t launch_t(const Problem& p, const AppendParams& P, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_append(const Problem& p, const AppendArgs& a, hipStream_t s) {
+hipError_t launch_append(const Problem& p, const AppendArgs& a, hipStream_t s, int count, int mode,
+                         int32_t* row_lens) {
   AppendParams P{};
+  P.count = count;
+  P.mode = mode;
+  P.row_lens = row_lens;
   P.k_pages = a.k_pages;
   P.v_pages = a.v_pages;
   P.blk_mean = a.blk_mean;

@@ -110,6 +110,8 @@ struct DecodeParams {
   int fused_sel;    // per-head selection inside the attention prologue (no selection kernel)
   int fused_merge;  // the last attention workgroup of a pair merges its splits (no merge kernel)
   int tokens;       // token-level variant: candidates are single tokens, scored by their keys
+  int qrows;        // query rows per sequence: 1, or the chunk length of the multi-query form
+  int chunk;        // multi-query form: the state holds the whole blocks before the chunk
   int bsel;         // candidate granularity: the block size, or 1 for the token-level variant
   int32_t* tlist;   // token-level variant: each pair's exact token list [pairs, umax] x (token | heads << 20, page)
   SelLayout sl;
@@ -128,6 +130,21 @@ __device__ __forceinline__ int append_pos(const DecodeParams& P, int b) {
 // seq_lens is written by that same kernel, so the length comes from before.
 __device__ __forceinline__ int first_kernel_len(const DecodeParams& P, int b) {
   return P.app.k_new ? append_pos(P, b) + 1 : clamp_len(P.seq_lens[b], P.max_seq_len);
+}
+// Multi-query form: row b is query b % qrows of sequence b / qrows, whose
+// block-table row and linear state it reads.
+__device__ __forceinline__ int seq_of(const DecodeParams& P, int b) { return b / P.qrows; }
+__device__ __forceinline__ int state_pair(const DecodeParams& P, int pair) {
+  return seq_of(P, pair / P.Hkv) * P.Hkv + pair % P.Hkv;
+}
+// Tokens the linear state holds for row b of length T: the whole blocks of
+// T for a decode row; for query i of a chunk (T = T0 + 1 + i) the whole
+// blocks of the T0 tokens before the chunk, since the chunk's blocks are
+// folded in after it.  Every token from there to T is in the row's window
+// (chunk length <= W - B + 1), so the exact part covers it.
+__device__ __forceinline__ int state_tokens(const DecodeParams& P, int T, int b) {
+  const int t = P.chunk ? T - 1 - b % P.qrows : T;
+  return t - t % P.B;
 }
 
 // Query of one head, 8 channels per lane.
@@ -198,7 +215,7 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
   const int tid = threadIdx.x;
   const int lig = tid % LPT;
   const int slot = tid / LPT;
-  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  const int32_t* bt = P.block_table + static_cast<size_t>(seq_of(P, b)) * P.max_blocks;
   const int lo = P.ns / P.B;   // first candidate block, whatever the length
 
   // Issue every load of the chunk before any arithmetic: page ids (bounded
@@ -291,7 +308,7 @@ __device__ __forceinline__ void score_tokens_part(const DecodeParams& P, int b, 
   const CandRange cr = candidate_range(T, 1, P.ns, P.W);
   const int nc = min(cr.count, P.nc_max);
   if (c_begin >= nc) return;
-  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  const int32_t* bt = P.block_table + static_cast<size_t>(seq_of(P, b)) * P.max_blocks;
   const char* kp = reinterpret_cast<const char*>(P.k_pages);
   Row8<KV> kr[NIT];
 #pragma unroll
@@ -347,8 +364,9 @@ __device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g
     return;
   }
 
-  const float* Sp = (app ? P.app.S : P.S) + static_cast<size_t>(pair) * D * D;
-  const float* zp = (app ? P.app.z : P.z) + nbase + r0;
+  const int spair = state_pair(P, pair);   // the sequence's state (the pair itself unless multi-query)
+  const float* Sp = (app ? P.app.S : P.S) + static_cast<size_t>(spair) * D * D;
+  const float* zp = (app ? P.app.z : P.z) + static_cast<size_t>(spair) * D + r0;
   float4 srow[NR];
   float qv[NR][G];
   float zr = 0.f;
@@ -883,7 +901,7 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
   int32_t* btrow = reinterpret_cast<int32_t*>(smem + P.sl.btrow);
   const int nwords = P.nwords;
   const int S = P.max_split;
-  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  const int32_t* bt = P.block_table + static_cast<size_t>(seq_of(P, b)) * P.max_blocks;
   const uint64_t* src = P.bits + (static_cast<size_t>(b) * P.Hq + g * G) * nwords;
   const int nbits = P.fused_sel ? 0 : G * nwords;   // bitmaps loaded from the selection kernel
   constexpr int HPW = (G + NW - 1) / NW;            // heads per wavefront of the fused selection
@@ -1187,7 +1205,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
   const SplitShare share = union_share<G, false, kFusedKplMax, false>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split,
                                                                [] {}, [](int, int, const int32_t*) {});
   const int T = share.T;
-  const int Ts = T - T % P.B;   // tokens the linear state holds
+  const int Ts = state_tokens(P, T, b);   // tokens the linear state holds
   if (split >= share.count) return;
   const int ne = share.ne;
   const int my_ent = share.ent;
@@ -1529,7 +1547,7 @@ __device__ void merge_pair(const DecodeParams& P, int pair, int b, int g, int ns
         ro += P.ro[((static_cast<size_t>(pair) * RO + rc) * G + hh) * D + c];
         rz += P.roz[(static_cast<size_t>(pair) * RO + rc) * G + hh];
       }
-      svc = P.sv[static_cast<size_t>(pair) * D + c];
+      svc = P.sv[static_cast<size_t>(state_pair(P, pair)) * D + c];
     }
     float M = 0.f;   // the linear part is in unshifted units (log-scale 0)
     float num = 0.f, den = 0.f, lnum = 0.f, lden = 0.f;
@@ -1552,7 +1570,7 @@ __device__ void merge_pair(const DecodeParams& P, int pair, int b, int g, int ns
     }
     if (tail) {
       const float num_u = svc + P.sigma * ro - lnum;
-      const float den_u = static_cast<float>(T - T % P.B) + P.sigma * rz - lden;   // n: tokens the state holds
+      const float den_u = static_cast<float>(state_tokens(P, T, b)) + P.sigma * rz - lden;   // n: tokens the state holds
       const float em = __expf(-M);
       num = fmaf(em, num_u, num);
       den = fmaf(em, den_u, den);
@@ -1656,7 +1674,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   const SplitShare share =
       union_share<G, DYN, FK, GS>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, stage_q, early);
   const int T = share.T;
-  const int Ts = T - T % P.B;           // tokens the linear state holds
+  const int Ts = state_tokens(P, T, b);           // tokens the linear state holds
   const int win0 = T - P.W;
   if (!DYN && split >= share.count) return;
   const int ne = share.ne;
@@ -1986,7 +2004,7 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
       ro_p[rc] = P.ro[((static_cast<size_t>(pair) * RO + rc) * G + hh) * D + c];
       rz_p[rc] = P.roz[(static_cast<size_t>(pair) * RO + rc) * G + hh];
     }
-    svc = P.sv[static_cast<size_t>(pair) * D + c];
+    svc = P.sv[static_cast<size_t>(state_pair(P, pair)) * D + c];
   }
   const int count = min(P.ucount[pair], P.umax);
   const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
@@ -2043,7 +2061,7 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
       rz += rz_p[rc];
     }
     const float num_u = svc + P.sigma * ro - lnum;
-    const float den_u = static_cast<float>(T - T % P.B) + P.sigma * rz - lden;   // n: tokens the state holds
+    const float den_u = static_cast<float>(state_tokens(P, T, b)) + P.sigma * rz - lden;   // n: tokens the state holds
     const float em = __expf(-M);
     num = fmaf(em, num_u, num);
     den = fmaf(em, den_u, den);
@@ -2280,7 +2298,7 @@ __global__ __launch_bounds__(kUnionThreads) void k_token_union(DecodeParams P) {
   const int w0 = max(T - P.W, nsink);   // first window token that is not a sink
   constexpr int kAll = (1 << G) - 1;
   int2* list = reinterpret_cast<int2*>(P.tlist) + static_cast<size_t>(pair) * P.umax;
-  const int32_t* bt = P.block_table + static_cast<size_t>(b) * P.max_blocks;
+  const int32_t* bt = P.block_table + static_cast<size_t>(seq_of(P, b)) * P.max_blocks;
   const uint64_t* bits = P.bits + (static_cast<size_t>(b) * P.Hq + g * G) * P.nwords;
 
   const int wpt = ceil_div(nw, NT);   // bitmap words per thread
@@ -2365,7 +2383,7 @@ __global__ __launch_bounds__(kThreads) void k_token_attend(DecodeParams P) {
   const int tg = lane / LPT;
   const int lig = lane % LPT;
   const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
-  const int Ts = T - T % P.B;           // tokens the linear state holds
+  const int Ts = state_tokens(P, T, b);           // tokens the linear state holds
   const int count = min(P.ucount[pair], P.umax);
   const int per = ceil_div(count, P.max_split);
   const int e0 = min(split * per, count);
@@ -2770,6 +2788,8 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.fused_sel = L.fused_sel;
   P.fused_merge = L.fused_merge;
   P.tokens = p.tokens;
+  P.qrows = p.qrows;
+  P.chunk = p.chunk;
   P.bsel = p.tokens ? 1 : p.B;
   P.tlist = reinterpret_cast<int32_t*>(a.ws + L.off_tlist);
   P.part = reinterpret_cast<float*>(a.ws + L.off_part);

@@ -49,6 +49,7 @@ hsla_status resolve(const hsla_config* cfg, int32_t batch, int32_t max_seq_len,
   p.linear_tail = cfg->linear_tail;
   p.grouped = cfg->selection == HSLA_SEL_GROUPED ? 1 : 0;
   p.tokens = cfg->selection == HSLA_SEL_TOKEN ? 1 : 0;
+  p.qrows = 1;
   p.deterministic = cfg->deterministic;
   p.bf16 = cfg->kv_dtype == HSLA_BF16;
   p.sigma = cfg->scale > 0.0f ? cfg->scale : 1.0f / sqrtf(static_cast<float>(cfg->head_dim));
@@ -266,6 +267,102 @@ hsla_status hsla_append_decode(const hsla_config* cfg, const hsla_kv_pool* pool,
   a.seq_lens_after = seq_lens_after;
   return decode_impl(cfg, pool, state, q, seq_lens_after, batch, max_seq_len, out, sel_idx, workspace,
                      workspace_bytes, stream, prof, &a);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The multi-query form's shapes: `seq` over the sequences (append), `rows`
+// over the batch x q_len query rows (decode).  Workspace: the decode's, then
+// the rows' lengths.
+hsla_status resolve_chunk(const hsla_config* cfg, int32_t batch, int32_t q_len, int32_t max_seq_len,
+                          int32_t max_blocks, Problem* seq, Problem* rows, size_t* ws_rows, size_t* ws_total) {
+  hsla_status st = resolve(cfg, batch, max_seq_len, max_blocks, seq);
+  if (st != HSLA_OK) return st;
+  if (seq->tokens) return HSLA_ERR_UNSUPPORTED;
+  if (q_len < 1 || q_len > seq->B || q_len > seq->W - seq->B + 1 || q_len > max_seq_len) return HSLA_ERR_INVALID_ARG;
+  if (static_cast<long>(batch) * q_len > (1L << 24)) return HSLA_ERR_INVALID_ARG;
+  if ((st = resolve(cfg, batch * q_len, max_seq_len, max_blocks, rows)) != HSLA_OK) return st;
+  rows->qrows = q_len;
+  rows->chunk = 1;
+  const size_t dec = hsla::decode_layout(*rows).total;
+  *ws_rows = (dec + 255) / 256 * 256;
+  *ws_total = *ws_rows + sizeof(int32_t) * static_cast<size_t>(batch) * q_len;
+  return HSLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hsla_prefill_chunk_workspace_size(const hsla_config* cfg, int32_t batch, int32_t q_len,
+                                         int32_t max_seq_len) {
+  Problem seq, rows;
+  size_t off = 0, total = 0;
+  if (resolve_chunk(cfg, batch, q_len, max_seq_len, -1, &seq, &rows, &off, &total) != HSLA_OK) return 0;
+  return total;
+}
+
+hsla_status hsla_prefill_chunk(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
+                               const void* k_chunk, const void* v_chunk, const int32_t* seq_lens_before,
+                               int32_t* seq_lens_after, const void* q, int32_t batch, int32_t q_len,
+                               int32_t max_seq_len, float* out, int32_t* sel_idx, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  Problem seq, rows;
+  size_t off = 0, total = 0;
+  hsla_status st = resolve_chunk(cfg, batch, q_len, max_seq_len, pool ? pool->max_blocks_per_seq : 0, &seq, &rows,
+                                 &off, &total);
+  if (st != HSLA_OK) return st;
+  if ((st = check_pool(pool, true)) != HSLA_OK) return st;
+  if ((st = check_state(state)) != HSLA_OK) return st;
+  if (!k_chunk || !v_chunk || !aligned(k_chunk, 16) || !aligned(v_chunk, 16)) return HSLA_ERR_INVALID_ARG;
+  if (!seq_lens_before || !aligned(seq_lens_before, 4)) return HSLA_ERR_INVALID_ARG;
+  if (!seq_lens_after || !aligned(seq_lens_after, 4) || seq_lens_after == seq_lens_before)
+    return HSLA_ERR_INVALID_ARG;
+  if (!q || !aligned(q, 16) || !out || !aligned(out, 16)) return HSLA_ERR_INVALID_ARG;
+  if (sel_idx && !aligned(sel_idx, 4)) return HSLA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < total || !aligned(workspace, 16)) return HSLA_ERR_WORKSPACE;
+  int32_t* row_lens = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + off);
+
+  hsla::AppendArgs a{};
+  a.k_pages = pool->k_pages;
+  a.v_pages = pool->v_pages;
+  a.blk_mean = pool->blk_mean;
+  a.blk_var = pool->blk_var;
+  a.block_table = pool->block_table;
+  a.S = state->S;
+  a.z = state->z;
+  a.sv = state->sv;
+  a.k_new = k_chunk;
+  a.v_new = v_chunk;
+  a.seq_lens_before = seq_lens_before;
+  a.seq_lens_after = seq_lens_after;
+
+  hsla::DecodeArgs d{};
+  d.k_pages = pool->k_pages;
+  d.v_pages = pool->v_pages;
+  d.blk_mean = pool->blk_mean;
+  d.blk_var = pool->blk_var;
+  d.block_table = pool->block_table;
+  d.S = rows.linear_tail ? state->S : nullptr;
+  d.z = rows.linear_tail ? state->z : nullptr;
+  d.sv = rows.linear_tail ? state->sv : nullptr;
+  d.q = q;
+  d.seq_lens = row_lens;
+  d.out = out;
+  d.sel_idx = sel_idx;
+  d.ws = static_cast<char*>(workspace);
+
+  (void)hipGetLastError();
+  // 1. the chunk's page slots and the query rows' lengths; 2. every query
+  // against the cache as it stood before the chunk's blocks were folded; 3.
+  // the fold of the completed block and the new lengths
+  if (hsla::launch_append(seq, a, stream, q_len, hsla::kAppendWriteRows, row_lens) != hipSuccess) return HSLA_ERR_HIP;
+  if (hsla::launch_decode(rows, hsla::decode_layout(rows), d, stream, nullptr, nullptr) != hipSuccess)
+    return HSLA_ERR_HIP;
+  if (hsla::launch_append(seq, a, stream, q_len, hsla::kAppendFold, nullptr) != hipSuccess) return HSLA_ERR_HIP;
+  return HSLA_OK;
 }
 
 }  // extern "C"

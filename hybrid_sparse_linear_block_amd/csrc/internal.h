@@ -24,6 +24,9 @@ struct Problem {
   int grouped;     // one selection per kv head (HSLA_SEL_GROUPED)
   int deterministic;  // static split-K attention (bitwise reproducible)
   int tokens;      // token-level variant (HSLA_SEL_TOKEN): candidates are single tokens
+  int qrows;       // query rows per sequence: 1, or the chunk length of the multi-query form
+                   // (then batch counts query rows: sequences x qrows)
+  int chunk;       // multi-query form: the state holds the whole blocks before the chunk
   float sigma;
   int batch, max_seq_len;
   int max_blocks;  // block table row stride
@@ -131,6 +134,14 @@ hipError_t launch_build(const Problem& p, const BuildLayout& L, const BuildArgs&
                         hipStream_t stream);
 
 // ---------------------------------------------------------------- append
-hipError_t launch_append(const Problem& p, const AppendArgs& a, hipStream_t stream);
+// Append of `count` tokens per sequence (k_new / v_new [batch, count, Hkv, D]):
+// kAppendWriteRows writes their page slots (and, with row_lens, each query
+// row's length T0 + 1 + i), kAppendFold folds the block they complete (at
+// most one: count <= B) into the state and statistics and sets
+// seq_lens_after.  A token append is count 1 with both.
+constexpr int kAppendWriteRows = 1;
+constexpr int kAppendFold = 2;
+hipError_t launch_append(const Problem& p, const AppendArgs& a, hipStream_t stream, int count = 1,
+                         int mode = kAppendWriteRows | kAppendFold, int32_t* row_lens = nullptr);
 
 }  // namespace hsla

@@ -12,7 +12,7 @@ import numpy as np
 import torch
 
 from . import (HSLA_BF16, HSLA_F32, HSLA_SEL_GROUPED, HSLA_SEL_PER_HEAD, HSLA_SEL_TOKEN, Config, Pool, State,
-               hsla_append_decode,
+               hsla_append_decode, hsla_prefill_chunk, hsla_prefill_chunk_workspace_size,
                hsla_append_token, hsla_build_state, hsla_build_workspace_size, hsla_decode,
                hsla_decode_workspace_size)
 
@@ -100,6 +100,31 @@ class DeviceCache:
                            self.batch, self.max_seq_len + 1, out, sel, self.decode_ws, stream=stream, prof=prof)
         self.cur = nxt
         self.host_lens += 1
+        return out, sel
+
+    def prefill_chunk(self, k_chunk: torch.Tensor, v_chunk: torch.Tensor, q: torch.Tensor,
+                      out: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None, stream=None):
+        """Append a chunk of Q tokens per sequence (k/v [batch, Q, Hkv, D]) and
+        decode each of its queries (q [batch, Q, Hq, D]) at its own position."""
+        cfg = self.cfg
+        Q = int(q.shape[1])
+        assert self.max_seq_len + Q <= self.capacity_len, "no room mapped for the chunk"
+        if out is None:
+            out = torch.empty((self.batch, Q, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=self.device)
+        if sel is None and cfg.top_k > 0:
+            sel = torch.empty((self.batch, Q, cfg.num_q_heads, cfg.top_k), dtype=torch.int32, device=self.device)
+        msl = self.max_seq_len + Q
+        key = (Q, msl)
+        if getattr(self, "_chunk_ws_key", None) != key:
+            n = hsla_prefill_chunk_workspace_size(cfg, self.batch, Q, msl)
+            assert n > 0, "chunk length not supported for this configuration"
+            self._chunk_ws = torch.empty(n, dtype=torch.uint8, device=self.device)
+            self._chunk_ws_key = key
+        nxt = 1 - self.cur
+        hsla_prefill_chunk(cfg, self.pool, self.state, k_chunk, v_chunk, self.lens[self.cur], self.lens[nxt], q,
+                           self.batch, Q, msl, out, sel, self._chunk_ws, stream=stream)
+        self.cur = nxt
+        self.host_lens += Q
         return out, sel
 
     def decode(self, q: torch.Tensor, out: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None,

@@ -260,6 +260,40 @@ hsla_status hsla_append_decode(const hsla_config* cfg, const hsla_kv_pool* pool,
                                float* out, int32_t* sel_idx, void* workspace, size_t workspace_bytes,
                                hipStream_t stream, hsla_profile* prof);
 
+/* Bytes of workspace hsla_prefill_chunk needs (0 on invalid arguments or
+ * an unsupported chunk).  Pure host function. */
+size_t hsla_prefill_chunk_workspace_size(const hsla_config* cfg, int32_t batch, int32_t q_len,
+                                         int32_t max_seq_len);
+
+/* Multi-query form: a chunk of q_len consecutive tokens per sequence is
+ * appended and each of its queries is decoded causally at its own position
+ * [SALSA abstract: the same sparse + window + linear partition at training
+ * and inference; SPLA Figure 1(a), "Recurrence"].  Query i of sequence b sits
+ * at position T0 = seq_lens_before[b] plus i, sees tokens 0 .. T0 + i, and
+ * gets exactly the output hsla_decode gives at length T0 + i + 1 (its own
+ * candidates, top-k, sinks, window and linear tail).  The same results as
+ * q_len rounds of hsla_append_decode, in three launches: the chunk's page
+ * slots, the q_len x batch decodes, then the fold of the block the chunk
+ * completed (at most one) into the state and statistics.
+ * k_chunk, v_chunk: device [batch, q_len, Hkv, head_dim] kv_dtype; the pages
+ *   of positions T0 .. T0 + q_len - 1 must be mapped by the caller.
+ * q: device [batch, q_len, Hq, head_dim] kv_dtype.
+ * seq_lens_before: device [batch], T0 >= 0 with T0 + q_len <= max_seq_len;
+ * seq_lens_after: device [batch], receives T0 + q_len; must not alias
+ *   seq_lens_before.
+ * out: device [batch, q_len, Hq, head_dim] float32; sel_idx: device
+ *   [batch, q_len, Hq, top_k] int32 or NULL (as for hsla_decode).
+ * Limits: 1 <= q_len <= min(block_size, window - block_size + 1), so that
+ *   every query's window covers the tokens between the state (whole blocks
+ *   before the chunk) and the query; block selection only
+ *   (HSLA_SEL_TOKEN -> HSLA_ERR_UNSUPPORTED).  state is required.
+ * workspace: at least hsla_prefill_chunk_workspace_size() bytes. */
+hsla_status hsla_prefill_chunk(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
+                               const void* k_chunk, const void* v_chunk, const int32_t* seq_lens_before,
+                               int32_t* seq_lens_after, const void* q, int32_t batch, int32_t q_len,
+                               int32_t max_seq_len, float* out, int32_t* sel_idx, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

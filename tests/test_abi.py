@@ -178,3 +178,54 @@ def test_append_decode_rejects_bad_pointers_and_sizes():
     assert call_append_decode(cfg(linear_tail=0), st=state(S=0)) == E
     assert call_append_decode(c, p=pool(max_blocks_per_seq=100)) == E
     assert call_append_decode(c, ws_bytes=16) == H.HSLA_ERR_WORKSPACE
+
+
+def call_prefill_chunk(c, p=None, st=None, k=FAKE, v=FAKE, before=FAKE, after=FAKE + 256, q=FAKE, batch=8,
+                       q_len=16, max_len=32768, out=FAKE, sel=FAKE, ws=FAKE, ws_bytes=1 << 40, null_state=False):
+    lib = H.load()
+    sp = None if null_state else ctypes.byref(st or state())
+    return lib.hsla_prefill_chunk(ctypes.byref(c.c()), ctypes.byref(p or pool()), sp, k, v, before, after, q,
+                                  batch, q_len, max_len, out, sel, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad,code", BAD_CONFIGS)
+def test_prefill_chunk_rejects_bad_configs(bad, code):
+    assert call_prefill_chunk(cfg(**bad)) == code
+    assert H.hsla_prefill_chunk_workspace_size(cfg(**bad), 8, 16, 32768) == 0
+
+
+def test_prefill_chunk_limits_and_workspace():
+    c = cfg()
+    E = H.HSLA_ERR_INVALID_ARG
+    # the chunk length: 1 .. min(block size, window - block size + 1)
+    assert H.hsla_prefill_chunk_workspace_size(c, 8, 0, 32768) == 0
+    assert H.hsla_prefill_chunk_workspace_size(c, 8, 65, 32768) == 0                    # > block size
+    assert H.hsla_prefill_chunk_workspace_size(cfg(window=96), 8, 34, 32768) == 0       # > W - B + 1 = 33
+    assert H.hsla_prefill_chunk_workspace_size(cfg(window=96), 8, 33, 32768) > 0
+    assert call_prefill_chunk(c, q_len=0) == E
+    assert call_prefill_chunk(c, q_len=65) == E
+    assert call_prefill_chunk(cfg(window=96), q_len=34) == E
+    # token-level selection has no chunk form here
+    assert H.hsla_prefill_chunk_workspace_size(cfg(selection=H.HSLA_SEL_TOKEN), 8, 16, 32768) == 0
+    assert call_prefill_chunk(cfg(selection=H.HSLA_SEL_TOKEN)) == H.HSLA_ERR_UNSUPPORTED
+    # the chunk's decode covers batch x q_len rows: its workspace exceeds one decode's
+    one = H.hsla_decode_workspace_size(c, 8, 32768)
+    ws = H.hsla_prefill_chunk_workspace_size(c, 8, 16, 32768)
+    assert ws > one and ws >= H.hsla_decode_workspace_size(c, 8 * 16, 32768) + 8 * 16 * 4
+    assert call_prefill_chunk(c, ws_bytes=ws - 1) == H.HSLA_ERR_WORKSPACE
+
+
+def test_prefill_chunk_rejects_bad_pointers():
+    c = cfg()
+    E = H.HSLA_ERR_INVALID_ARG
+    assert call_prefill_chunk(c, after=FAKE) == E          # aliases seq_lens_before
+    assert call_prefill_chunk(c, after=0) == E
+    assert call_prefill_chunk(c, before=0) == E
+    assert call_prefill_chunk(c, k=0) == E
+    assert call_prefill_chunk(c, v=FAKE + 2) == E
+    assert call_prefill_chunk(c, q=0) == E
+    assert call_prefill_chunk(c, out=FAKE + 4) == E
+    assert call_prefill_chunk(c, sel=FAKE + 2) == E
+    assert call_prefill_chunk(c, null_state=True) == E
+    assert call_prefill_chunk(c, p=pool(max_blocks_per_seq=100)) == E
+    assert call_prefill_chunk(c, batch=0) == E

@@ -1,0 +1,113 @@
+"""hsla_prefill_chunk (the multi-query form) against the oracle.
+
+Every query row of the chunk is compared with the oracle's decode at its
+own position (decode_chunk_head: query i of sequence b at length T0 + i + 1),
+with the selection rule of the decode tests.  The chunk's page slots are
+filled with a wrong value before the call, so the rows must come from the
+chunk's keys and values.  The cache after the chunk (pages, block statistics,
+state, lengths) must be bitwise equal to the one q_len hsla_append_token
+calls leave, including chunks that complete a block.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from test_gpu_parity import _announce, _wl, cfg_of, check_case
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # collected on CPU hosts, skipped there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from hybrid_sparse_linear_block_amd.device import DeviceCache, to_device  # noqa: E402
+
+# T0 (the cache's length before the chunk) and the chunk length Q per case;
+# sequence 0 completes a block inside the chunk in every case but one
+CASES = {
+    "bf16_g4": (dict(), (1530, 1137), 16),
+    "bf16_g4_q1_completes": (dict(), (1535, 1203), 1),
+    "f32_d64_b16": (dict(kv_dtype=W.F32, head_dim=64, block_size=16, window=64, top_k=12), (1471, 1203), 16),
+    "bf16_g8": (dict(num_q_heads=16, num_kv_heads=2), (1530, 1203), 8),
+    "grouped": (dict(grouped=1), (1530, 1137), 16),
+    "no_linear_tail": (dict(linear_tail=0), (1530, 1137), 16),
+    "deterministic": (dict(deterministic=1), (1530, 1137), 16),
+    "no_candidates": (dict(), (200, 37), 16),
+    "ragged_b1": (dict(batch=3, num_q_heads=8, num_kv_heads=8, top_k=8), (2043, 300, 1031), 16),
+    "long_window_q64": (dict(window=512), (3000, 1986), 64),
+}
+
+
+def _setup(name):
+    kw, t0, Q = CASES[name]
+    lens = tuple(t + Q for t in t0)
+    wl = _wl(f"chunk_{name}", 80, seq_lens=lens, **kw)
+    inp = W.make_inputs(wl)
+    Hkv, G, D = wl.num_kv_heads, wl.group, wl.head_dim
+    # the chunk's keys/values (the sequences' last Q tokens) and queries
+    kc = np.stack([np.stack([np.stack([inp["pairs"][(b, g)][0][t0[b] + i] for g in range(Hkv)])
+                             for i in range(Q)]) for b in range(wl.batch)])
+    vc = np.stack([np.stack([np.stack([inp["pairs"][(b, g)][1][t0[b] + i] for g in range(Hkv)])
+                             for i in range(Q)]) for b in range(wl.batch)])
+    rng = np.random.default_rng([777, wl.cid])
+    qf = rng.standard_normal((wl.batch, Q, wl.num_q_heads, D)).astype(np.float32)
+    qc = W.bf16_round(qf) if wl.kv_dtype == W.BF16 else qf
+    # a wrong value in the chunk's page slots
+    bad = np.uint16(0x4040) if wl.kv_dtype == W.BF16 else np.float32(3.0)
+    for b in range(wl.batch):
+        for i in range(Q):
+            t = t0[b] + i
+            page = inp["block_table"][b, t // wl.block_size]
+            inp["k_pages"][page, :, t % wl.block_size, :] = bad
+            inp["v_pages"][page, :, t % wl.block_size, :] = bad
+    return wl, inp, np.asarray(t0, np.int64), Q, kc, vc, qc
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_chunk_rows_match_the_oracle(name):
+    wl, inp, t0, Q, kc, vc, qc = _setup(name)
+    _announce(wl, f"prefill chunk Q={Q} from T0={t0.tolist()}")
+    lens = t0 + Q
+    dc = DeviceCache(cfg_of(wl), inp["k_pages"], inp["v_pages"], inp["block_table"], t0, capacity_len=int(lens.max()))
+    dc.build()
+    out, sel = dc.prefill_chunk(to_device(kc), to_device(vc), to_device(qc))
+    torch.cuda.synchronize()
+    assert dc.seq_lens.cpu().numpy().tolist() == lens.tolist()
+    out = out.cpu().numpy().reshape(wl.batch * Q, wl.num_q_heads, wl.head_dim)
+    sel = None if sel is None else sel.cpu().numpy().reshape(wl.batch * Q, wl.num_q_heads, wl.top_k)
+
+    # query row r = b Q + i is a decode of sequence b at length T0_b + i + 1
+    rows = dataclasses.replace(wl, batch=wl.batch * Q, seq_lens=tuple(int(t0[r // Q]) + r % Q + 1
+                                                                       for r in range(wl.batch * Q)))
+    inp_rows = {"q": qc.reshape(wl.batch * Q, wl.num_q_heads, wl.head_dim), "block_table": None}
+
+    def pair_data(r, g):
+        K, V = inp["pairs"][(r // Q, g)]
+        L = int(t0[r // Q]) + r % Q + 1
+        return K[:L], V[:L]
+
+    heads = [(r, h) for r in range(wl.batch * Q) for h in range(wl.num_q_heads)]
+    worst, flips = check_case(rows, inp_rows, None, out, sel, heads=heads, check_build=False, pair_data=pair_data)
+    print(f"  worst row error {worst:.3e}, near-tie flips {flips}")
+
+
+@pytest.mark.parametrize("name", ["bf16_g4", "f32_d64_b16", "bf16_g4_q1_completes", "no_linear_tail"])
+def test_chunk_leaves_the_cache_q_appends_leave(name):
+    wl, inp, t0, Q, kc, vc, qc = _setup(name)
+    _announce(wl, f"prefill chunk Q={Q} vs {Q} appends")
+    cap = int((t0 + Q).max())
+    a = DeviceCache(cfg_of(wl), inp["k_pages"], inp["v_pages"], inp["block_table"], t0, capacity_len=cap)
+    b = DeviceCache(cfg_of(wl), inp["k_pages"], inp["v_pages"], inp["block_table"], t0, capacity_len=cap)
+    a.build()
+    b.build()
+    a.prefill_chunk(to_device(kc), to_device(vc), to_device(qc))
+    for i in range(Q):
+        b.append(to_device(np.ascontiguousarray(kc[:, i])), to_device(np.ascontiguousarray(vc[:, i])))
+    torch.cuda.synchronize()
+    assert np.array_equal(a.host_lens, b.host_lens)
+    assert torch.equal(a.seq_lens, b.seq_lens)
+    for t in ("k_pages", "v_pages", "blk_mean", "blk_var", "S", "z", "sv"):
+        assert torch.equal(getattr(a, t), getattr(b, t)), t
