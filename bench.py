@@ -54,6 +54,8 @@ def parse(argv=None):
                     help="fixed split of the attention work (bitwise reproducible) instead of the dynamic one")
     ap.add_argument("--grouped", action="store_true",
                     help="the grouped-selection variant (one block selection per kv head)")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="the multi-query form: chunks of this many tokens per sequence (hsla_prefill_chunk)")
     ap.add_argument("--tokens", action="store_true",
                     help="the token-level variant: top_k single tokens per head (top_k x block size of the "
                          "workload's block budget), scored by their keys")
@@ -493,6 +495,103 @@ def setup(args, extra_steps):
     return dict(wl=wl, inp=inp, caches=caches, preps=preps, qs=qs, build_ms=build_ms, hip=hip, stream=stream, R=R)
 
 
+def chunk_bytes(wl, t0, Q, sel):
+    """Algorithmic bytes of one chunk of Q queries per sequence (multi-query
+    form): every exact page once per (sequence, kv head) for the whole chunk
+    (the union over the Q rows and G heads of sinks, windows and selected
+    blocks), candidate statistics and state once, queries, outputs, the
+    chunk's rows written and the block fold amortised.  Also the bytes of Q
+    separate single-query decodes, which is what query rows read one by one."""
+    d, G, e, B = wl.head_dim, wl.group, wl.elem_bytes, wl.block_size
+    need = rows = 0
+    for b in range(wl.batch):
+        T_end = int(t0[b]) + Q
+        for g in range(wl.num_kv_heads):
+            mask = np.zeros(T_end, bool)
+            mask[:min(wl.num_sink, T_end)] = True
+            mask[max(0, int(t0[b]) + 1 - wl.window):] = True
+            for i in range(Q):
+                for blk in sel[b, i, g * G:(g + 1) * G].ravel():
+                    if blk >= 0:
+                        mask[blk * B:(blk + 1) * B] = True
+                L = int(t0[b]) + i + 1
+                rows += (n_cand(L, wl) * 2 * d * 4 + ((d * d + 2 * d) * 4 if wl.linear_tail else 0)
+                         + union_tokens(L, wl, sel[b, i, g * G:(g + 1) * G]) * 2 * d * e)
+            need += (n_cand(T_end, wl) * 2 * d * 4 + ((d * d + 2 * d) * 4 if wl.linear_tail else 0)
+                     + int(mask.sum()) * 2 * d * e)
+            io = Q * G * d * (e + 4) + Q * G * wl.top_k * 4 + 2 * Q * d * e \
+                + int((B * 2 * d * e + 2 * (d * d + 2 * d) * 4) * Q / B)
+            need += io
+            rows += io
+    return need, rows
+
+
+def chunk_main(args):
+    """The multi-query form: a chunk of Q tokens per sequence appended and
+    every one of its queries decoded (hsla_prefill_chunk), at the workload's
+    context.  value = query tokens per second."""
+    import torch
+
+    import workloads as W
+    from hybrid_sparse_linear_block_amd.device import DeviceCache, config_for, to_device
+
+    torch.cuda.set_device(0)
+    wl = workload(args.workload, args.grouped, False)
+    Q, steps, warm, R = args.chunk, args.steps, args.warmup, max(1, args.replicas)
+    per_rep = -(-(steps + warm) // R) + 1
+    room = per_rep * Q
+    wl = W.dataclasses.replace(wl, append_room=1 + -(-room // wl.block_size))
+    inp = W.make_inputs(wl, keep_pairs=False)
+    cfg = config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
+                     wl.window, wl.linear_tail, wl.kv_dtype, grouped=wl.grouped,
+                     deterministic=int(args.deterministic))
+    cap = max(wl.seq_lens) + room + 1
+    caches = []
+    for r in range(R):
+        dc = DeviceCache(cfg, inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"], capacity_len=cap)
+        dc.build()
+        caches.append(dc)
+    rng = np.random.default_rng([99, Q])
+    cvt = (lambda x: W.bf16_round(x)) if wl.kv_dtype == W.BF16 else (lambda x: x.astype(np.float32))
+    kc = to_device(cvt(rng.standard_normal((wl.batch, Q, wl.num_kv_heads, wl.head_dim)).astype(np.float32)))
+    vc = to_device(cvt(rng.standard_normal((wl.batch, Q, wl.num_kv_heads, wl.head_dim)).astype(np.float32)))
+    qc = to_device(cvt(rng.standard_normal((wl.batch, Q, wl.num_q_heads, wl.head_dim)).astype(np.float32)))
+    outs = [torch.empty((wl.batch, Q, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+            for _ in range(R)]
+    sels = [torch.empty((wl.batch, Q, wl.num_q_heads, wl.top_k), dtype=torch.int32, device="cuda")
+            for _ in range(R)]
+    t0_last = caches[0].host_lens.copy()
+    caches[0].prefill_chunk(kc, vc, qc, outs[0], sels[0])
+    torch.cuda.synchronize()
+    need, rows = chunk_bytes(wl, t0_last, Q, sels[0].cpu().numpy())
+    for i in range(warm):
+        caches[(i + 1) % R].prefill_chunk(kc, vc, qc, outs[(i + 1) % R], sels[(i + 1) % R])
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        r = (warm + 1 + i) % R
+        caches[r].prefill_chunk(kc, vc, qc, outs[r], sels[r])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    us = wall / steps * 1e6
+    res = {
+        "metric": "multi-query chunk: query tokens/s at the workload's context", "value": round(wl.batch * Q / (wall / steps), 1),
+        "unit": "query tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": round(us / 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.kv_dtype == W.BF16 else "f32", "accumulate": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "ctx": int(max(wl.seq_lens)), "chunk": Q,
+                   "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                   "block": wl.block_size, "top_k": wl.top_k, "replicas": R,
+                   "selection": "grouped" if wl.grouped else "per_head",
+                   "step": "hsla_prefill_chunk (chunk append + Q query rows + fold)"},
+        "us_per_step": round(us, 2),
+        "step_roofline": {"bytes": need, "achieved": round(need / (us * 1e-6) / 1e9, 1),
+                          "frac": round(need / (us * 1e-6) / 8e12, 4), "unit": "GB/s",
+                          "bytes_as_q_decodes": rows},
+    }
+    print(json.dumps(res))
+
+
 def hybrid_main(args):
     """Build + 32-layer hybrid decode at 32768 tokens, batch 1: every layer
     has its own cache, budget and linear-tail switch; a step is one append +
@@ -674,6 +773,9 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "hybrid32_32k":
         hybrid_main(args)
+        return
+    if args.chunk:
+        chunk_main(args)
         return
     if args.traffic_run:
         traffic_run(args)

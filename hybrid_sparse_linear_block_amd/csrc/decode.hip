@@ -23,6 +23,10 @@
 //      selected").
 //   4. k_merge          log-sum-exp combination of the splits and the
 //      residual linear part into the normalised output.
+//
+// Multi-query form (qrows > 1): the batch counts query rows, row b being
+// query b % qrows of sequence b / qrows at its own length; every stage runs
+// per row, reading the sequence's block-table row and linear state.
 #include <math.h>
 
 #include <algorithm>

@@ -113,7 +113,7 @@ class DeviceCache:
             out = torch.empty((self.batch, Q, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=self.device)
         if sel is None and cfg.top_k > 0:
             sel = torch.empty((self.batch, Q, cfg.num_q_heads, cfg.top_k), dtype=torch.int32, device=self.device)
-        msl = self.max_seq_len + Q
+        msl = self.capacity_len   # one workspace for every chunk up to the mapped capacity
         key = (Q, msl)
         if getattr(self, "_chunk_ws_key", None) != key:
             n = hsla_prefill_chunk_workspace_size(cfg, self.batch, Q, msl)
