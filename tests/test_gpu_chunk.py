@@ -111,3 +111,56 @@ def test_chunk_leaves_the_cache_q_appends_leave(name):
     assert torch.equal(a.seq_lens, b.seq_lens)
     for t in ("k_pages", "v_pages", "blk_mean", "blk_var", "S", "z", "sv"):
         assert torch.equal(getattr(a, t), getattr(b, t)), t
+
+
+def test_chunk_full_size_llama8b_32k():
+    # the configuration `bench.py --chunk 16` times: batch 8 at 32768 tokens,
+    # 32q/8kv, d 128, B 64, k 16; sampled (sequence, kv head) pairs and three
+    # query rows of each against the oracle, every row for the properties
+    # that hold at any size
+    Q = 16
+    wl = W.dataclasses.replace(W.llama8b_32k(), append_room=2)
+    _announce(wl, f"full size, prefill chunk Q={Q}, sampled pairs")
+    inp = W.make_inputs(wl, keep_pairs=False)
+    t0 = np.asarray(wl.seq_lens, np.int64)
+    dc = DeviceCache(cfg_of(wl), inp["k_pages"], inp["v_pages"], inp["block_table"], t0,
+                     capacity_len=int(t0.max()) + Q)
+    dc.build()
+    rng = np.random.default_rng([99, Q])
+    kc, vc = (W.bf16_round(rng.standard_normal((wl.batch, Q, wl.num_kv_heads, wl.head_dim)).astype(np.float32))
+              for _ in range(2))
+    qc = W.bf16_round(rng.standard_normal((wl.batch, Q, wl.num_q_heads, wl.head_dim)).astype(np.float32))
+    out, sel = dc.prefill_chunk(to_device(kc), to_device(vc), to_device(qc))
+    torch.cuda.synchronize()
+    out, sel = out.cpu().numpy(), sel.cpu().numpy()
+    assert np.isfinite(out).all()
+    B = wl.block_size
+    for b in range(wl.batch):
+        for i in range(Q):
+            L = int(t0[b]) + i + 1
+            n_cand = -(-(L - wl.window) // B) - wl.num_sink // B
+            for h in range(wl.num_q_heads):
+                row = [x for x in sel[b, i, h].tolist() if x >= 0]
+                assert row == sorted(set(row)) and len(row) == min(wl.top_k, n_cand), (b, i, h)
+                assert all(wl.num_sink // B <= x < wl.num_sink // B + n_cand for x in row), (b, i, h)
+
+    rows = dataclasses.replace(wl, batch=wl.batch * Q, seq_lens=tuple(int(t0[r // Q]) + r % Q + 1
+                                                                       for r in range(wl.batch * Q)))
+    full = {}
+
+    def pair_data(r, g):
+        b, i = r // Q, r % Q
+        if (b, g) not in full:
+            K, V = W.gen_pair(wl, b, g, inp["q"])
+            full[(b, g)] = (np.concatenate([K[:t0[b]], kc[b, :, g]]), np.concatenate([V[:t0[b]], vc[b, :, g]]))
+        K, V = full[(b, g)]
+        return K[:int(t0[b]) + i + 1], V[:int(t0[b]) + i + 1]
+
+    G = wl.group
+    pairs = [(0, 0), (wl.batch // 2, wl.num_kv_heads // 2), (wl.batch - 1, wl.num_kv_heads - 1)]
+    heads = [(b * Q + i, h) for b, g in pairs for i in (0, Q // 2, Q - 1) for h in range(g * G, (g + 1) * G)]
+    inp_rows = {"q": qc.reshape(wl.batch * Q, wl.num_q_heads, wl.head_dim), "block_table": None}
+    worst, flips = check_case(rows, inp_rows, None, out.reshape(wl.batch * Q, wl.num_q_heads, wl.head_dim),
+                              sel.reshape(wl.batch * Q, wl.num_q_heads, wl.top_k), heads=heads,
+                              check_build=False, pair_data=pair_data)
+    print(f"  worst row error {worst:.3e}, near-tie flips {flips}")
