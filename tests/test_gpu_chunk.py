@@ -164,3 +164,55 @@ def test_chunk_full_size_llama8b_32k():
                               sel.reshape(wl.batch * Q, wl.num_q_heads, wl.top_k), heads=heads,
                               check_build=False, pair_data=pair_data)
     print(f"  worst row error {worst:.3e}, near-tie flips {flips}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f32"])
+def test_prefill_from_empty_in_chunks(kv):
+    # a prefill from nothing as chunked calls: T0 = (0, 3), eight chunks of
+    # 16 (B 16, W 64), so that later rows have candidates, a selection and a
+    # linear tail; every row of every chunk against the oracle
+    Q, n_chunks, t_start = 16, 8, (0, 3)
+    kw = dict(kv_dtype=W.BF16 if kv == "bf16" else W.F32, head_dim=64, block_size=16, window=64, top_k=2,
+              num_sink=4)
+    final = tuple(t + Q * n_chunks for t in t_start)
+    wl = _wl(f"chunk_from_empty_{kv}", 81, seq_lens=final, **kw)
+    _announce(wl, f"prefill from {list(t_start)} in {n_chunks} chunks of {Q}")
+    inp = W.make_inputs(wl)
+    bad = np.uint16(0x4040) if wl.kv_dtype == W.BF16 else np.float32(3.0)
+    for b in range(wl.batch):
+        for t in range(t_start[b], final[b]):
+            page = inp["block_table"][b, t // wl.block_size]
+            inp["k_pages"][page, :, t % wl.block_size, :] = bad
+            inp["v_pages"][page, :, t % wl.block_size, :] = bad
+    t0 = np.asarray(t_start, np.int64)
+    dc = DeviceCache(cfg_of(wl), inp["k_pages"], inp["v_pages"], inp["block_table"], t0,
+                     capacity_len=int(max(final)))
+    dc.build()
+    rng = np.random.default_rng([5150, wl.cid])
+    worst_all = 0.0
+    for c in range(n_chunks):
+        kc = np.stack([np.stack([np.stack([inp["pairs"][(b, g)][0][t0[b] + i] for g in range(wl.num_kv_heads)])
+                                 for i in range(Q)]) for b in range(wl.batch)])
+        vc = np.stack([np.stack([np.stack([inp["pairs"][(b, g)][1][t0[b] + i] for g in range(wl.num_kv_heads)])
+                                 for i in range(Q)]) for b in range(wl.batch)])
+        qf = rng.standard_normal((wl.batch, Q, wl.num_q_heads, wl.head_dim)).astype(np.float32)
+        qc = W.bf16_round(qf) if wl.kv_dtype == W.BF16 else qf
+        out, sel = dc.prefill_chunk(to_device(kc), to_device(vc), to_device(qc))
+        torch.cuda.synchronize()
+        assert dc.seq_lens.cpu().numpy().tolist() == (t0 + Q).tolist()
+        R = wl.batch * Q
+        rows = dataclasses.replace(wl, batch=R, seq_lens=tuple(int(t0[r // Q]) + r % Q + 1 for r in range(R)))
+
+        def pair_data(r, g, t0=t0.copy()):
+            K, V = inp["pairs"][(r // Q, g)]
+            L = int(t0[r // Q]) + r % Q + 1
+            return K[:L], V[:L]
+
+        heads = [(r, h) for r in range(R) for h in range(wl.num_q_heads)]
+        worst, _ = check_case(rows, {"q": qc.reshape(R, wl.num_q_heads, wl.head_dim), "block_table": None}, None,
+                              out.cpu().numpy().reshape(R, wl.num_q_heads, wl.head_dim),
+                              sel.cpu().numpy().reshape(R, wl.num_q_heads, wl.top_k), heads=heads,
+                              check_build=False, pair_data=pair_data)
+        worst_all = max(worst_all, worst)
+        t0 = t0 + Q
+    print(f"  worst row error over {n_chunks} chunks {worst_all:.3e}")
