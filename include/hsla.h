@@ -271,10 +271,13 @@ size_t hsla_prefill_chunk_workspace_size(const hsla_config* cfg, int32_t batch, 
  * and inference; SPLA Figure 1(a), "Recurrence"].  Query i of sequence b sits
  * at position T0 = seq_lens_before[b] plus i, sees tokens 0 .. T0 + i, and
  * gets exactly the output hsla_decode gives at length T0 + i + 1 (its own
- * candidates, top-k, sinks, window and linear tail).  The same results as
- * q_len rounds of hsla_append_decode, in three launches: the chunk's page
- * slots, the q_len x batch decodes, then the fold of the block the chunk
- * completed (at most one) into the state and statistics.
+ * candidates, top-k, sinks, window and linear tail): what q_len rounds of
+ * hsla_append_decode compute, up to rounding (every query's linear part is
+ * taken from the state as it stood before the chunk), in three launches: the
+ * chunk's page slots, the q_len x batch decodes, then the fold of the block
+ * the chunk completed (at most one) into the state and statistics.  The
+ * cache afterwards (pages, statistics, state, lengths) is bitwise what
+ * q_len hsla_append_token calls leave.
  * k_chunk, v_chunk: device [batch, q_len, Hkv, head_dim] kv_dtype; the pages
  *   of positions T0 .. T0 + q_len - 1 must be mapped by the caller.
  * q: device [batch, q_len, Hq, head_dim] kv_dtype.
