@@ -216,3 +216,75 @@ def test_prefill_from_empty_in_chunks(kv):
         worst_all = max(worst_all, worst)
         t0 = t0 + Q
     print(f"  worst row error over {n_chunks} chunks {worst_all:.3e}")
+
+
+@pytest.mark.parametrize("deterministic", [1, 0])
+def test_chunk_graph_replays_match_eager_chunks(deterministic):
+    # two chunks per captured graph (the ping-ponged length buffers return),
+    # replayed three times with eager torch work and synchronisation in
+    # between; every replay against the eager chunks of the same lengths
+    Q, replays = 16, 3
+    t_start = (1530, 1137)
+    steps = 2 * replays
+    wl = _wl("chunk_graph", 82, deterministic=deterministic, append_room=4,
+             seq_lens=tuple(t + Q * steps for t in t_start))
+    _announce(wl, f"prefill chunk Q={Q} in a HIP graph, deterministic={deterministic}")
+    inp = W.make_inputs(wl, keep_pairs=False)
+    t0 = np.asarray(t_start, np.int64)
+    cap = int(max(wl.seq_lens))
+    rng = np.random.default_rng([31, deterministic])
+    cvt = W.bf16_round
+    kc = to_device(cvt(rng.standard_normal((wl.batch, Q, wl.num_kv_heads, wl.head_dim)).astype(np.float32)))
+    vc = to_device(cvt(rng.standard_normal((wl.batch, Q, wl.num_kv_heads, wl.head_dim)).astype(np.float32)))
+    qc = to_device(cvt(rng.standard_normal((wl.batch, Q, wl.num_q_heads, wl.head_dim)).astype(np.float32)))
+    caches = [DeviceCache(cfg_of(wl), inp["k_pages"], inp["v_pages"], inp["block_table"], t0, capacity_len=cap)
+              for _ in range(2)]
+    for dc in caches:
+        dc.build()
+    eager, graphed = caches
+    outs = [torch.empty((wl.batch, Q, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+            for _ in range(2)]
+    sels = [torch.empty((wl.batch, Q, wl.num_q_heads, wl.top_k), dtype=torch.int32, device="cuda") for _ in range(2)]
+    want = []
+    for s in range(steps):
+        o, sl = eager.prefill_chunk(kc, vc, qc)
+        if s % 2 == 1:
+            torch.cuda.synchronize()
+            want.append((o.cpu().numpy(), sl.cpu().numpy()))
+
+    # the captured cache takes the workspace a call on a third cache
+    # allocated outside the capture (same chunk length and capacity), so
+    # that nothing is allocated while capturing
+    graphed2 = DeviceCache(cfg_of(wl), inp["k_pages"], inp["v_pages"], inp["block_table"], t0, capacity_len=cap)
+    graphed2.build()
+    graphed2.prefill_chunk(kc, vc, qc, outs[0], sels[0])
+    torch.cuda.synchronize()
+    graphed.__dict__.update({"_chunk_ws": graphed2._chunk_ws, "_chunk_ws_key": graphed2._chunk_ws_key})
+    gs = torch.cuda.Stream()
+    saved = (graphed.cur, graphed.host_lens.copy())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    gs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=gs):
+        graphed.prefill_chunk(kc, vc, qc, outs[0], sels[0], stream=gs.cuda_stream)
+        graphed.prefill_chunk(kc, vc, qc, outs[1], sels[1], stream=gs.cuda_stream)
+    graphed.cur, graphed.host_lens[:] = saved
+    noise = torch.randn(512, 512, device="cuda")
+    for r in range(replays):
+        graph.replay()
+        torch.cuda.synchronize()
+        go, gsel = outs[1].cpu().numpy(), sels[1].cpu().numpy()
+        noise = noise @ noise.T / 512.0
+        torch.cuda.synchronize()
+        wo, wsel = want[r]
+        assert np.array_equal(gsel, wsel), r
+        if deterministic:
+            assert np.array_equal(go, wo), r
+        else:
+            err = np.abs(go - wo).max(axis=-1) / np.abs(wo).max(axis=-1)
+            assert err.max() < 1e-5, (r, float(err.max()))
+    graphed.host_lens += steps * Q
+    assert np.array_equal(graphed.host_lens, eager.host_lens)
+    assert torch.equal(graphed.lens[graphed.cur], eager.lens[eager.cur])
+    for t in ("k_pages", "v_pages", "blk_mean", "blk_var", "S", "z", "sv"):
+        assert torch.equal(getattr(graphed, t), getattr(eager, t)), t
