@@ -763,7 +763,7 @@ def main():
         print(profile_summary(*args.profile_summary))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus above 1 is not supported "
+        print("bench.py: the library runs on exactly one GPU; --gpus above 1 is not supported "
               "(the path shards by (sequence, kv head) with no exchange, see the design notes).", file=sys.stderr)
         sys.exit(2)
     import torch
