@@ -764,7 +764,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: the library runs on exactly one GPU; --gpus above 1 is not supported "
-              "(the path shards by (sequence, kv head) with no exchange, see the design notes).", file=sys.stderr)
+              "(the path would shard by (sequence, kv head), with no exchange between GPUs).", file=sys.stderr)
         sys.exit(2)
     import torch
 
