@@ -45,8 +45,9 @@ struct BlockStatsLds {
   float mean[D];
 };
 
-// Statistics of the block the new token fills (SPLA, section "Method": the
-// mean and the per-channel variance of the block's keys): rows [0, B) of
+// Statistics of the block the new token fills (SPLA, section "Principled
+// Block Selection via Taylor Expansion": the mean and the per-channel
+// variance of the block's keys): rows [0, B) of
 // the page-head tile at row0 of k_pages, row `last` taken from k_new at
 // nbase (its page write may not have landed).  NT threads = D/8 channel
 // groups x (NT / (D/8)) row groups; each thread loads its rows as
@@ -54,7 +55,7 @@ struct BlockStatsLds {
 // The second pass re-reads the rows (cache hits) for the squared deviations
 // from the mean.  Every thread of the workgroup must call it.
 template <typename KV, int D, int NT>
-__device__ void filled_block_stats(const void* k_pages, const void* k_new, size_t row0, int last, size_t nbase,
+__device__ __forceinline__ void filled_block_stats(const void* k_pages, const void* k_new, size_t row0, int last, size_t nbase,
                                    int B, float* mean_out, float* var_out, BlockStatsLds<NT, D>& s) {
   constexpr int CG = D / 8;      // channel groups of 8
   constexpr int RG = NT / CG;    // row groups
@@ -146,26 +147,30 @@ __device__ __forceinline__ void stage_block_rows(const CompletedBlock& cb, int j
   using F = FoldStage<KV, D>;
   constexpr int PER = (2 * F::kRows * F::kVec + NT - 1) / NT;
   const int per_kv = n * F::kVec;
-  uint4 buf[PER];
+  // every slot loads (past the rows: the last one again), so that buf stays
+  // in registers (a native vector type: HIP's uint4 is a union, which keeps
+  // the array on the stack)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 buf[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
-    const int idx = static_cast<int>(threadIdx.x) + p * NT;
+    const int idx = min(static_cast<int>(threadIdx.x) + p * NT, 2 * per_kv - 1);
     const int kv = idx < per_kv ? 0 : 1;
     const int rem = idx - kv * per_kv;
     const int j = rem / F::kVec;
     const int c16 = rem % F::kVec;
-    if (idx < 2 * per_kv) {
-      const char* row = kv ? block_row<KV, D>(cb.v_pages, cb.v_new, cb, j0 + j)
-                           : block_row<KV, D>(cb.k_pages, cb.k_new, cb, j0 + j);
-      buf[p] = reinterpret_cast<const uint4*>(row)[c16];
-    }
+    const char* row = kv ? block_row<KV, D>(cb.v_pages, cb.v_new, cb, j0 + j)
+                         : block_row<KV, D>(cb.k_pages, cb.k_new, cb, j0 + j);
+    buf[p] = reinterpret_cast<const u32x4*>(row)[c16];
   }
+  // slots past the rows store the last row's vector again: the same value
+  // to the same place as its own thread
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
-    const int idx = static_cast<int>(threadIdx.x) + p * NT;
+    const int idx = min(static_cast<int>(threadIdx.x) + p * NT, 2 * per_kv - 1);
     const int kv = idx < per_kv ? 0 : 1;
     const int rem = idx - kv * per_kv;
-    if (idx < 2 * per_kv) lds[kv * F::kRows * F::kVec + rem] = buf[p];
+    reinterpret_cast<u32x4*>(lds)[kv * F::kRows * F::kVec + rem] = buf[p];
   }
 }
 
@@ -179,7 +184,7 @@ __device__ __forceinline__ void stage_block_rows(const CompletedBlock& cb, int j
 // sum runs in row order, then is added once.  Every thread of the
 // workgroup must call it.
 template <typename KV, int D, int NT, int NR, int RG>
-__device__ void fold_completed_block(const CompletedBlock& cb, uint4* lds, float4 (&srow)[NR], int r_first, int col4,
+__device__ __forceinline__ void fold_completed_block(const CompletedBlock& cb, uint4* lds, float4 (&srow)[NR], int r_first, int col4,
                                      int zrow, float& z, int svcol, float& sv) {
   using F = FoldStage<KV, D>;
   float4 acc[NR];

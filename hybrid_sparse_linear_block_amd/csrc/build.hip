@@ -9,7 +9,7 @@
 // the chunk are staged in LDS; the workgroup writes the statistics of every
 // full block in the chunk and a chunk partial of S, z, sv to the workspace.
 // For bf16 keys/values the d x d contraction K^T V runs on MFMA
-// (v_mfma_f32_32x32x8_bf16, fp32 accumulation, exact bf16 products); tiles are
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation, exact bf16 products); tiles are
 // stored channel-major in LDS so that each lane's MFMA operand (4 consecutive
 // tokens of one channel) is one 8-byte LDS read.  fp32 keys/values use fp32
 // FMAs on VALU.

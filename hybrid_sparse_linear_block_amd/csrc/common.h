@@ -9,6 +9,22 @@ namespace hsla {
 constexpr int kWave = 64;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Loads through an explicit address space.  A pointer whose address space
+// the compiler cannot infer (one chosen between two buffers, or one that may
+// point to LDS or to global memory) becomes a flat access, which counts on
+// both the vector-memory and the LDS counters: every later LDS access then
+// waits for it, and so for every global load issued before it.
+template <typename T>
+__device__ __forceinline__ T ld_global(const void* p) {
+  return *(const __attribute__((address_space(1))) T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ T ld_lds(const void* p) {
+  return *(const __attribute__((address_space(3))) T*)(p);
+}
 
 // ---------------------------------------------------------------------------
 // Storage formats.  bf16 values are carried as raw 16-bit patterns; a bf16

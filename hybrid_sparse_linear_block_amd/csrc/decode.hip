@@ -125,6 +125,27 @@ struct DecodeParams {
 
 __device__ __forceinline__ int clamp_len(int T, int max_len) { return min(max(T, 1), max_len); }
 
+// Data handed between workgroups of one launch goes through agent-scope
+// atomic stores and loads: each access is coherent across the XCDs' L2
+// caches on its own, so no cache-wide release (an L2 writeback, which costs
+// microseconds per workgroup) is needed.  A writer waits for its stores to
+// complete (s_waitcnt) before it publishes a count; a reader issues its
+// loads only after it has read that count.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+// Every store this thread issued has completed (vmcnt 0), with the
+// compiler kept from moving memory operations across the wait.
+__device__ __forceinline__ void stores_complete() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Position of the appended token (the append's own clamp).
 __device__ __forceinline__ int append_pos(const DecodeParams& P, int b) {
   return min(max(P.app.lens_before[b], 0), P.max_seq_len - 1);
@@ -209,42 +230,37 @@ __device__ __forceinline__ float q_elem(const void* q, size_t idx) {
 // ---------------------------------------------------------------------------
 // 1. Block scores + global-state readout
 // ---------------------------------------------------------------------------
-template <typename KV, int D, int G>
-__device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, int chunk) {
-  constexpr int LPT = D / 8;            // lanes per candidate (8 channels each)
-  constexpr int CPP = kThreads / LPT;   // candidates per pass
-  constexpr int NIT = kScoreChunk / CPP;
-  static_assert(G <= LPT, "one writer lane per head");
-  const int c_begin = chunk * kScoreChunk;   // < nc_max
-  const int tid = threadIdx.x;
-  const int lig = tid % LPT;
-  const int slot = tid / LPT;
-  const int32_t* bt = P.block_table + static_cast<size_t>(seq_of(P, b)) * P.max_blocks;
-  const int lo = P.ns / P.B;   // first candidate block, whatever the length
-
-  // Issue every load of the chunk before any arithmetic: page ids (bounded
-  // by the longest sequence, so that they need not wait for this one's
-  // length), then the statistics rows, then the queries.
+// The statistics rows of one chunk of kScoreChunk candidates: D/8 lanes
+// share a candidate (8 channels each), a pass covers kThreads / (D/8)
+// candidates.  page < 0 marks a slot past the candidates.
+template <int D>
+struct StatRows {
+  static constexpr int LPT = D / 8;            // lanes per candidate
+  static constexpr int CPP = kThreads / LPT;   // candidates per pass
+  static constexpr int NIT = kScoreChunk / CPP;
   int page[NIT];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) page[it] = bt[lo + min(c_begin + slot + it * CPP, P.nc_max - 1)];
-  const int T = first_kernel_len(P, b);
-  const int nc = min(candidate_range(T, P.B, P.ns, P.W).count, P.nc_max);
-  if (c_begin >= nc) return;
-#pragma unroll
-  for (int it = 0; it < NIT; ++it)
-    if (c_begin + slot + it * CPP >= nc) page[it] = -1;
   float4 m0[NIT], m1[NIT], v0[NIT], v1[NIT];
+};
+
+// Issues the statistics loads of a chunk whose pages are set; unused slots
+// read page 0.
+template <int D>
+__device__ __forceinline__ void stat_load(const DecodeParams& P, int g, StatRows<D>& r) {
+  const int lig = threadIdx.x % StatRows<D>::LPT;
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {   // unconditional loads; unused slots read page 0
-    const size_t off = (static_cast<size_t>(max(page[it], 0)) * P.Hkv + g) * D + lig * 8;
-    m0[it] = *reinterpret_cast<const float4*>(P.blk_mean + off);
-    m1[it] = *reinterpret_cast<const float4*>(P.blk_mean + off + 4);
-    v0[it] = *reinterpret_cast<const float4*>(P.blk_var + off);
-    v1[it] = *reinterpret_cast<const float4*>(P.blk_var + off + 4);
+  for (int it = 0; it < StatRows<D>::NIT; ++it) {
+    const size_t off = (static_cast<size_t>(max(r.page[it], 0)) * P.Hkv + g) * D + lig * 8;
+    r.m0[it] = *reinterpret_cast<const float4*>(P.blk_mean + off);
+    r.m1[it] = *reinterpret_cast<const float4*>(P.blk_mean + off + 4);
+    r.v0[it] = *reinterpret_cast<const float4*>(P.blk_var + off);
+    r.v1[it] = *reinterpret_cast<const float4*>(P.blk_var + off + 4);
   }
-  // sigma q; the score is sigma q . mu + log(1 + sum_c (sigma q_c)^2 / 2 var_c).
-  float qs[G][8];
+}
+
+// sigma q of the pair's G heads, the lane's 8 channels.
+template <typename KV, int D, int G>
+__device__ __forceinline__ void score_query(const DecodeParams& P, int b, int g, float (&qs)[G][8]) {
+  const int lig = threadIdx.x % (D / 8);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     QReg<KV> qr;
@@ -255,11 +271,23 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
 #pragma unroll
     for (int i = 0; i < 8; ++i) qs[h][i] = P.sigma * qf[i];
   }
+}
+
+// Scores of a chunk's candidates from its statistics rows, stored as order
+// keys: score = sigma q . mu + log(1 + sum_c (sigma q_c)^2 / 2 var_c).
+template <int D, int G>
+__device__ __forceinline__ void score_finish(const DecodeParams& P, int b, int g, int c_begin, const StatRows<D>& r,
+                                             const float (&qs)[G][8]) {
+  constexpr int LPT = StatRows<D>::LPT;
+  constexpr int CPP = StatRows<D>::CPP;
+  static_assert(G <= LPT, "one writer lane per head");
+  const int lig = threadIdx.x % LPT;
+  const int slot = threadIdx.x / LPT;
   const int hsel = lig % G;   // the head whose score this lane finishes
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const float mu[8] = {m0[it].x, m0[it].y, m0[it].z, m0[it].w, m1[it].x, m1[it].y, m1[it].z, m1[it].w};
-    const float va[8] = {v0[it].x, v0[it].y, v0[it].z, v0[it].w, v1[it].x, v1[it].y, v1[it].z, v1[it].w};
+  for (int it = 0; it < StatRows<D>::NIT; ++it) {
+    const float mu[8] = {r.m0[it].x, r.m0[it].y, r.m0[it].z, r.m0[it].w, r.m1[it].x, r.m1[it].y, r.m1[it].z, r.m1[it].w};
+    const float va[8] = {r.v0[it].x, r.v0[it].y, r.v0[it].z, r.v0[it].w, r.v1[it].x, r.v1[it].y, r.v1[it].z, r.v1[it].w};
     float d1 = 0.f, d2 = 0.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -276,22 +304,40 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
       d2 = (h == hsel) ? c : d2;
     }
     const int cidx = c_begin + slot + it * CPP;
-    if (lig < G && page[it] >= 0) {
+    if (lig < G && r.page[it] >= 0) {
       // log(1 + x) via the hardware logarithm: x >= 0, absolute error ~1e-7.
       P.keys[(static_cast<size_t>(b) * P.Hq + g * G + lig) * P.sstride + cidx] = f32_order_key(d1 + __logf(1.f + d2));
     }
   }
 }
 
-// Rows [rc*32, rc*32 + 32) of the state readout: partial S^T q and q . z
-// of the pair's G heads (SPLA, section "Method": the linear part reads the
-// global state).  With the append taken in, row chunk 0 writes the new
-// token's page slot and length, and when the token completes its block
-// every chunk first adds the block to its rows of S and z (chunk 0 also to
-// sv) and writes them back, so that the readout sees the state the
-// stand-alone append would leave; one more workgroup per pair (rc = d/32)
-// computes the block's statistics.  Without the linear tail only the
-// append's part runs.
+// One scoring workgroup of k_score_readout: the chunk's candidates for the
+// G query heads of the group.  Every load of the chunk is issued before any
+// arithmetic: page ids (bounded by the longest sequence, so that they need
+// not wait for this one's length), then the statistics rows, then the
+// queries.
+template <typename KV, int D, int G>
+__device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, int chunk) {
+  using R = StatRows<D>;
+  const int c_begin = chunk * kScoreChunk;   // < nc_max
+  const int slot = threadIdx.x / R::LPT;
+  const int32_t* bt = P.block_table + static_cast<size_t>(seq_of(P, b)) * P.max_blocks;
+  const int lo = P.ns / P.B;   // first candidate block, whatever the length
+  R r;
+#pragma unroll
+  for (int it = 0; it < R::NIT; ++it) r.page[it] = bt[lo + min(c_begin + slot + it * R::CPP, P.nc_max - 1)];
+  const int T = first_kernel_len(P, b);
+  const int nc = min(candidate_range(T, P.B, P.ns, P.W).count, P.nc_max);
+  if (c_begin >= nc) return;
+#pragma unroll
+  for (int it = 0; it < R::NIT; ++it)
+    if (c_begin + slot + it * R::CPP >= nc) r.page[it] = -1;
+  stat_load<D>(P, g, r);
+  float qs[G][8];
+  score_query<KV, D, G>(P, b, g, qs);
+  score_finish<D, G>(P, b, g, c_begin, r, qs);
+}
+
 // Token-level variant ("SALS: Sparse Attention in Latent Space for KV Cache
 // Compression", Approach, here on the plain keys): the scores sigma q.k_t of
 // 256 candidate tokens of one (sequence, kv head) for its G query heads, as
@@ -339,14 +385,99 @@ __device__ __forceinline__ void score_tokens_part(const DecodeParams& P, int b, 
   }
 }
 
+// The readout's LDS: one instance per kernel.
+template <int D, int G>
+struct ReadoutLds {
+  float red[kThreads / kWave][D / 4][G][4];
+  float zs[kRoRows];
+  uint4 fold[kFoldStageBytes / 16];   // block stage, or the statistics' sums
+};
+template <int D, int G>
+__device__ __forceinline__ ReadoutLds<D, G>& readout_lds() {
+  __shared__ ReadoutLds<D, G> lds;
+  return lds;
+}
+
+// The registers of one row chunk's readout, loaded by readout_load and used
+// by readout_finish: thread (rg, col4) holds columns 4 col4 .. 4 col4 + 3
+// of rows r0 + rg + RG i (i < NR) of S and the G heads' query entries of
+// those rows; threads tid < kRoRows hold z[r0 + tid]; thread h kRoRows + r
+// (h < G) holds head h's query entry of row r0 + r (for q . z).
+template <int D, int G>
+struct ReadoutRegs {
+  static constexpr int C4 = D / 4;            // float4 columns per row
+  static constexpr int RG = kThreads / C4;    // row groups
+  static constexpr int NR = kRoRows / RG;     // rows per thread
+  static_assert(kRoRows % RG == 0 && G * kRoRows <= kThreads, "rows per readout workgroup");
+  float4 srow[NR];
+  float qv[NR][G];
+  float zr;
+  float qz;
+  uint32_t kn, vn;   // with the append, row chunk 0: element tid < D of the new key and value (storage bits)
+};
+
+// Rows [rc*32, rc*32 + 32) of the state readout: partial S^T q and q . z
+// of the pair's G heads (SPLA, section "Residual Linear Attention (RLA)":
+// the linear part reads the global state).  readout_load issues the loads
+// (only with the linear tail; the append's fold loads the rows itself when
+// it needs them without the tail).
 template <typename KV, int D, int G>
-__device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g, int rc) {
-  constexpr int C4 = D / 4;            // float4 columns per row
-  constexpr int RG = kThreads / C4;    // row groups
-  constexpr int NR = kRoRows / RG;     // rows per thread
-  static_assert(kRoRows % RG == 0, "rows per readout workgroup");
-  __shared__ float red[kThreads / kWave][C4][G][4];
-  __shared__ float zs[kRoRows];
+__device__ __forceinline__ void readout_load(const DecodeParams& P, int b, int g, int rc, ReadoutRegs<D, G>& R) {
+  using RR = ReadoutRegs<D, G>;
+  const int tid = threadIdx.x;
+  const int col4 = tid % RR::C4;
+  const int rg = tid / RR::C4;
+  const int r0 = rc * kRoRows;
+  const bool app = P.app.k_new != nullptr;
+  R.zr = 0.f;
+  R.qz = 0.f;
+  R.kn = R.vn = 0u;
+  if (app && rc == 0 && tid < D) {   // the new token's row, for its page slot
+    const size_t e = (static_cast<size_t>(b) * P.Hkv + g) * D + tid;
+    if constexpr (KV::kBytes == 2) {
+      R.kn = reinterpret_cast<const uint16_t*>(P.app.k_new)[e];
+      R.vn = reinterpret_cast<const uint16_t*>(P.app.v_new)[e];
+    } else {
+      R.kn = reinterpret_cast<const uint32_t*>(P.app.k_new)[e];
+      R.vn = reinterpret_cast<const uint32_t*>(P.app.v_new)[e];
+    }
+  }
+  if (!P.linear_tail || rc >= D / kRoRows) return;
+  const int spair = state_pair(P, b * P.Hkv + g);   // the sequence's state (the pair itself unless multi-query)
+  const float* Sp = (app ? P.app.S : P.S) + static_cast<size_t>(spair) * D * D;
+  const float* zp = (app ? P.app.z : P.z) + static_cast<size_t>(spair) * D + r0;
+  const size_t qbase = (static_cast<size_t>(b) * P.Hq + g * G) * D;
+#pragma unroll
+  for (int i = 0; i < RR::NR; ++i)
+    R.srow[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(r0 + rg + i * RR::RG) * D + col4 * 4);
+  if (tid < kRoRows) R.zr = zp[tid];
+#pragma unroll
+  for (int i = 0; i < RR::NR; ++i)
+#pragma unroll
+    for (int h = 0; h < G; ++h) R.qv[i][h] = q_elem<KV>(P.q, qbase + static_cast<size_t>(h) * D + r0 + rg + i * RR::RG);
+  if (tid < G * kRoRows) R.qz = q_elem<KV>(P.q, qbase + static_cast<size_t>(tid / kRoRows) * D + r0 + tid % kRoRows);
+}
+
+// The rest of row chunk rc, once its loads are issued.  With the append
+// taken in, row chunk 0 writes the new token's page slot and length, and
+// when the token completes its block every chunk first adds the block to
+// its rows of S and z (chunk 0 also to sv) and writes them back, so that the
+// readout sees the state the stand-alone append would leave; one more chunk
+// per pair (rc = d/32) computes the block's statistics.  Without the linear
+// tail only the append's part runs.  t_app >= 0: the append's position and
+// page_app the page of its block, as the caller already holds them; t_app <
+// 0: both are read here.
+template <typename KV, int D, int G>
+__device__ __forceinline__ void readout_finish(const DecodeParams& P, int b, int g, int rc, ReadoutRegs<D, G>& R,
+                                               int t_app, int page_app) {
+  using RR = ReadoutRegs<D, G>;
+  constexpr int NR = RR::NR;
+  constexpr int RG = RR::RG;
+  constexpr int C4 = RR::C4;
+  ReadoutLds<D, G>& lds = readout_lds<D, G>();
+  auto& red = lds.red;
+  auto& zs = lds.zs;
+  auto& fold_lds = lds.fold;
   const int tid = threadIdx.x;
   const int col4 = tid % C4;
   const int rg = tid / C4;
@@ -354,86 +485,76 @@ __device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g
   const int r0 = rc * kRoRows;
   const bool app = P.app.k_new != nullptr;
   const bool lin = P.linear_tail != 0;
-  const size_t qbase = (static_cast<size_t>(b) * P.Hq + g * G) * D;
   const size_t nbase = static_cast<size_t>(pair) * D;   // k_new / v_new row of the pair
-  __shared__ uint4 fold_lds[kFoldStageBytes / 16];      // block stage, or the statistics' sums
-  if (app && rc == D / kRoRows) {   // the statistics workgroup of the append
-    const int T = append_pos(P, b);
-    if ((T + 1) % P.B != 0) return;
-    const size_t page = static_cast<size_t>(P.block_table[static_cast<size_t>(b) * P.max_blocks + T / P.B]);
-    const size_t so = (page * P.Hkv + g) * D;
-    filled_block_stats<KV, D, kThreads>(P.app.k_pages, P.app.k_new, (page * P.Hkv + g) * P.B, T % P.B, nbase, P.B,
-                                        P.app.blk_mean + so, P.app.blk_var + so,
-                                        *reinterpret_cast<BlockStatsLds<kThreads, D>*>(fold_lds));
-    return;
-  }
-
-  const int spair = state_pair(P, pair);   // the sequence's state (the pair itself unless multi-query)
-  const float* Sp = (app ? P.app.S : P.S) + static_cast<size_t>(spair) * D * D;
-  const float* zp = (app ? P.app.z : P.z) + static_cast<size_t>(spair) * D + r0;
-  float4 srow[NR];
-  float qv[NR][G];
-  float zr = 0.f;
-  auto load_rows = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NR; ++i)
-      srow[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(r0 + rg + i * RG) * D + col4 * 4);
-    if (tid < kRoRows) zr = zp[tid];
-  };
-  // The readout's loads go first; the append's position and page take two
-  // dependent round trips behind them.
-  if (lin) {
-    load_rows();
-#pragma unroll
-    for (int i = 0; i < NR; ++i)
-#pragma unroll
-      for (int h = 0; h < G; ++h) qv[i][h] = q_elem<KV>(P.q, qbase + static_cast<size_t>(h) * D + r0 + rg + i * RG);
-  }
   int T = 0;
   size_t row0 = 0, page = 0;
   bool completes = false;
   if (app) {
-    T = append_pos(P, b);
-    page = static_cast<size_t>(P.block_table[static_cast<size_t>(b) * P.max_blocks + T / P.B]);
+    if (t_app >= 0) {
+      T = t_app;
+      page = static_cast<size_t>(page_app);
+    } else {
+      T = append_pos(P, b);
+      page = static_cast<size_t>(P.block_table[static_cast<size_t>(b) * P.max_blocks + T / P.B]);
+    }
     row0 = (page * P.Hkv + g) * P.B;   // first row of the page-head tile
     completes = (T + 1) % P.B == 0;    // uniform
-    if (rc == 0) {
-      if (tid < D) {
-        kv_put<KV>(P.app.k_pages, (row0 + T % P.B) * D + tid, P.app.k_new, nbase + tid);
-        kv_put<KV>(P.app.v_pages, (row0 + T % P.B) * D + tid, P.app.v_new, nbase + tid);
+  }
+  if (app && rc == D / kRoRows) {   // the statistics of the block the token completes
+    if (!completes) return;
+    const size_t so = (page * P.Hkv + g) * D;
+    filled_block_stats<KV, D, kThreads>(P.app.k_pages, P.app.k_new, row0, T % P.B, nbase, P.B, P.app.blk_mean + so,
+                                        P.app.blk_var + so, *reinterpret_cast<BlockStatsLds<kThreads, D>*>(fold_lds));
+    return;
+  }
+  if (app && rc == 0) {
+    if (tid < D) {   // the values were loaded with the chunk's rows
+      const size_t e = (row0 + T % P.B) * D + tid;
+      if constexpr (KV::kBytes == 2) {
+        reinterpret_cast<uint16_t*>(P.app.k_pages)[e] = static_cast<uint16_t>(R.kn);
+        reinterpret_cast<uint16_t*>(P.app.v_pages)[e] = static_cast<uint16_t>(R.vn);
+      } else {
+        reinterpret_cast<uint32_t*>(P.app.k_pages)[e] = R.kn;
+        reinterpret_cast<uint32_t*>(P.app.v_pages)[e] = R.vn;
       }
-      if (g == 0 && tid == 0 && P.app.lens_after) P.app.lens_after[b] = T + 1;
     }
+    if (g == 0 && tid == 0 && P.app.lens_after) P.app.lens_after[b] = T + 1;
   }
   if (!lin) {
     if (!completes) return;
-    load_rows();
+    const float* Sp = P.app.S + static_cast<size_t>(pair) * D * D;
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      R.srow[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(r0 + rg + i * RG) * D + col4 * 4);
+    if (tid < kRoRows) R.zr = P.app.z[nbase + r0 + tid];
   }
   if (completes) {
     const CompletedBlock cb{P.app.k_pages, P.app.v_pages, P.app.k_new, P.app.v_new, row0, nbase, T % P.B, P.B};
     const int zrow = tid < kRoRows ? r0 + tid : -1;
     const int svcol = rc == 0 && tid < D ? tid : -1;
     float sv = svcol >= 0 ? P.app.sv[nbase + svcol] : 0.f;
-    fold_completed_block<KV, D, kThreads, NR, RG>(cb, fold_lds, srow, r0 + rg, col4, zrow, zr, svcol, sv);
+    fold_completed_block<KV, D, kThreads, NR, RG>(cb, fold_lds, R.srow, r0 + rg, col4, zrow, R.zr, svcol, sv);
     float* Sw = P.app.S + static_cast<size_t>(pair) * D * D;
 #pragma unroll
     for (int i = 0; i < NR; ++i)
-      *reinterpret_cast<float4*>(Sw + static_cast<size_t>(r0 + rg + i * RG) * D + col4 * 4) = srow[i];
-    if (zrow >= 0) P.app.z[nbase + zrow] = zr;
-    if (svcol >= 0) P.app.sv[nbase + svcol] = sv;
+      *reinterpret_cast<float4*>(Sw + static_cast<size_t>(r0 + rg + i * RG) * D + col4 * 4) = R.srow[i];
+    if (zrow >= 0) P.app.z[nbase + zrow] = R.zr;
+    if (svcol >= 0) {
+      P.app.sv[nbase + svcol] = sv;
+    }
   }
   if (!lin) return;
-  if (tid < kRoRows) zs[tid] = zr;
+  if (tid < kRoRows) zs[tid] = R.zr;
   float acc[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.f;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      acc[h][0] = fmaf(qv[i][h], srow[i].x, acc[h][0]);
-      acc[h][1] = fmaf(qv[i][h], srow[i].y, acc[h][1]);
-      acc[h][2] = fmaf(qv[i][h], srow[i].z, acc[h][2]);
-      acc[h][3] = fmaf(qv[i][h], srow[i].w, acc[h][3]);
+      acc[h][0] = fmaf(R.qv[i][h], R.srow[i].x, acc[h][0]);
+      acc[h][1] = fmaf(R.qv[i][h], R.srow[i].y, acc[h][1]);
+      acc[h][2] = fmaf(R.qv[i][h], R.srow[i].z, acc[h][2]);
+      acc[h][3] = fmaf(R.qv[i][h], R.srow[i].w, acc[h][3]);
     }
   }
   // Row groups inside a wavefront sit C4 lanes apart.
@@ -462,16 +583,24 @@ __device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g
     for (int w = 0; w < kThreads / kWave; ++w) v += red[w][c / 4][h][c % 4];
     ro[idx] = v;
   }
-  if (tid < G) {
-    const int h = tid;
-    float qr[kRoRows];
-#pragma unroll
-    for (int r = 0; r < kRoRows; ++r) qr[r] = q_elem<KV>(P.q, qbase + static_cast<size_t>(h) * D + r0 + r);
-    float v = 0.f;
-#pragma unroll
-    for (int r = 0; r < kRoRows; ++r) v = fmaf(qr[r], zs[r], v);
-    P.roz[(static_cast<size_t>(pair) * P.ro_wgs + rc) * G + h] = v;
+  // q . z over the chunk's rows: thread h kRoRows + r takes row r of head
+  // h, then a sum over the 32 lanes of the head (rows of 16 lanes, then
+  // the lanes 16 apart)
+  float qzv = tid < G * kRoRows ? R.qz * zs[tid % kRoRows] : 0.f;
+  qzv = reduce_sum_lanes<16>(qzv);
+  qzv = pair_sum<16>(qzv);
+  if (tid < G * kRoRows && tid % kRoRows == 0) {
+    P.roz[(static_cast<size_t>(pair) * P.ro_wgs + rc) * G + tid / kRoRows] = qzv;
   }
+}
+
+// A whole row chunk: its loads, `mid` while they are in flight, the rest.
+template <typename KV, int D, int G, typename Mid>
+__device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g, int rc, Mid&& mid) {
+  ReadoutRegs<D, G> R;
+  readout_load<KV, D, G>(P, b, g, rc, R);
+  mid();
+  readout_finish<KV, D, G>(P, b, g, rc, R, -1, 0);
 }
 
 template <typename KV, int D, int G>
@@ -494,7 +623,7 @@ __global__ __launch_bounds__(kThreads) void k_score_readout(DecodeParams P) {
       score_part<KV, D, G>(P, b, g, x);
     }
   } else {
-    readout_part<KV, D, G>(P, b, g, x - P.score_wgs);
+    readout_part<KV, D, G>(P, b, g, x - P.score_wgs, [] {});
   }
 }
 
@@ -893,8 +1022,8 @@ struct SplitShare {
   int ne;      // entries of this split (uniform)
 };
 template <int G, bool FULL, int FK, bool GS, typename Stage, typename Early>
-__device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, int b, int g, int split,
-                                  Stage&& stage, Early&& early) {
+__device__ __forceinline__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, int b, int g, int split,
+                                                  Stage&& stage, Early&& early) {
   constexpr int NW = kThreads / kWave;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -918,14 +1047,17 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
   uint64_t v[2];
   int w[4];
   uint32_t kr[HPW][FK];
-  if (P.fused_sel) {
+  auto load_keys = [&](auto ld) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < HPW; ++i) {
       const int h = min(wave + NW * i, G - 1);
       const uint32_t* kh = P.keys + (static_cast<size_t>(b) * P.Hq + g * G + h) * P.sstride;
 #pragma unroll
-      for (int j = 0; j < FK; ++j) kr[i][j] = kh[min(lane + kWave * j, P.sstride - 1)];
+      for (int j = 0; j < FK; ++j) kr[i][j] = ld(kh + min(lane + kWave * j, P.sstride - 1));
     }
+  };
+  if (P.fused_sel) {
+    load_keys([](const uint32_t* p) { return *p; });
   } else {
 #pragma unroll
     for (int u = 0; u < 2; ++u) v[u] = src[min(tid + u * kThreads, max(nbits, 1) - 1)];
@@ -933,6 +1065,11 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
 #pragma unroll
   for (int u = 0; u < 4; ++u) w[u] = bt[min(tid + u * kThreads, P.nblk_max - 1)];
   const int T = __builtin_amdgcn_readfirstlane(clamp_len(P.seq_lens[b], P.max_seq_len));
+  // page of block j: from the staged row in LDS, else from global memory
+  // (explicit address spaces: a pointer to either would be a flat access)
+  auto page_of = [&](int j) __attribute__((always_inline)) -> int {
+    return P.bt_staged ? ld_lds<int32_t>(btrow + j) : ld_global<int32_t>(bt + j);
+  };
   const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
   const int nc = min(cr.count, P.nc_max);
   const int nb = min(ceil_div(T, P.B), P.nblk_max);
@@ -965,7 +1102,7 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
     // whatever the selection: the caller may start loading them now, so that
     // they arrive while the selection runs.
     __syncthreads();   // the block-table row
-    early(nc > 0 ? cr.lo + nc : 0, nb, P.bt_staged ? btrow : bt);
+    early(nc > 0 ? cr.lo + nc : 0, nb, page_of);
   }
   if constexpr (!GS) {
     if (P.fused_sel) {
@@ -1111,7 +1248,7 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
         if (((m >> lane) & 1ull) && at < P.umax) {
           const int j = (c0 + c) * kWave + lane;
           uent[at] = j | (head_mask(j) << 20);
-          upg[at] = P.bt_staged ? btrow[j] : bt[j];
+          upg[at] = page_of(j);
         }
       }
       done += total;
@@ -1139,7 +1276,7 @@ __device__ SplitShare union_share(const DecodeParams& P, char* smem, int pair, i
       }
       const int j = (c0 + c) * kWave + bit;
       r.ent = j | (head_mask(j) << 20);
-      r.page = P.bt_staged ? btrow[j] : bt[j];
+      r.page = page_of(j);
     }
     done += total;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // reads above before the next round's writes
@@ -1206,8 +1343,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
     qr[h].load(reinterpret_cast<const char*>(P.q) +
                ((static_cast<size_t>(b) * P.Hq + g * G + h) * D + lig * 8) * KV::kBytes);
   extern __shared__ uint64_t dyn_lds[];
-  const SplitShare share = union_share<G, false, kFusedKplMax, false>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split,
-                                                               [] {}, [](int, int, const int32_t*) {});
+  const SplitShare share = union_share<G, false, kFusedKplMax, false>(
+      P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, [] {}, [](int, int, auto&&) {});
   const int T = share.T;
   const int Ts = state_tokens(P, T, b);   // tokens the linear state holds
   if (split >= share.count) return;
@@ -1494,38 +1631,28 @@ template <int NT>
 struct VSlice;
 template <>
 struct VSlice<8> {   // D = 128: 8 channels of a row per lane
-  uint4 r;
-  __device__ __forceinline__ void load(const char* p) { r = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ uint32_t word(int i) const { return i == 0 ? r.x : i == 1 ? r.y : i == 2 ? r.z : r.w; }
-  __device__ __forceinline__ void zero() { r = make_uint4(0, 0, 0, 0); }
+  u32x4 r;
+  __device__ __forceinline__ void load(const char* p) { r = ld_global<u32x4>(p); }
+  __device__ __forceinline__ uint32_t word(int i) const { return r[i]; }
 };
 template <>
 struct VSlice<4> {   // D = 64: 4 channels of a row per lane
-  uint2 r;
-  __device__ __forceinline__ void load(const char* p) { r = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ uint32_t word(int i) const { return i == 0 ? r.x : r.y; }
-  __device__ __forceinline__ void zero() { r = make_uint2(0, 0); }
+  u32x2 r;
+  __device__ __forceinline__ void load(const char* p) { r = ld_global<u32x2>(p); }
+  __device__ __forceinline__ uint32_t word(int i) const { return r[i]; }
 };
 
-// Partials shared between the attention workgroups of a pair go through
-// agent-scope atomic stores and loads: each access is coherent across the
-// XCDs' L2 caches on its own, so no cache-wide release (an L2 writeback,
-// which costs microseconds per workgroup) is needed.  A writer waits for its
-// stores to complete before it counts itself done.
-__device__ __forceinline__ void store_agent(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-}
 
 // The merge of one pair's nsplit split partials and its residual linear part
 // (SPLA Abstract: global state minus the exact tokens' share), done by the
 // pair's last attention workgroup: thread entries (head, channel) walk the
-// splits with a running maximum, every split's loads issued together.
+// splits with a running maximum, kMergeBatch splits' loads issued together.
+// Everything another workgroup of the launch wrote -- split partials,
+// readout partials, and in the one-launch step the folded sv -- is read
+// with agent-scope loads.
+constexpr int kMergeBatch = 4;
 template <int D, int G>
-__device__ void merge_pair(const DecodeParams& P, int pair, int b, int g, int nsplit, int T) {
+__device__ __forceinline__ void merge_pair(const DecodeParams& P, int pair, int b, int g, int nsplit, int T) {
   constexpr int RO = D / kRoRows;
   const float* pb = P.part + static_cast<size_t>(pair) * P.max_split * G * P.pstride;
   const CandRange cr = candidate_range(T, P.B, P.ns, P.W);
@@ -1533,43 +1660,44 @@ __device__ void merge_pair(const DecodeParams& P, int pair, int b, int g, int ns
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int hh = idx / D;
     const int c = idx % D;
-    float ms[kFusedMergeSplits], ls[kFusedMergeSplits], lw[kFusedMergeSplits], a[kFusedMergeSplits],
-        la[kFusedMergeSplits];
-#pragma unroll
-    for (int s = 0; s < kFusedMergeSplits; ++s) {
-      const float* ps = pb + (static_cast<size_t>(min(s, nsplit - 1)) * G + hh) * P.pstride;
-      ms[s] = load_agent(ps);
-      ls[s] = load_agent(ps + 1);
-      lw[s] = load_agent(ps + 2);
-      a[s] = load_agent(ps + 4 + c);
-      la[s] = load_agent(ps + 4 + D + c);
-    }
     float ro = 0.f, rz = 0.f, svc = 0.f;
     if (tail) {
 #pragma unroll
       for (int rc = 0; rc < RO; ++rc) {
-        ro += P.ro[((static_cast<size_t>(pair) * RO + rc) * G + hh) * D + c];
-        rz += P.roz[(static_cast<size_t>(pair) * RO + rc) * G + hh];
+        ro += load_agent(P.ro + ((static_cast<size_t>(pair) * RO + rc) * G + hh) * D + c);
+        rz += load_agent(P.roz + (static_cast<size_t>(pair) * RO + rc) * G + hh);
       }
-      svc = P.sv[static_cast<size_t>(state_pair(P, pair)) * D + c];
+      svc = load_agent(P.sv + static_cast<size_t>(state_pair(P, pair)) * D + c);
     }
     float M = 0.f;   // the linear part is in unshifted units (log-scale 0)
     float num = 0.f, den = 0.f, lnum = 0.f, lden = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += kMergeBatch) {
+      float ms[kMergeBatch], ls[kMergeBatch], lw[kMergeBatch], a[kMergeBatch], la[kMergeBatch];
 #pragma unroll
-    for (int s = 0; s < kFusedMergeSplits; ++s) {
-      if (s >= nsplit) break;
-      lnum += la[s];
-      lden += lw[s];
-      if (ms[s] != kNegInf) {
-        if (ms[s] > M) {
-          const float r = __expf(M - ms[s]);
-          num *= r;
-          den *= r;
-          M = ms[s];
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const float* ps = pb + (static_cast<size_t>(min(s0 + i, nsplit - 1)) * G + hh) * P.pstride;
+        ms[i] = load_agent(ps);
+        ls[i] = load_agent(ps + 1);
+        lw[i] = load_agent(ps + 2);
+        a[i] = load_agent(ps + 4 + c);
+        la[i] = load_agent(ps + 4 + D + c);
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        if (s0 + i >= nsplit) break;
+        lnum += la[i];
+        lden += lw[i];
+        if (ms[i] != kNegInf) {
+          if (ms[i] > M) {
+            const float r = __expf(M - ms[i]);
+            num *= r;
+            den *= r;
+            M = ms[i];
+          }
+          const float f = __expf(ms[i] - M);
+          num = fmaf(f, a[i], num);
+          den = fmaf(f, ls[i], den);
         }
-        const float f = __expf(ms[s] - M);
-        num = fmaf(f, a[s], num);
-        den = fmaf(f, ls[s], den);
       }
     }
     if (tail) {
@@ -1636,7 +1764,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   const size_t v_lane = (static_cast<size_t>(4 * q4) * D + NT * n16) * 2;
 
   struct Slice {
-    uint4 k[KS];
+    u32x4 k[KS];
     VSlice<NT> v[4];
     int t0;   // first token (uniform); kDeadT0 for a slice without a page (no row valid)
     int fm;   // heads that selected the block (uniform)
@@ -1646,7 +1774,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   auto load_slice = [&](int ent, int pg, int sub, bool live, Slice& x) __attribute__((always_inline)) {
     const size_t base = ((static_cast<size_t>(max(pg, 0)) * P.Hkv + g) * B + sub * SL) * D * 2;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) x.k[s] = *reinterpret_cast<const uint4*>(kp + base + k_lane + 16 * s);
+    for (int s = 0; s < KS; ++s) x.k[s] = ld_global<u32x4>(kp + base + k_lane + 16 * s);
 #pragma unroll
     for (int j = 0; j < 4; ++j) x.v[j].load(vp + base + v_lane + static_cast<size_t>(j) * D * 2);
     x.t0 = (live && pg >= 0) ? (ent & 0xFFFFF) * B + sub * SL : kDeadT0;
@@ -1657,11 +1785,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   // Dynamic split: this wavefront's slices of the window blocks, loaded
   // before the selection: slices r = split * NW + wave + m S NW (m < kPre)
   // of the window region, so that its first npre slices are taken this way.
-  // One per wavefront measured faster than two.
+  // One per wavefront measured faster than two or three: more window
+  // traffic in flight delays the selection's own loads.
   constexpr int kPre = 1;
   Slice pre[kPre];
   int npre = 0, nwin_sl = 0;
-  auto early = [&](int jw0, int nbk, const int32_t* pages) __attribute__((always_inline)) {
+  auto early = [&](int jw0, int nbk, auto&& page_of) __attribute__((always_inline)) {
     nwin_sl = (nbk - jw0) * spb;
     const int span = P.max_split * NW;
     npre = min(kPre * span, nwin_sl);
@@ -1671,7 +1800,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
       const bool live = DYN && r < npre;
       const int j = jw0 + (live ? r : 0) / spb;
       const int sub = (live ? r : 0) % spb;
-      load_slice(j, live ? pages[j] : 0, sub, live, pre[m]);
+      load_slice(j, live ? page_of(j) : 0, sub, live, pre[m]);
     }
   };
   extern __shared__ uint64_t dyn_lds[];
@@ -1828,7 +1957,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     };
     auto fetch_u = [&](int u, int i, Slice& x) __attribute__((always_inline)) {
       const int qc = u * kUnitSlices + i;
-      const bool live = u < nunits && qc < nclaim;
+      const bool live = u >= 0 && u < nunits && qc < nclaim;
       const int q = qc < w0 ? qc : qc + npre;
       const int e = (live ? q : 0) / spb;
       const int sub = (live ? q : 0) - e * spb;
@@ -1838,7 +1967,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     int ua = __builtin_amdgcn_readfirstlane(claim());
     fetch_u(ua, 0, sb);
 #pragma unroll
-    for (int m = 0; m < kPre; ++m) process(pre[m]);   // the prefetched window slices (masked if none)
+    for (int m = 0; m < kPre; ++m)   // the prefetched window slices (masked if none)
+      if (m == 0 || pre[m].t0 != kDeadT0) process(pre[m]);
     while (ua < nunits) {
       const int cn = claim();
       fetch_u(ua, 1, sa);
@@ -1949,14 +2079,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     // The pair's last workgroup to finish merges: every thread's partial
     // stores complete first, then one thread counts the workgroup done.
     __shared__ int is_last;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    stores_complete();
     __syncthreads();
     const int writers = DYN ? P.max_split : min(share.count, P.max_split);
+    int32_t* done = P.ctr + static_cast<size_t>(pair) * kCtrStride + kDoneSlot;
     if (tid == 0)
-      is_last = __hip_atomic_fetch_add(P.ctr + static_cast<size_t>(pair) * kCtrStride + kDoneSlot, 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT) == writers - 1;
+      is_last = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == writers - 1;
     __syncthreads();
     if (is_last) merge_pair<D, G>(P, pair, b, g, writers, T);
   }

@@ -144,8 +144,11 @@ typedef struct hsla_config {
  * blk_mean, blk_var: [num_pages, num_kv_heads, head_dim] float32 statistics
  *   of the block stored in that page (defined only for full blocks).
  * block_table: [batch, max_blocks_per_seq] int32, row-major; entry (b, j) is
- *   the page of block j of sequence b.  Only entries j < ceil(T_b / B) are
- *   read (and entry T_b / B by an append). */
+ *   the page of block j of sequence b.  The kernels may load any entry
+ *   j < ceil(max_seq_len / B) of a row (they prefetch the row before the
+ *   sequence's length is known), but only entries j < ceil(T_b / B) (and
+ *   entry T_b / B by an append) are used as page indices, so the rest may
+ *   hold anything. */
 typedef struct hsla_kv_pool {
   void* k_pages;
   void* v_pages;
@@ -235,7 +238,8 @@ size_t hsla_decode_workspace_size(const hsla_config* cfg, int32_t batch, int32_t
  *   selected block indices (token indices with HSLA_SEL_TOKEN) in ascending
  *   order, padded with -1.
  * workspace: device scratch of at least hsla_decode_workspace_size() bytes;
- *   contents on entry are ignored.
+ *   contents on entry are ignored.  Calls that share a workspace must not
+ *   run concurrently.
  * prof: optional timing hook (NULL for none). */
 hsla_status hsla_decode(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
                         const void* q, const int32_t* seq_lens, int32_t batch,

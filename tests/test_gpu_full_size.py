@@ -88,6 +88,44 @@ def test_full_size_workload(name):
                     assert blk in sel[b, h].tolist(), (b, g, blk, h)
 
 
+@pytest.mark.parametrize("name", ["llama8b_32k", "needle_128k"])
+def test_full_size_append_decode(name):
+    """The call the benchmark times: one hsla_append_decode with the
+    default (dynamic) split at full size -- the token's page write, the fold
+    of a block it completes with that block's statistics, and the decode at
+    T + 1 -- checked against the oracle at T + 1 on sampled pairs.  The
+    first sequence is one token shorter, so that its appended token
+    completes a block."""
+    base = FULL[name]()
+    lens = list(base.seq_lens)
+    lens[0] -= 1
+    wl = W.dataclasses.replace(base, seq_lens=tuple(lens))
+    assert (wl.seq_lens[0] + 1) % wl.block_size == 0
+    _announce(wl, "full size, hsla_append_decode, sampled pairs at T + 1")
+    inp = W.make_inputs(wl, keep_pairs=False)
+    dc = DeviceCache(cfg_of(wl), inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"],
+                     capacity_len=int(max(wl.seq_lens)) + 1)
+    dc.build()
+    k_tok, v_tok = W.gen_token(wl, 0)
+    out, sel = dc.append_decode(to_device(k_tok), to_device(v_tok), to_device(inp["q"]))
+    torch.cuda.synchronize()
+    out, sel = out.cpu().numpy(), sel.cpu().numpy()
+    grown = W.dataclasses.replace(wl, seq_lens=tuple(t + 1 for t in wl.seq_lens))
+    assert dc.seq_lens.cpu().numpy().tolist() == list(grown.seq_lens)
+    check_properties(grown, out, sel)
+
+    def pair_data(b, g):
+        K, V = W.gen_pair(wl, b, g, inp["q"])
+        return np.concatenate([K, k_tok[b, g][None]]), np.concatenate([V, v_tok[b, g][None]])
+
+    G = wl.group
+    pairs = sorted(set(sampled_pairs(grown)) | {(0, 0)})
+    heads = [(b, h) for b, g in pairs for h in range(g * G, (g + 1) * G)]
+    worst, flips = check_case(grown, inp, dc, out, sel, heads=heads, pair_data=pair_data)
+    print(f"  pairs {pairs}: worst row error {worst:.3e}, near-tie flips {flips}")
+    sys.stdout.flush()
+
+
 def test_full_size_hybrid_32_layers():
     """Build + decode of all 32 layers at 32768 tokens (budgets from
     {4, 8, 16, 32}, every fourth layer without the linear tail); one pair

@@ -251,6 +251,21 @@ def test_dense_when_budget_covers_all_candidates(form, T, B, ns, Wn, d):
     np.testing.assert_allclose(r.out, _sdpa(q, K, V, p.sigma), rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("d", [16, 64, 128])
+def test_default_scale_is_the_standard_one(d):
+    """With no scale given, the dense limit equals torch's attention at its
+    own default scaling (1/sqrt(d)): pins the oracle's default sigma against
+    a routine that fixes it independently."""
+    rng = np.random.default_rng(d)
+    q, K, V = _rand_case(rng, 120, d)
+    p = _params(head_dim=d, block_size=8, num_sink=4, window=16, top_k=10 ** 6)
+    assert p.scale == 0.0
+    r = O.decode_head(q, K, V, p)
+    qt, kt, vt = (torch.from_numpy(x)[None, None] for x in (q[None], K, V))
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[0, 0, 0].numpy()
+    np.testing.assert_allclose(r.out, ref, rtol=1e-12, atol=1e-13)
+
+
 @pytest.mark.parametrize("form", ["definition", "subtraction"])
 def test_sink_plus_window_when_no_budget_and_no_tail(form):
     rng = np.random.default_rng(11)
