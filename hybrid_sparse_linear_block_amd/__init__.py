@@ -31,7 +31,8 @@ HSLA_MAX_PROFILE_EVENTS = 8
 
 EXPORTED = ("hsla_status_string", "hsla_version", "hsla_build_workspace_size", "hsla_build_state",
             "hsla_append_token", "hsla_decode_workspace_size", "hsla_decode", "hsla_append_decode",
-            "hsla_prefill_chunk_workspace_size", "hsla_prefill_chunk")
+            "hsla_prefill_chunk_workspace_size", "hsla_prefill_chunk", "hsla_noalloc_scratch_bytes",
+            "hsla_append_decode_noalloc")
 
 
 class hsla_config(ctypes.Structure):
@@ -111,6 +112,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsla_prefill_chunk.argtypes = [P(hsla_config), P(hsla_kv_pool), P(hsla_state), vp, vp, vp, vp, vp, i32,
                                        i32, i32, vp, vp, vp, sz, vp]
     lib.hsla_prefill_chunk.restype = ctypes.c_int
+    lib.hsla_noalloc_scratch_bytes.argtypes = []
+    lib.hsla_noalloc_scratch_bytes.restype = sz
+    lib.hsla_append_decode_noalloc.argtypes = [P(hsla_config), P(hsla_kv_pool), P(hsla_state), vp, vp, vp, vp, vp,
+                                               i32, i32, vp, vp, vp]
+    lib.hsla_append_decode_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -239,6 +245,18 @@ def hsla_append_decode(cfg: Config, pool: Pool, state: State, k_new, v_new, seq_
         ctypes.byref(cfg.c()), ctypes.byref(pool.c()), ctypes.byref(state.c()), _ptr(k_new), _ptr(v_new),
         _ptr(seq_lens_before), _ptr(seq_lens_after), _ptr(q), batch, max_seq_len, _ptr(out), _ptr(sel_idx),
         _ptr(workspace), nbytes, _stream(stream), ctypes.byref(prof) if prof is not None else None))
+
+
+def hsla_noalloc_scratch_bytes() -> int:
+    return int(load().hsla_noalloc_scratch_bytes())
+
+
+def hsla_append_decode_noalloc(cfg: Config, pool: Pool, state: State, k_new, v_new, seq_lens_before, seq_lens_after,
+                               q, batch: int, max_seq_len: int, out, sel_idx, stream=None) -> None:
+    _check("hsla_append_decode_noalloc", load().hsla_append_decode_noalloc(
+        ctypes.byref(cfg.c()), ctypes.byref(pool.c()), ctypes.byref(state.c()), _ptr(k_new), _ptr(v_new),
+        _ptr(seq_lens_before), _ptr(seq_lens_after), _ptr(q), batch, max_seq_len, _ptr(out), _ptr(sel_idx),
+        _stream(stream)))
 
 
 def hsla_prefill_chunk_workspace_size(cfg: Config, batch: int, q_len: int, max_seq_len: int) -> int:

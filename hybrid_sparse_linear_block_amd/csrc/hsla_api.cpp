@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "hsla.h"
@@ -273,6 +274,32 @@ hsla_status hsla_append_decode(const hsla_config* cfg, const hsla_kv_pool* pool,
 
 namespace {
 
+// The no-allocation variant of hsla_append_decode: the decode workspace is a
+// file-scope device array of fixed size.  Every GPU the library runs on
+// holds its own copy (until the process ends); its address on a device is
+// looked up once, with that device current, and kept.  Like the workspace
+// it stands in for, its contents on entry do not matter.
+constexpr size_t kNoAllocScratchBytes = HSLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device (nullptr on a
+// HIP error).
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // The multi-query form's shapes: `seq` over the sequences (append), `rows`
 // over the batch x q_len query rows (decode).  Workspace: the decode's, then
 // the rows' lengths.
@@ -363,6 +390,33 @@ hsla_status hsla_prefill_chunk(const hsla_config* cfg, const hsla_kv_pool* pool,
     return HSLA_ERR_HIP;
   if (hsla::launch_append(seq, a, stream, q_len, hsla::kAppendFold, nullptr) != hipSuccess) return HSLA_ERR_HIP;
   return HSLA_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t hsla_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+hsla_status hsla_append_decode_noalloc(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
+                                       const void* k_new, const void* v_new, const int32_t* seq_lens_before,
+                                       int32_t* seq_lens_after, const void* q, int32_t batch, int32_t max_seq_len,
+                                       float* out, int32_t* sel_idx, hipStream_t stream) {
+  const size_t need = hsla_decode_workspace_size(cfg, batch, max_seq_len);
+  if (need == 0) {   // the configuration itself is rejected: the same status as the workspace form
+    Problem p;
+    const hsla_status st = resolve(cfg, batch, max_seq_len, -1, &p);
+    return st != HSLA_OK ? st : HSLA_ERR_INVALID_ARG;
+  }
+  if (need > kNoAllocScratchBytes) {
+    fprintf(stderr, "libhsla: hsla_append_decode_noalloc needs %zu bytes of scratch, more than its %zu\n", need,
+            kNoAllocScratchBytes);
+    return HSLA_ERR_WORKSPACE;
+  }
+  void* ws = scratch_on_current_device();
+  if (!ws) return HSLA_ERR_HIP;
+  return hsla_append_decode(cfg, pool, state, k_new, v_new, seq_lens_before, seq_lens_after, q, batch, max_seq_len,
+                            out, sel_idx, ws, kNoAllocScratchBytes, stream, nullptr);
 }
 
 }  // extern "C"

@@ -264,6 +264,31 @@ hsla_status hsla_append_decode(const hsla_config* cfg, const hsla_kv_pool* pool,
                                float* out, int32_t* sel_idx, void* workspace, size_t workspace_bytes,
                                hipStream_t stream, hsla_profile* prof);
 
+/* Scratch of hsla_append_decode_noalloc: 16 MiB per GPU. */
+#define HSLA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* Bytes of that scratch (HSLA_NOALLOC_SCRATCH_BYTES).  Pure host function. */
+size_t hsla_noalloc_scratch_bytes(void);
+
+/* hsla_append_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Arguments and results as hsla_append_decode, without the
+ * workspace and the timing hook.  The workspace is instead a fixed array of
+ * HSLA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends (its first call on a device looks up the array's address
+ * there).  The call allocates nothing.
+ * Limits and errors: when hsla_decode_workspace_size(cfg, batch,
+ * max_seq_len) exceeds HSLA_NOALLOC_SCRATCH_BYTES it returns
+ * HSLA_ERR_WORKSPACE (and says so on stderr) and enqueues nothing; other
+ * errors as hsla_append_decode.  Every call on one GPU shares that GPU's
+ * array: calls whose work overlaps on one GPU (other host threads, other
+ * streams) race and give wrong results; calls ordered on one stream, or
+ * synchronised, are safe. */
+hsla_status hsla_append_decode_noalloc(const hsla_config* cfg, const hsla_kv_pool* pool, const hsla_state* state,
+                                       const void* k_new, const void* v_new, const int32_t* seq_lens_before,
+                                       int32_t* seq_lens_after, const void* q, int32_t batch, int32_t max_seq_len,
+                                       float* out, int32_t* sel_idx, hipStream_t stream);
+
 /* Bytes of workspace hsla_prefill_chunk needs (0 on invalid arguments or
  * an unsupported chunk).  Pure host function. */
 size_t hsla_prefill_chunk_workspace_size(const hsla_config* cfg, int32_t batch, int32_t q_len,

@@ -229,3 +229,23 @@ def test_prefill_chunk_rejects_bad_pointers():
     assert call_prefill_chunk(c, null_state=True) == E
     assert call_prefill_chunk(c, p=pool(max_blocks_per_seq=100)) == E
     assert call_prefill_chunk(c, batch=0) == E
+
+
+def test_noalloc_rejects_a_shape_beyond_its_scratch():
+    """hsla_append_decode_noalloc refuses a shape whose workspace exceeds its
+    fixed scratch before it touches the GPU (no pointer is dereferenced)."""
+    assert H.hsla_noalloc_scratch_bytes() == 16 << 20
+    c = cfg(top_k=8, window=256)
+    batch, msl = 256, 8192
+    assert H.hsla_decode_workspace_size(c, batch, msl) > H.hsla_noalloc_scratch_bytes()
+    fake = 1 << 20   # 16-byte aligned, never dereferenced
+    pool = H.hsla_kv_pool(fake, fake, fake, fake, fake, msl // 64 + 1, 1)
+    state = H.hsla_state(fake, fake, fake)
+    lib = H.load()
+    st = lib.hsla_append_decode_noalloc(ctypes.byref(c.c()), ctypes.byref(pool), ctypes.byref(state), fake, fake,
+                                        fake, fake + 4096, fake, batch, msl, fake, None, None)
+    assert st == H.HSLA_ERR_WORKSPACE
+    # an invalid configuration keeps its own status
+    st = lib.hsla_append_decode_noalloc(ctypes.byref(cfg(head_dim=96).c()), ctypes.byref(pool), ctypes.byref(state),
+                                        fake, fake, fake, fake + 4096, fake, 1, 1024, fake, None, None)
+    assert st == H.HSLA_ERR_UNSUPPORTED
