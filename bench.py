@@ -72,6 +72,8 @@ def parse(argv=None):
                     help="rocprofv3 counter files of three --build-run passes -> summary on stdout")
     ap.add_argument("--profile-summary", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="rocprofv3 --stats kernel file -> markdown summary on stdout")
+    ap.add_argument("--counters-collect", nargs="+", metavar="CSV",
+                    help="rocprofv3 --pmc counter files of --traffic-run passes -> markdown table per decode kernel")
     ap.add_argument("--no-secondary", action="store_true",
                     help="measure only --workload (the default run adds needle_128k beside llama8b_32k)")
     ap.add_argument("--separate-append", action="store_true",
@@ -276,33 +278,66 @@ def _counter_rows(path, counter):
     return rows
 
 
+TRAFFIC_KERNELS = ("k_score_readout", "k_attend", "k_merge")
+
+
 def traffic_collect(fetch_csv, write_csv):
-    """Per-launch HBM bytes of the attention kernel: the counters' KiB per
+    """Per-launch HBM bytes of the decode kernels: the counters' KiB per
     dispatch, each scaled by (bytes the copy moved) / (what the counter read
-    for the copy), averaged over the attention dispatches."""
-    out = {}
+    for the copy), averaged over each kernel's dispatches.  The attention
+    kernel's sum is the `traffic` of the bench line."""
     scales, per = {}, {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path, counter)
         copy = [v for n, v in rows if "k_" not in n and v * 1024 > COPY_BYTES / 4]
-        attend = [v for n, v in rows if "k_attend" in n]
-        if not copy or not attend:
+        if not copy or not any("k_attend" in n for n, _ in rows):
             raise SystemExit(f"{path}: no copy or attention dispatches for {counter}")
         scales[counter] = COPY_BYTES / (max(copy) * 1024.0)
-        per[counter] = float(np.mean(attend)) * 1024.0 * scales[counter]
+        for k in TRAFFIC_KERNELS:
+            v = [x for n, x in rows if k in n]
+            if v:
+                per.setdefault(k, {})[counter] = float(np.mean(v)) * 1024.0 * scales[counter]
     name = traffic_key(workload(parse_known_workload(), "--grouped" in sys.argv, "--tokens" in sys.argv))
     try:
         out = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         out = {}
-    out[name] = {"source_sha": source_sha(), "bytes_per_launch": int(per["FETCH_SIZE"] + per["WRITE_SIZE"]),
-                 "fetch_bytes": int(per["FETCH_SIZE"]), "write_bytes": int(per["WRITE_SIZE"]),
+    att = per["k_attend"]
+    out[name] = {"source_sha": source_sha(), "bytes_per_launch": int(att["FETCH_SIZE"] + att["WRITE_SIZE"]),
+                 "fetch_bytes": int(att["FETCH_SIZE"]), "write_bytes": int(att["WRITE_SIZE"]),
                  "fetch_scale": round(scales["FETCH_SIZE"], 4), "write_scale": round(scales["WRITE_SIZE"], 4),
-                 "copy_bytes": COPY_BYTES}
+                 "copy_bytes": COPY_BYTES,
+                 "kernels": {k: {"fetch_bytes": int(v.get("FETCH_SIZE", 0)), "write_bytes": int(v.get("WRITE_SIZE", 0))}
+                             for k, v in per.items()}}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
     print(json.dumps(out[name]))
+
+
+def counters_collect(paths):
+    """Mean per dispatch of every counter in the given rocprofv3 counter
+    files, one column per decode kernel (the dispatches of --traffic-run)."""
+    import csv
+    kernels = ("k_score_readout", "k_attend", "k_merge")
+    vals, order = {}, []
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            k = next((k for k in kernels if k in r["Kernel_Name"]), None)
+            if k is None:
+                continue
+            c = r["Counter_Name"]
+            if c not in order:
+                order.append(c)
+            vals.setdefault((c, k), []).append(float(r["Counter_Value"]))
+    lines = ["| counter | " + " | ".join(f"`{k}`" for k in kernels) + " |", "|---|" + "---:|" * len(kernels)]
+    for c in order:
+        cells = []
+        for k in kernels:
+            v = vals.get((c, k))
+            cells.append(f"{np.mean(v):.4g}" if v else "")
+        lines.append(f"| {c} | " + " | ".join(cells) + " |")
+    return "\n".join(lines)
 
 
 def parse_known_workload():
@@ -327,23 +362,31 @@ def profile_summary(stats_csv, command):
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
     trace = os.path.join(os.path.dirname(stats_csv), os.path.basename(stats_csv).replace("kernel_stats", "kernel_trace"))
     if os.path.exists(trace):
-        # Attention dispatches in launch order, split into the phases of the
-        # default benchmark run (main() below launches them in this order).
+        # Decode kernels' dispatches in launch order, cut into the records
+        # and phases of the default benchmark run (measure() launches them in
+        # this order, one record after the other).
         import shlex
         a = parse(shlex.split(command.split(" -- ", 1)[1])[2:]) if " -- " in command else parse([])
         K, Wm, R = a.steps, a.warmup, max(1, a.replicas)
-        rows = sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"]))
-        us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows if "k_attend" in r["Kernel_Name"]]
+        records = [a.workload]
+        if a.workload == "llama8b_32k" and not (a.grouped or a.tokens or a.no_secondary):
+            records.append("needle_128k")
         phases = [("spot check", 1), ("warmup steps", Wm), ("timed steps", K), ("event-timed steps", K),
                   ("selection reads", R), ("warm decode-only loop", K)]
-        if len(us) == sum(n for _, n in phases):
-            lines += ["", "Attention dispatches by phase of the run (from the kernel trace of the same run):", "",
-                      "| phase | calls | avg us | median us |", "|---|---:|---:|---:|"]
+        per_rec = sum(n for _, n in phases)
+        rows = sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"]))
+        for kern in ("k_score_readout", "k_attend", "k_merge"):
+            us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows if kern in r["Kernel_Name"]]
+            if len(us) != per_rec * len(records):
+                continue
+            lines += ["", f"`{kern}` dispatches by record and phase (kernel trace of the same run):", "",
+                      "| record | phase | calls | avg us | median us |", "|---|---|---:|---:|---:|"]
             at = 0
-            for name, n in phases:
-                seg = us[at:at + n]
-                at += n
-                lines.append(f"| {name} | {n} | {np.mean(seg):.2f} | {np.median(seg):.2f} |")
+            for rec in records:
+                for name, n in phases:
+                    seg = us[at:at + n]
+                    at += n
+                    lines.append(f"| {rec} | {name} | {n} | {np.mean(seg):.2f} | {np.median(seg):.2f} |")
     return "\n".join(lines)
 
 
@@ -912,6 +955,9 @@ def main():
         return
     if args.profile_summary:
         print(profile_summary(*args.profile_summary))
+        return
+    if args.counters_collect:
+        print(counters_collect(args.counters_collect))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: the library runs on exactly one GPU; --gpus above 1 is not supported "

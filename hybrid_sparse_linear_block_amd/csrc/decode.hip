@@ -703,6 +703,106 @@ __device__ __forceinline__ void radix_pick(const uint4 c4, int lane, int& digit,
   rem = __builtin_amdgcn_readlane(rem_here, src);
 }
 
+// Value of lane ^ S, for S = 1 .. 32, without LDS: DPP quad permutes for 1
+// and 2, two bank-masked DPP row shifts for 4 and 8 (each half of the row
+// reads from the other), the gfx950 row swaps for 16 and 32.  A swap
+// returns the lane's own value in one result and its partner's in the
+// other; taking the one that differs from the own value is right whichever
+// is which (when they are equal either is the partner's).
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  const int x = static_cast<int>(v);
+  if constexpr (S == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  } else if constexpr (S == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  } else if constexpr (S == 4) {
+    const int t = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xf, 0x5, false);   // row_shl:4 into banks 0, 2
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(t, x, 0x114, 0xf, 0xA, false));   // row_shr:4 into 1, 3
+  } else if constexpr (S == 8) {
+    const int t = __builtin_amdgcn_update_dpp(x, x, 0x108, 0xf, 0x3, false);   // row_shl:8 into banks 0, 1
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(t, x, 0x118, 0xf, 0xC, false));   // row_shr:8 into 2, 3
+  } else if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return r[0] == v ? r[1] : r[0];
+  } else {
+    static_assert(S == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return r[0] == v ? r[1] : r[0];
+  }
+}
+
+// One compare-exchange step of the sort below: pairs (lane, lane ^ S) of a
+// run of SIZE lanes; in a run that ends descending the lower lane keeps the
+// larger value.
+template <int SIZE, int S>
+__device__ __forceinline__ uint32_t sort_step(uint32_t v, int lane) {
+  const uint32_t o = lane_xor<S>(v);
+  const bool desc = (lane & SIZE) == 0;
+  const bool lower = (lane & S) == 0;
+  return (lower == desc) ? max(v, o) : min(v, o);
+}
+template <int SIZE, int S>
+__device__ __forceinline__ uint32_t sort_merge(uint32_t v, int lane) {
+  v = sort_step<SIZE, S>(v, lane);
+  if constexpr (S > 1) v = sort_merge<SIZE, S / 2>(v, lane);
+  return v;
+}
+
+// Descending bitonic sort of one value per lane across the wavefront: lane
+// i ends with the (i+1)-th largest.  21 compare-exchange steps, all in
+// registers.
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane) {
+  v = sort_merge<2, 1>(v, lane);
+  v = sort_merge<4, 2>(v, lane);
+  v = sort_merge<8, 4>(v, lane);
+  v = sort_merge<16, 8>(v, lane);
+  v = sort_merge<32, 16>(v, lane);
+  return sort_merge<64, 32>(v, lane);
+}
+
+// k-th largest of n > k order keys held in registers (lane l: keys l,
+// l + 64, ...; 0 where there is none, which orders below every key), for
+// k <= 64.  The k-th largest of the lane maxima is a lower bound of the
+// answer (those maxima are k of the keys); when at most `cap` keys reach
+// it -- the usual case: the k largest keys rarely crowd into a few lanes --
+// they are gathered into one value per lane and sorted, and the k-th of
+// them is the answer.  Two wavefront sorts, no histogram.  Returns false
+// (and leaves thr alone) when more keys reach the bound.
+template <int KPL>
+__device__ __forceinline__ bool wave_topk_sorted(const uint32_t* key, int k, int lane, uint32_t* hist,
+                                                 uint32_t& thr) {
+  uint32_t lmax = 0u;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) lmax = max(lmax, key[j]);
+  const uint32_t bound =
+      static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_sort_desc(lmax, lane)), k - 1));
+  int c = 0;   // keys >= bound, gathered into hist[0 .. 63]
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const bool in = key[j] >= bound;
+    const uint64_t m = __ballot(in);
+    const int pos = c + __popcll(m & lanes_below(lane));
+    if (in && pos < kWave) hist[pos] = key[j];
+    c += __popcll(m);
+  }
+  if (c > kWave) return false;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  uint32_t x = lane < c ? hist[lane] : 0u;
+  if (c <= kWave / 2) {   // lanes 32 .. 63 hold zeros: sorting each half leaves lanes 0 .. 31 descending
+    x = sort_merge<2, 1>(x, lane);
+    x = sort_merge<4, 2>(x, lane);
+    x = sort_merge<8, 4>(x, lane);
+    x = sort_merge<16, 8>(x, lane);
+    x = sort_merge<32, 16>(x, lane);
+  } else {
+    x = wave_sort_desc(x, lane);
+  }
+  thr = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), k - 1));
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // hist is read before any later use
+  return true;
+}
+
 // k-th largest of n order keys for one wavefront: `thr` is that key and
 // `rem` how many keys equal to it are taken (the lowest indices first).
 // Radix select over 8-bit digits, skipping the high bits every key shares,
@@ -711,8 +811,7 @@ __device__ __forceinline__ void radix_pick(const uint4 c4, int lane, int& digit,
 // are read through key_at on every pass.
 // With keys in registers and k <= 64, the smallest of the 64 lane maxima is
 // a lower bound of the k-th largest key (each lane holds one key at least
-// that large), so only keys at or above it take part; they are few and
-// rarely share a radix bin.
+// that large), so only keys at or above it take part.
 template <int KPL, typename KeyAt>
 __device__ __forceinline__ void wave_topk_threshold(const uint32_t* key, KeyAt key_at, int n, int k, int lane,
                                                     uint32_t* hist, uint32_t& thr, int& rem) {
@@ -784,64 +883,83 @@ __device__ __forceinline__ void head_select(KeyAt key_at, const uint32_t* key, i
                                             int ncopy = 1) {
   const bool take_all = k >= nc;
   const bool take_none = (k <= 0) || (nc == 0);
-  uint32_t thr = 0;
-  int rem = k;
-  if (!take_all && !take_none) wave_topk_threshold<KPL>(key, key_at, nc, k, lane, hist, thr, rem);
   int nsel = 0;
   if constexpr (KPL > 0) {
-    // Keys in registers: every word's masks first (independent ballots),
-    // then the selection as 64-bit mask arithmetic in scalar registers, then
-    // the stores -- no chain of dependent per-word steps.
-    uint64_t vm[KPL], gm[KPL], em[KPL];   // valid, above the threshold, equal to it
+    // Keys in registers, 0 where a lane holds no candidate (0 orders below
+    // every key).  The selection is built as whole 64-bit masks, one per
+    // register slot (word w, bit i: candidate 64 w + i), in scalar
+    // registers: keys >= the threshold, and when fewer keys equal to it are
+    // taken than there are, those above it plus the lowest-index equal ones.
+    uint32_t kz[KPL];
 #pragma unroll
-    for (int w = 0; w < KPL; ++w) {
-      const bool valid = w * kWave + lane < nc;
-      vm[w] = __ballot(valid);
-      gm[w] = __ballot(valid && key[w] > thr);
-      em[w] = __ballot(valid && key[w] == thr);
-    }
-    int eq_total = 0;
-#pragma unroll
-    for (int w = 0; w < KPL; ++w) eq_total += __popcll(em[w]);
+    for (int j = 0; j < KPL; ++j) kz[j] = lane + kWave * j < nc ? key[j] : 0u;
     uint64_t sm[KPL];
-    int eq_left = rem;   // keys equal to the threshold still to take, lowest indices first
+    if (take_none) {
 #pragma unroll
-    for (int w = 0; w < KPL; ++w) {
-      if (take_none) {
-        sm[w] = 0ull;
-      } else if (take_all) {
-        sm[w] = vm[w];
-      } else if (eq_total == rem) {   // every equal key is taken
-        sm[w] = gm[w] | em[w];
-      } else {
-        uint64_t e = em[w];
-        const int c = __popcll(e);
-        if (c > eq_left) {   // keep the lowest eq_left of them
-          uint64_t keep = 0ull;
-          for (int r = 0; r < eq_left; ++r) {
-            const uint64_t low = e & (~e + 1ull);
-            keep |= low;
-            e ^= low;
-          }
-          e = keep;
+      for (int w = 0; w < KPL; ++w) sm[w] = 0ull;
+    } else if (take_all) {
+#pragma unroll
+      for (int w = 0; w < KPL; ++w) sm[w] = __ballot(w * kWave + lane < nc);
+    } else {
+      uint32_t thr = 0;
+      if (k > kWave || !wave_topk_sorted<KPL>(kz, k, lane, hist, thr)) {
+        int rem_unused;
+        wave_topk_threshold<KPL>(key, key_at, nc, k, lane, hist, thr, rem_unused);
+      }
+      int ge_total = 0;
+#pragma unroll
+      for (int w = 0; w < KPL; ++w) {
+        sm[w] = __ballot(kz[w] >= thr);
+        ge_total += __popcll(sm[w]);
+      }
+      if (ge_total > k) {   // keep only the lowest-index keys equal to thr that fit
+        uint64_t em[KPL];
+        int eq_total = 0;
+#pragma unroll
+        for (int w = 0; w < KPL; ++w) {
+          em[w] = __ballot(kz[w] == thr);
+          eq_total += __popcll(em[w]);
         }
-        eq_left -= __popcll(e);
-        sm[w] = gm[w] | e;
+        int eq_left = k - (ge_total - eq_total);
+#pragma unroll
+        for (int w = 0; w < KPL; ++w) {
+          uint64_t e = em[w];
+          const int c = __popcll(e);
+          if (c > eq_left) {
+            uint64_t keep = 0ull;
+            for (int r = 0; r < eq_left; ++r) {
+              const uint64_t low = e & (~e + 1ull);
+              keep |= low;
+              e ^= low;
+            }
+            e = keep;
+          }
+          eq_left -= __popcll(e);
+          sm[w] = (sm[w] & ~em[w]) | e;
+        }
       }
     }
+    // the bitmap: word w from lane w
+    uint64_t mine = 0ull;
 #pragma unroll
-    for (int w = 0; w < KPL; ++w) {
-      if (w < nwords) {
+    for (int w = 0; w < KPL; ++w)
+      if (lane == w) mine = sm[w];
+    if (lane < nwords)
+      for (int x = 0; x < ncopy; ++x) bits_row[lane + x * nwords] = mine;
+    if (out) {
+#pragma unroll
+      for (int w = 0; w < KPL; ++w) {
         const int pos = nsel + __popcll(sm[w] & lanes_below(lane));
         const bool sel = (sm[w] >> lane) & 1ull;
-        for (int x = 0; x < ncopy; ++x) {
-          if (sel && out && pos < k) out[pos + x * k] = lo + w * kWave + lane;
-          if (lane == 0) bits_row[w + x * nwords] = sm[w];
-        }
+        for (int x = 0; x < ncopy; ++x)
+          if (sel && pos < k) out[pos + x * k] = lo + w * kWave + lane;
         nsel += __popcll(sm[w]);
       }
     }
   } else {
+    uint32_t thr = 0;
+    int rem = k;
+    if (!take_all && !take_none) wave_topk_threshold<KPL>(key, key_at, nc, k, lane, hist, thr, rem);
     int neq = 0;
     // When every key equal to the threshold is taken, the selection is just
     // key >= thr and no rank among equal keys is needed.
