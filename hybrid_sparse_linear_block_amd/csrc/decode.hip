@@ -273,22 +273,57 @@ __device__ __forceinline__ void score_query(const DecodeParams& P, int b, int g,
   }
 }
 
+// Group sums of P (a, c) pairs held in v[0 .. 2P) by each lane of an
+// L-lane group, scattered: each exchange step pairs lanes whose bit L/2
+// differs (row_mirror, row_half_mirror, then the quad swaps of 2 and 1);
+// while more than one pair is held, the lane keeps half of them (the upper
+// half when its bit is set) and adds what its partner sends of that half,
+// afterwards both values are summed with the partner.  Lane lig ends with the
+// sums of pair lig / (L / P0) (P0 the pairs at the start), one step per lane
+// bit instead of a whole reduction per value.
+template <int L, int P>
+__device__ __forceinline__ void pair_sums_scatter(const float* v, int lig, float& a, float& c) {
+  if constexpr (L == 1) {
+    static_assert(P == 1, "one pair per lane at the end");
+    a = v[0];
+    c = v[1];
+  } else {
+    constexpr int kCtrl = L == 16 ? 0x140 : L == 8 ? 0x141 : L == 4 ? 0x4E : 0xB1;
+    if constexpr (P > 1) {
+      const bool hi = (lig & (L / 2)) != 0;
+      float w[P];
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const float keep = hi ? v[P + i] : v[i];
+        const float send = hi ? v[i] : v[P + i];
+        w[i] = keep + dpp_f<kCtrl>(send);
+      }
+      pair_sums_scatter<L / 2, P / 2>(w, lig, a, c);
+    } else {
+      const float w[2] = {v[0] + dpp_f<kCtrl>(v[0]), v[1] + dpp_f<kCtrl>(v[1])};
+      pair_sums_scatter<L / 2, 1>(w, lig, a, c);
+    }
+  }
+}
+
 // Scores of a chunk's candidates from its statistics rows, stored as order
 // keys: score = sigma q . mu + log(1 + sum_c (sigma q_c)^2 / 2 var_c).
 template <int D, int G>
-__device__ __forceinline__ void score_finish(const DecodeParams& P, int b, int g, int c_begin, const StatRows<D>& r,
-                                             const float (&qs)[G][8]) {
+__device__ __forceinline__ void score_finish(const DecodeParams& P, int b, int g, int c_begin, int nc,
+                                             const StatRows<D>& r, const float (&qs)[G][8]) {
   constexpr int LPT = StatRows<D>::LPT;
   constexpr int CPP = StatRows<D>::CPP;
-  static_assert(G <= LPT, "one writer lane per head");
+  static_assert(G <= LPT && (G & (G - 1)) == 0, "whole lane groups per head");
+  constexpr int LPH = LPT / G;                 // lanes holding one head's sums
   const int lig = threadIdx.x % LPT;
   const int slot = threadIdx.x / LPT;
-  const int hsel = lig % G;   // the head whose score this lane finishes
+  const int hsel = lig / LPH;                  // the head whose score this lane holds
+  uint32_t* keys = P.keys + (static_cast<size_t>(b) * P.Hq + g * G) * P.sstride;   // the group's key rows
 #pragma unroll
   for (int it = 0; it < StatRows<D>::NIT; ++it) {
     const float mu[8] = {r.m0[it].x, r.m0[it].y, r.m0[it].z, r.m0[it].w, r.m1[it].x, r.m1[it].y, r.m1[it].z, r.m1[it].w};
     const float va[8] = {r.v0[it].x, r.v0[it].y, r.v0[it].z, r.v0[it].w, r.v1[it].x, r.v1[it].y, r.v1[it].z, r.v1[it].w};
-    float d1 = 0.f, d2 = 0.f;
+    float v[2 * G];   // (q . mu, sum q^2 var / 2) of each head, this lane's 8 channels
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float a = 0.f, c = 0.f;
@@ -297,16 +332,15 @@ __device__ __forceinline__ void score_finish(const DecodeParams& P, int b, int g
         a = fmaf(qs[h][i], mu[i], a);
         c = fmaf(qs[h][i] * qs[h][i], va[i], c);
       }
-      c *= 0.5f;
-      a = reduce_sum_lanes<LPT>(a);
-      c = reduce_sum_lanes<LPT>(c);
-      d1 = (h == hsel) ? a : d1;
-      d2 = (h == hsel) ? c : d2;
+      v[2 * h] = a;
+      v[2 * h + 1] = 0.5f * c;
     }
+    float d1, d2;
+    pair_sums_scatter<LPT, G>(v, lig, d1, d2);
     const int cidx = c_begin + slot + it * CPP;
-    if (lig < G && r.page[it] >= 0) {
+    if (lig % LPH == 0 && cidx < nc) {
       // log(1 + x) via the hardware logarithm: x >= 0, absolute error ~1e-7.
-      P.keys[(static_cast<size_t>(b) * P.Hq + g * G + lig) * P.sstride + cidx] = f32_order_key(d1 + __logf(1.f + d2));
+      keys[hsel * P.sstride + cidx] = f32_order_key(d1 + __logf(1.f + d2));
     }
   }
 }
@@ -335,7 +369,7 @@ __device__ __forceinline__ void score_part(const DecodeParams& P, int b, int g, 
   stat_load<D>(P, g, r);
   float qs[G][8];
   score_query<KV, D, G>(P, b, g, qs);
-  score_finish<D, G>(P, b, g, c_begin, r, qs);
+  score_finish<D, G>(P, b, g, c_begin, nc, r, qs);
 }
 
 // Token-level variant ("SALS: Sparse Attention in Latent Space for KV Cache
