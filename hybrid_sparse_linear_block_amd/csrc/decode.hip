@@ -422,9 +422,12 @@ __device__ __forceinline__ void score_tokens_part(const DecodeParams& P, int b, 
 // The readout's LDS: one instance per kernel.
 template <int D, int G>
 struct ReadoutLds {
-  float red[kThreads / kWave][D / 4][G][4];
+  // the fold's stage is done with before the readout's sums are written
+  union {
+    float red[kThreads / kWave][D / 4][G][4];
+    uint4 fold[kFoldStageBytes / 16];   // block stage, or the statistics' sums
+  };
   float zs[kRoRows];
-  uint4 fold[kFoldStageBytes / 16];   // block stage, or the statistics' sums
 };
 template <int D, int G>
 __device__ __forceinline__ ReadoutLds<D, G>& readout_lds() {
@@ -568,6 +571,7 @@ __device__ __forceinline__ void readout_finish(const DecodeParams& P, int b, int
     const int svcol = rc == 0 && tid < D ? tid : -1;
     float sv = svcol >= 0 ? P.app.sv[nbase + svcol] : 0.f;
     fold_completed_block<KV, D, kThreads, NR, RG>(cb, fold_lds, R.srow, r0 + rg, col4, zrow, R.zr, svcol, sv);
+    __syncthreads();   // the stage is read before the readout's sums overwrite it
     float* Sw = P.app.S + static_cast<size_t>(pair) * D * D;
 #pragma unroll
     for (int i = 0; i < NR; ++i)
