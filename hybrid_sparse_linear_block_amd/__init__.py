@@ -16,6 +16,9 @@ from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhsla.so")
+# the same library with every entry point checking lengths and block tables
+# before it launches (HSLA_DEBUG_CHECKS); open it with open_library()
+DEBUG_LIB_PATH = os.path.join(HERE, "libhsla_debug.so")
 
 HSLA_OK = 0
 HSLA_ERR_INVALID_ARG = -1
@@ -32,7 +35,7 @@ HSLA_MAX_PROFILE_EVENTS = 8
 EXPORTED = ("hsla_status_string", "hsla_version", "hsla_build_workspace_size", "hsla_build_state",
             "hsla_append_token", "hsla_decode_workspace_size", "hsla_decode", "hsla_append_decode",
             "hsla_prefill_chunk_workspace_size", "hsla_prefill_chunk", "hsla_noalloc_scratch_bytes",
-            "hsla_append_decode_noalloc")
+            "hsla_append_decode_noalloc", "hsla_check_tables", "hsla_check_tables_host")
 
 
 class hsla_config(ctypes.Structure):
@@ -80,6 +83,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """A libhsla build at `path` with every entry point's argument types
+    set, independent of the one load() keeps (the debug library, say)."""
     try:
         import torch  # noqa: F401
     except ImportError:
@@ -117,7 +127,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsla_append_decode_noalloc.argtypes = [P(hsla_config), P(hsla_kv_pool), P(hsla_state), vp, vp, vp, vp, vp,
                                                i32, i32, vp, vp, vp]
     lib.hsla_append_decode_noalloc.restype = ctypes.c_int
-    _lib = lib
+    lib.hsla_check_tables.argtypes = [P(hsla_config), P(hsla_kv_pool), vp, i32, i32, i32, vp, vp]
+    lib.hsla_check_tables.restype = ctypes.c_int
+    lib.hsla_check_tables_host.argtypes = [P(hsla_config), i32, i32, vp, vp, i32, i32, i32, vp]
+    lib.hsla_check_tables_host.restype = ctypes.c_int
     return lib
 
 
@@ -257,6 +270,28 @@ def hsla_append_decode_noalloc(cfg: Config, pool: Pool, state: State, k_new, v_n
         ctypes.byref(cfg.c()), ctypes.byref(pool.c()), ctypes.byref(state.c()), _ptr(k_new), _ptr(v_new),
         _ptr(seq_lens_before), _ptr(seq_lens_after), _ptr(q), batch, max_seq_len, _ptr(out), _ptr(sel_idx),
         _stream(stream)))
+
+
+def hsla_check_tables(cfg: Config, pool: Pool, seq_lens, batch: int, max_seq_len: int, extra: int, result,
+                      stream=None) -> None:
+    """Enqueues the length / block-table check; `result` is a device int32[2]
+    (violations, key of the first), valid once the stream has synchronised."""
+    _check("hsla_check_tables", load().hsla_check_tables(
+        ctypes.byref(cfg.c()), ctypes.byref(pool.c()), _ptr(seq_lens), batch, max_seq_len, extra, _ptr(result),
+        _stream(stream)))
+
+
+def hsla_check_tables_host(cfg: Config, max_blocks_per_seq: int, num_pages: int, block_table, seq_lens,
+                           batch: int, max_seq_len: int, extra: int):
+    """The same check on host int32 arrays (numpy); no GPU.  Returns
+    (status, violations, key of the first)."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    res = np.zeros(2, dtype=np.int32)
+    st = load().hsla_check_tables_host(ctypes.byref(cfg.c()), max_blocks_per_seq, num_pages, bt.ctypes.data,
+                                       lens.ctypes.data, batch, max_seq_len, extra, res.ctypes.data)
+    return int(st), int(res[0]), int(res[1])
 
 
 def hsla_prefill_chunk_workspace_size(cfg: Config, batch: int, q_len: int, max_seq_len: int) -> int:

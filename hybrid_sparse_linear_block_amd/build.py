@@ -1,4 +1,7 @@
-"""Build libhsla.so for gfx950 with hipcc (in-tree, next to this file).
+"""Build libhsla.so and libhsla_debug.so for gfx950 with hipcc (in-tree,
+next to this file).  The debug library is the same code with
+HSLA_DEBUG_CHECKS defined in the C ABI layer: every entry point checks the
+lengths and block tables its kernels will use before it launches them.
 
     python hybrid_sparse_linear_block_amd/build.py
 
@@ -18,7 +21,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhsla.so")
-SOURCES = ["hsla_api.cpp", "decode.hip", "build.hip", "append.hip"]
+DEBUG_LIB = os.path.join(HERE, "libhsla_debug.so")
+SOURCES = ["hsla_api.cpp", "decode.hip", "build.hip", "append.hip", "check.hip"]
+DEBUG_DEFINES = ["-DHSLA_DEBUG_CHECKS=1"]
 ARCH = os.environ.get("HSLA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -34,9 +39,10 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, debug = job
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ("_debug" if debug else "") + ".o")
+    cmd = [HIPCC, *CFLAGS, *(DEBUG_DEFINES if debug else []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -47,18 +53,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """Both libraries: the kernels are compiled once; only the C ABI layer
+    differs (HSLA_DEBUG_CHECKS)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + [("hsla_api.cpp", True)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    release, api_debug = objs[:len(SOURCES)], objs[len(SOURCES)]
+    _link(release, LIB)
+    _link([api_debug] + release[1:], DEBUG_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {DEBUG_LIB}")
     return LIB
 
 

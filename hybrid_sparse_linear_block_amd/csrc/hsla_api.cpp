@@ -102,6 +102,77 @@ void record_event(void* ctx, int idx, const char* name) {
   c->prof->recorded = idx + 1;
 }
 
+hsla::CheckTablesArgs check_args(const Problem& p, const hsla_kv_pool* pool, const int32_t* lens, int extra,
+                                 int32_t* result) {
+  hsla::CheckTablesArgs a{};
+  a.block_table = pool->block_table;
+  a.seq_lens = lens;
+  a.result = result;
+  a.batch = p.batch;
+  a.max_blocks = pool->max_blocks_per_seq;
+  a.num_pages = pool->num_pages;
+  a.B = p.B;
+  a.max_seq_len = p.max_seq_len;
+  a.extra = extra;
+  a.min_len = extra > 0 ? 0 : 1;
+  return a;
+}
+
+#ifdef HSLA_DEBUG_CHECKS
+// Debug build: before anything is enqueued, every entry point checks the
+// lengths and block-table entries its kernels will use (on the GPU, into a
+// file-scope device array; the call waits for the result), and returns
+// HSLA_ERR_INVALID_ARG with the first violation on stderr instead of
+// launching on a bad table.  Calls are serialised; the wait makes them
+// unsuitable for graph capture.
+static __device__ int32_t debug_result[2];
+std::mutex g_debug_mutex;
+void* g_debug_ptr[64] = {};
+
+hsla_status debug_check_tables(const Problem& p, const hsla_kv_pool* pool, const int32_t* lens, int extra,
+                               hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_debug_mutex);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return HSLA_ERR_HIP;
+  if (!g_debug_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(debug_result)) != hipSuccess || !ptr) return HSLA_ERR_HIP;
+    g_debug_ptr[dev] = ptr;
+  }
+  int32_t* res = static_cast<int32_t*>(g_debug_ptr[dev]);
+  const hsla::CheckTablesArgs a = check_args(p, pool, lens, extra, res);
+  (void)hipGetLastError();
+  if (hsla::launch_check_tables(a, stream) != hipSuccess || hipStreamSynchronize(stream) != hipSuccess)
+    return HSLA_ERR_HIP;
+  int32_t r[2] = {0, 0};
+  if (hipMemcpy(r, res, sizeof(r), hipMemcpyDeviceToHost) != hipSuccess) return HSLA_ERR_HIP;
+  if (r[0] == 0) return HSLA_OK;
+  const long m = static_cast<long>(a.max_blocks) + 1;
+  const int b = static_cast<int>(r[1] / m);
+  const long j = r[1] % m - 1;
+  int32_t v = 0;
+  if (j < 0) {
+    (void)hipMemcpy(&v, lens + b, sizeof(v), hipMemcpyDeviceToHost);
+    fprintf(stderr, "libhsla (debug checks): %d violation(s); first: sequence %d has length %d (allowed %d .. %d)\n",
+            r[0], b, v, a.min_len, a.max_seq_len - a.extra);
+  } else {
+    (void)hipMemcpy(&v, a.block_table + static_cast<size_t>(b) * a.max_blocks + j, sizeof(v), hipMemcpyDeviceToHost);
+    fprintf(stderr, "libhsla (debug checks): %d violation(s); first: block %ld of sequence %d maps to page %d, "
+            "outside [0, %d)\n", r[0], j, b, v, a.num_pages);
+  }
+  return HSLA_ERR_INVALID_ARG;
+}
+#define HSLA_DEBUG_CHECK(p, pool, lens, extra, stream)                                   \
+  do {                                                                                   \
+    const hsla_status dbg_ = debug_check_tables((p), (pool), (lens), (extra), (stream)); \
+    if (dbg_ != HSLA_OK) return dbg_;                                                    \
+  } while (0)
+#else
+#define HSLA_DEBUG_CHECK(p, pool, lens, extra, stream) \
+  do {                                                 \
+  } while (0)
+#endif
+
 }  // namespace
 
 extern "C" {
@@ -147,6 +218,7 @@ hsla_status hsla_build_state(const hsla_config* cfg, const hsla_kv_pool* pool, c
   a.sv = state->sv;
   a.seq_lens = seq_lens;
   a.ws = static_cast<float*>(workspace);
+  HSLA_DEBUG_CHECK(p, pool, seq_lens, 0, stream);
   (void)hipGetLastError();  // a stale error from another runtime user is not ours
   return hsla::launch_build(p, L, a, stream) == hipSuccess ? HSLA_OK : HSLA_ERR_HIP;
 }
@@ -177,6 +249,7 @@ hsla_status hsla_append_token(const hsla_config* cfg, const hsla_kv_pool* pool, 
   a.v_new = v_new;
   a.seq_lens_before = seq_lens_before;
   a.seq_lens_after = seq_lens_after;
+  HSLA_DEBUG_CHECK(p, pool, seq_lens_before, 1, stream);
   (void)hipGetLastError();
   return hsla::launch_append(p, a, stream) == hipSuccess ? HSLA_OK : HSLA_ERR_HIP;
 }
@@ -185,6 +258,38 @@ size_t hsla_decode_workspace_size(const hsla_config* cfg, int32_t batch, int32_t
   Problem p;
   if (resolve(cfg, batch, max_seq_len, -1, &p) != HSLA_OK) return 0;
   return hsla::decode_layout(p).total;
+}
+
+hsla_status hsla_check_tables(const hsla_config* cfg, const hsla_kv_pool* pool, const int32_t* seq_lens,
+                              int32_t batch, int32_t max_seq_len, int32_t extra, int32_t* result,
+                              hipStream_t stream) {
+  Problem p;
+  hsla_status st = resolve(cfg, batch, max_seq_len, pool ? pool->max_blocks_per_seq : 0, &p);
+  if (st != HSLA_OK) return st;
+  if (!pool || !pool->block_table || !aligned(pool->block_table, 4) || pool->num_pages < 1 ||
+      pool->max_blocks_per_seq < 1)
+    return HSLA_ERR_INVALID_ARG;
+  if (!seq_lens || !aligned(seq_lens, 4) || !result || !aligned(result, 4) || extra < 0) return HSLA_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return hsla::launch_check_tables(check_args(p, pool, seq_lens, extra, result), stream) == hipSuccess
+             ? HSLA_OK
+             : HSLA_ERR_HIP;
+}
+
+hsla_status hsla_check_tables_host(const hsla_config* cfg, int32_t max_blocks_per_seq, int32_t num_pages,
+                                   const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                                   int32_t max_seq_len, int32_t extra, int32_t* result) {
+  Problem p;
+  hsla_status st = resolve(cfg, batch, max_seq_len, max_blocks_per_seq, &p);
+  if (st != HSLA_OK) return st;
+  if (!block_table || !seq_lens || !result || num_pages < 1 || max_blocks_per_seq < 1 || extra < 0)
+    return HSLA_ERR_INVALID_ARG;
+  hsla_kv_pool pool{};
+  pool.block_table = block_table;
+  pool.max_blocks_per_seq = max_blocks_per_seq;
+  pool.num_pages = num_pages;
+  hsla::check_tables_host(check_args(p, &pool, seq_lens, extra, result));
+  return result[0] == 0 ? HSLA_OK : HSLA_ERR_INVALID_ARG;
 }
 
 }  // extern "C"
@@ -222,6 +327,11 @@ hsla_status decode_impl(const hsla_config* cfg, const hsla_kv_pool* pool, const 
   a.sel_idx = sel_idx;
   a.ws = static_cast<char*>(workspace);
   if (app) a.app = *app;
+  if (app) {
+    HSLA_DEBUG_CHECK(p, pool, app->seq_lens_before, 1, stream);
+  } else {
+    HSLA_DEBUG_CHECK(p, pool, seq_lens, 0, stream);
+  }
   ProfileCtx ctx{prof, stream, false};
   if (prof) prof->recorded = 0;
   (void)hipGetLastError();
@@ -381,6 +491,7 @@ hsla_status hsla_prefill_chunk(const hsla_config* cfg, const hsla_kv_pool* pool,
   d.sel_idx = sel_idx;
   d.ws = static_cast<char*>(workspace);
 
+  HSLA_DEBUG_CHECK(seq, pool, seq_lens_before, q_len, stream);
   (void)hipGetLastError();
   // 1. the chunk's page slots and the query rows' lengths; 2. every query
   // against the cache as it stood before the chunk's blocks were folded; 3.

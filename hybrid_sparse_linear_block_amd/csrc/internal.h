@@ -144,4 +144,20 @@ constexpr int kAppendFold = 2;
 hipError_t launch_append(const Problem& p, const AppendArgs& a, hipStream_t stream, int count = 1,
                          int mode = kAppendWriteRows | kAppendFold, int32_t* row_lens = nullptr);
 
+// ---------------------------------------------------------------- checks
+// Lengths and block-table entries as the kernels use them: a row's length T
+// must satisfy min_len <= T and T + extra <= max_seq_len (extra = tokens
+// the call appends), and its entries j < ceil((T + extra) / B) must be pages
+// in [0, num_pages).  result[0] receives the number of violations, result[1]
+// the key of the first (row b's length: b (max_blocks + 1); its entry j:
+// b (max_blocks + 1) + j + 1), INT_MAX when there is none.
+struct CheckTablesArgs {
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t* result;
+  int batch, max_blocks, num_pages, B, max_seq_len, extra, min_len;
+};
+hipError_t launch_check_tables(const CheckTablesArgs& a, hipStream_t stream);   // device arrays
+void check_tables_host(const CheckTablesArgs& a);                               // host arrays
+
 }  // namespace hsla

@@ -52,7 +52,9 @@
  *     enqueued; on a negative status nothing has been enqueued, except
  *     HSLA_ERR_HIP, which reports a failed launch.  Device-side contents
  *     (block tables, lengths) are trusted: a length above max_seq_len or a
- *     page index outside [0, num_pages) is undefined behaviour.
+ *     page index outside [0, num_pages) is undefined behaviour, which
+ *     hsla_check_tables / hsla_check_tables_host detect on request and the
+ *     debug build (libhsla_debug.so) on every call.
  */
 #ifndef HSLA_H
 #define HSLA_H
@@ -220,6 +222,38 @@ hsla_status hsla_append_token(const hsla_config* cfg, const hsla_kv_pool* pool,
                               const hsla_state* state, const void* k_new, const void* v_new,
                               const int32_t* seq_lens_before, int32_t* seq_lens_after,
                               int32_t batch, int32_t max_seq_len, hipStream_t stream);
+
+/* Checks of what the kernels trust [SPLA, "Page Attention and Selection":
+ * the paged cache they read through the block table].  Every row b must
+ * satisfy min_len <= T_b and T_b + extra <= max_seq_len, where T_b =
+ * seq_lens[b], extra = tokens the call appends (0 for hsla_decode and
+ * hsla_build_state, whose lengths include the current token; 1 for the
+ * seq_lens_before of hsla_append_token and hsla_append_decode; q_len for
+ * hsla_prefill_chunk) and min_len = 1 when extra is 0, else 0; and every
+ * entry j < ceil((T_b + extra) / B) of the row must be a page in
+ * [0, num_pages).  Entries past that are not checked (the kernels never use
+ * them as page indices).
+ * result: int32[2]: result[0] = number of violations; result[1] = the first
+ *   one as a key: b (max_blocks_per_seq + 1) for row b's length,
+ *   b (max_blocks_per_seq + 1) + j + 1 for its entry j; INT32_MAX if none.
+ * hsla_check_tables: block_table (pool), seq_lens and result are device
+ *   pointers; the check is enqueued on `stream` (two small kernels, no
+ *   memset, capturable) and result is valid once the stream has
+ *   synchronised.  Returns HSLA_OK once enqueued.
+ * hsla_check_tables_host: the same check on host arrays (block_table
+ *   [batch, max_blocks_per_seq], seq_lens [batch], result [2]); runs on the
+ *   calling thread, needs no GPU, and returns HSLA_OK when there is no
+ *   violation, else HSLA_ERR_INVALID_ARG with result filled.
+ * A library built with HSLA_DEBUG_CHECKS (libhsla_debug.so) runs the device
+ * check inside every entry point that enqueues work, waits for it, and on a
+ * violation returns HSLA_ERR_INVALID_ARG with the first violation on stderr,
+ * enqueueing nothing else. */
+hsla_status hsla_check_tables(const hsla_config* cfg, const hsla_kv_pool* pool, const int32_t* seq_lens,
+                              int32_t batch, int32_t max_seq_len, int32_t extra, int32_t* result,
+                              hipStream_t stream);
+hsla_status hsla_check_tables_host(const hsla_config* cfg, int32_t max_blocks_per_seq, int32_t num_pages,
+                                   const int32_t* block_table, const int32_t* seq_lens, int32_t batch,
+                                   int32_t max_seq_len, int32_t extra, int32_t* result);
 
 /* Bytes of workspace hsla_decode needs for this shape (0 on invalid
  * arguments).  Pure host function. */
