@@ -49,7 +49,8 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b_32k",
                     choices=["llama8b_32k", "needle_128k", "ragged_paged", "hybrid32_32k"])
-    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="independent caches the steps rotate over; 0: enough that the statistics and states\n                    they re-read span twice the 256 MB Infinity Cache")
     ap.add_argument("--deterministic", action="store_true",
                     help="fixed split of the attention work (bitwise reproducible) instead of the dynamic one")
     ap.add_argument("--grouped", action="store_true",
@@ -79,6 +80,25 @@ def parse(argv=None):
     ap.add_argument("--separate-append", action="store_true",
                     help="step = hsla_append_token + hsla_decode instead of one hsla_append_decode call")
     return ap.parse_args(argv)
+
+
+MALL_BYTES = 256 << 20
+
+
+def replicas_for(a):
+    """The caches a run rotates over: --replicas, else enough that the
+    block statistics and linear states one visit of a cache reads (the bytes
+    a step re-reads from its previous visit) span twice the Infinity Cache
+    (MALL), so that no step finds them there, as a model's successive
+    layers would not (the gathered K/V pages are loaded non-temporally and
+    are never re-read across steps anyway)."""
+    if a.replicas > 0:
+        return a.replicas
+    wl = workload(a.workload, a.grouped, a.tokens)
+    blocks = sum(-(-int(t) // wl.block_size) for t in wl.seq_lens)
+    per = blocks * wl.num_kv_heads * wl.head_dim * 8 + \
+        wl.batch * wl.num_kv_heads * (wl.head_dim ** 2 + 2 * wl.head_dim) * 4
+    return max(4, -(-2 * MALL_BYTES // per) + 1)
 
 
 def workload(name, grouped=False, tokens=False):
@@ -367,7 +387,7 @@ def profile_summary(stats_csv, command):
         # this order, one record after the other).
         import shlex
         a = parse(shlex.split(command.split(" -- ", 1)[1])[2:]) if " -- " in command else parse([])
-        K, Wm, R = a.steps, a.warmup, max(1, a.replicas)
+        K, Wm, R = a.steps, a.warmup, replicas_for(a)
         records = [a.workload]
         if a.workload == "llama8b_32k" and not (a.grouped or a.tokens or a.no_secondary):
             records.append("needle_128k")
@@ -500,7 +520,7 @@ def setup(args, extra_steps):
 
     torch.cuda.set_device(0)
     wl = workload(args.workload, args.grouped, args.tokens)
-    steps, warm, R = args.steps, args.warmup, max(1, args.replicas)
+    steps, warm, R = args.steps, args.warmup, replicas_for(args)
     appends_per_replica = -(-(extra_steps + warm) // R) + 1
     wl = W.dataclasses.replace(wl, append_room=1 + -(-appends_per_replica // wl.block_size))
     t0 = time.perf_counter()
@@ -583,7 +603,7 @@ def chunk_main(args):
 
     torch.cuda.set_device(0)
     wl = workload(args.workload, args.grouped, False)
-    Q, steps, warm, R = args.chunk, args.steps, args.warmup, max(1, args.replicas)
+    Q, steps, warm, R = args.chunk, args.steps, args.warmup, replicas_for(args)
     per_rep = -(-(steps + warm) // R) + 1
     room = per_rep * Q
     wl = W.dataclasses.replace(wl, append_room=1 + -(-room // wl.block_size))

@@ -21,6 +21,12 @@ template <typename T>
 __device__ __forceinline__ T ld_global(const void* p) {
   return *(const __attribute__((address_space(1))) T*)(p);
 }
+// The same load marked non-temporal: for data read once per step (gathered
+// K/V pages), so that it does not displace what the next kernels reuse.
+template <typename T>
+__device__ __forceinline__ T ld_global_nt(const void* p) {
+  return __builtin_nontemporal_load((const __attribute__((address_space(1))) T*)(p));
+}
 template <typename T>
 __device__ __forceinline__ T ld_lds(const void* p) {
   return *(const __attribute__((address_space(3))) T*)(p);
@@ -48,6 +54,9 @@ template <>
 struct Row8<KvBf16> {
   uint4 raw;  // 8 bf16
   __device__ __forceinline__ void load(const void* p) { raw = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load_nt(const void* p) {
+    raw = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(p)));
+  }
   __device__ __forceinline__ void zero() { raw = make_uint4(0, 0, 0, 0); }
   __device__ __forceinline__ void to_f32(float (&f)[8]) const {
     f[0] = bf16_lo(raw.x); f[1] = bf16_hi(raw.x);
@@ -63,6 +72,11 @@ struct Row8<KvF32> {
   __device__ __forceinline__ void load(const void* p) {
     a = reinterpret_cast<const float4*>(p)[0];
     b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void load_nt(const void* p) {
+    const auto* q = (const __attribute__((address_space(1))) u32x4*)(p);
+    a = __builtin_bit_cast(float4, __builtin_nontemporal_load(q));
+    b = __builtin_bit_cast(float4, __builtin_nontemporal_load(q + 1));
   }
   __device__ __forceinline__ void zero() {
     a = make_float4(0.f, 0.f, 0.f, 0.f);

@@ -130,7 +130,12 @@ __device__ __forceinline__ int clamp_len(int T, int max_len) { return min(max(T,
 // caches on its own, so no cache-wide release (an L2 writeback, which costs
 // microseconds per workgroup) is needed.  A writer waits for its stores to
 // complete (s_waitcnt) before it publishes a count; a reader issues its
-// loads only after it has read that count.
+// loads only after it has read that count, behind an agent-scope acquire
+// fence.  This leans on gfx950's agent-scope cache policy (stores written
+// through to the memory side that all XCDs share and acknowledged only
+// there, loads that bypass the per-XCD caches), not on a release fence of
+// the HIP memory model, whose L2 writeback per workgroup is the cost
+// avoided.
 __device__ __forceinline__ void store_agent(float* p, float v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1562,8 +1567,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
       for (int i = 0; i < U; ++i) {
         const int t = t0 + grp + NGRP * i;
         x.tok[i] = (ok && t < T) ? t : -1;
-        x.k[i].load(kp + base + lane_off[i]);
-        x.v[i].load(vp + base + lane_off[i]);
+        x.k[i].load_nt(kp + base + lane_off[i]);
+        x.v[i].load_nt(vp + base + lane_off[i]);
       }
       x.fm = (ent >> 20) & kAll;
       const bool sw = t0 < ns || t0 + kUnit > win0;
@@ -1582,8 +1587,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attend(DecodeParams P) {
         x.tok[i] = ok ? t : -1;
         x.fmr[i] = (ent >> 20) & kAll;
         const size_t off = (((static_cast<size_t>(max(page, 0)) * P.Hkv + g) * B + row) * D + lig * 8) * KV::kBytes;
-        x.k[i].load(kp + off);
-        x.v[i].load(vp + off);
+        x.k[i].load_nt(kp + off);
+        x.v[i].load_nt(vp + off);
       }
       // Per-row selection masks differ across the unit; the unit's active set
       // is the union over its blocks.
@@ -1788,13 +1793,15 @@ struct VSlice;
 template <>
 struct VSlice<8> {   // D = 128: 8 channels of a row per lane
   u32x4 r;
-  __device__ __forceinline__ void load(const char* p) { r = ld_global<u32x4>(p); }
+  __device__ __forceinline__ void load(const char* p) { r = ld_global_nt<u32x4>(p); }
+  __device__ __forceinline__ void clear() { r = u32x4{0u, 0u, 0u, 0u}; }
   __device__ __forceinline__ uint32_t word(int i) const { return r[i]; }
 };
 template <>
 struct VSlice<4> {   // D = 64: 4 channels of a row per lane
   u32x2 r;
-  __device__ __forceinline__ void load(const char* p) { r = ld_global<u32x2>(p); }
+  __device__ __forceinline__ void load(const char* p) { r = ld_global_nt<u32x2>(p); }
+  __device__ __forceinline__ void clear() { r = u32x2{0u, 0u}; }
   __device__ __forceinline__ uint32_t word(int i) const { return r[i]; }
 };
 
@@ -1876,9 +1883,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   constexpr int R = 4 * G;              // value rows used: p_hi, p_lo, w_hi, w_lo per head
   constexpr int kAll = (1 << G) - 1;
   constexpr int SL = 16;                // rows per slice
-  __shared__ float s_pub[NW][G][SL];    // scores of a wavefront's current slice
-  __shared__ float m_pub[NW][G];        // running maximum per head
-  __shared__ float c_pub[NW][G];        // rescale factor of the last slice
   __shared__ float red[NW][2][G][D];    // per-wavefront sums of p v and w v
   __shared__ float wst[NW][G][3];       // per-wavefront m, sum p, sum w
   __shared__ uint4 q_lds[16][D / 8 + 1];
@@ -1896,10 +1900,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   const int ns = P.ns;
   const int spb = B / SL;               // slices per block
 
-  if (lane < G) {
-    m_pub[wave][lane] = kNegInf;
-    c_pub[wave][lane] = 1.f;
-  }
   // Query operand rows (heads; rows G..15 zero) staged in LDS, 16 bytes of
   // padding per row so that the 16 rows fall on distinct banks.  Loaded
   // first, in the same round trip as the split's union data; union_share
@@ -1916,7 +1916,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   };
   const char* kp = reinterpret_cast<const char*>(P.k_pages);
   const char* vp = reinterpret_cast<const char*>(P.v_pages);
-  const size_t k_lane = (static_cast<size_t>(n16) * D + q4 * (D / 4)) * 2;
+  const size_t k_lane = (static_cast<size_t>(n16) * D + 8 * q4) * 2;
   const size_t v_lane = (static_cast<size_t>(4 * q4) * D + NT * n16) * 2;
 
   struct Slice {
@@ -1930,7 +1930,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   auto load_slice = [&](int ent, int pg, int sub, bool live, Slice& x) __attribute__((always_inline)) {
     const size_t base = ((static_cast<size_t>(max(pg, 0)) * P.Hkv + g) * B + sub * SL) * D * 2;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) x.k[s] = ld_global<u32x4>(kp + base + k_lane + 16 * s);
+    for (int s = 0; s < KS; ++s) x.k[s] = ld_global_nt<u32x4>(kp + base + k_lane + 64 * s);
 #pragma unroll
     for (int j = 0; j < 4; ++j) x.v[j].load(vp + base + v_lane + static_cast<size_t>(j) * D * 2);
     x.t0 = (live && pg >= 0) ? (ent & 0xFFFFF) * B + sub * SL : kDeadT0;
@@ -1977,9 +1977,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[4];                        // running max of heads 4 q4 + i
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m_run[i] = kNegInf;
+  // Lane (q4, n16) scores column n16, i.e. head hl, and builds value-operand
+  // rows 16 mt + n16, which belong to the same head: its scores never leave
+  // the lane.  m_ref is the head's reference maximum: exponentials are taken
+  // against it, and it moves (with a rescale of the sums) only when a score
+  // exceeds it by more than kLazyMax, so p = e^(s - m_ref) <= e^kLazyMax.
+  const int hl = n16 % G;
+  constexpr float kLazyMax = 8.f;
+  float m_ref = kNegInf;
   float l_acc[MT];                       // sum of this lane's value-operand row (fp32)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) l_acc[mt] = 0.f;
@@ -1997,86 +2002,100 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   // Every fetched slice of the loop is processed, without a branch around
   // it, so that no load stays in flight across the loop back edge.
   auto process = [&](Slice& x) __attribute__((always_inline)) {
-    // ---- scores: rows 4 q4 + i are heads, column n16 is token t0 + n16
-    // lane (q4, n16) takes head n16's channels q4 D/4 + 8 s .. + 8 from LDS
+    // ---- scores, transposed: row 4 q4 + i is token t0 + 4 q4 + i, column
+    // n16 is head hl (the K operand rows are tokens; channels 32 s + 8 q4
+    // .. + 8 of both operands)
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, q_lds[n16][q4 * KS + s]),
-                                                   __builtin_bit_cast(bf16x8_t, x.k[s]), sc, 0, 0, 0);
-    const int t = x.t0 + n16;
-    const bool valid = t < T;
-    const bool sw = t < ns || t >= win0;
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x.k[s]),
+                                                   __builtin_bit_cast(bf16x8_t, q_lds[hl][4 * s + q4]), sc, 0, 0, 0);
+    const int tb = x.t0 + 4 * q4;       // the lane's first token
+    const bool sel = (x.fm >> hl) & 1;
+    float sv[4];
+    bool over = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * q4 + i;
-      if (4 * i >= 4 * G && G < 4) break;   // rows past G (G < 4) are never read
-      const bool inc = valid && h < G && (sw || ((x.fm >> h) & 1));
-      const float sv = inc ? P.sigma * sc[i] : kNegInf;
-      const float mnew = fmaxf(m_run[i], row16_max(sv));
-      const float cf = (mnew == m_run[i]) ? 1.f : fast_exp(m_run[i] - mnew);
-      m_run[i] = mnew;
-      if (h < G) {
-        s_pub[wave][h][n16] = sv;
-        if (n16 == 0) {
-          m_pub[wave][h] = mnew;
-          c_pub[wave][h] = cf;
+    for (int j = 0; j < 4; ++j) {
+      const int t = tb + j;
+      const bool inc = t < T && (sel || t < ns || t >= win0);
+      sv[j] = inc ? P.sigma * sc[j] : kNegInf;
+      over |= sv[j] > m_ref + kLazyMax;
+    }
+    // ---- a reference moves (uniform branch, rare after the first slices):
+    // the head's new maximum over the slice's 16 tokens (lanes n16 + 16 q4),
+    // then the p rows of the sums are rescaled
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      float a, c;
+      lane_pair<16>(mx, a, c);
+      mx = fmaxf(a, c);
+      lane_pair<32>(mx, a, c);
+      mx = fmaxf(a, c);
+      const float mnew = fmaxf(m_ref, mx);
+      const float cf = mnew == m_ref ? 1.f : fast_exp(m_ref - mnew);   // m_ref = -inf: 0
+      m_ref = mnew;
+      float cfh[G];   // head h's factor sits in lane h
+#pragma unroll
+      for (int h = 0; h < G; ++h) cfh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cf), h));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * q4 + i;   // acc row: type r / G, head r % G
+          float f = 1.f;
+#pragma unroll
+          for (int h = 0; h < G; ++h) f = (r < 2 * G && r % G == h) ? cfh[h] : f;
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) acc[mt][tt][i] *= f;
         }
+        if ((16 * mt + n16) < 2 * G) l_acc[mt] *= cf;   // the lane's own p row
       }
     }
-    // ---- rescale the p rows of heads whose maximum moved
+    // ---- value operand rows: lane (q4, n16) builds row r = 16 mt + n16
+    // (type r / G: 0 p_hi, 1 p_lo, 2 w_hi, 3 w_lo, >= 4 unused) for tokens
+    // tb .. tb + 3
+    float pv[4], wv[4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mt + 4 * q4 + i;
-        const float f = r < 2 * G ? c_pub[wave][r % G] : 1.f;
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) acc[mt][tt][i] *= f;
-      }
-    // ---- value operand rows: lane (q4, n16) builds row 16 mt + n16 for
-    // tokens 4 q4 .. 4 q4 + 3
+    for (int j = 0; j < 4; ++j) {
+      const bool inc = sv[j] != kNegInf;
+      pv[j] = inc ? fast_exp(sv[j] - m_ref) : 0.f;
+      // subtraction terms only for tokens the state holds (complete blocks)
+      wv[j] = (inc && tb + j < Ts) ? 1.f + sv[j] : 0.f;
+    }
     s16x4_t av[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int r = 16 * mt + n16;
-      const int typ = r / G;           // 0 p_hi, 1 p_lo, 2 w_hi, 3 w_lo, >= 4 unused
-      const int h = r % G;
-      const float4 s4 = *reinterpret_cast<const float4*>(&s_pub[wave][h][4 * q4]);
-      const float mh = m_pub[wave][h];
-      const float ch = c_pub[wave][h];
-      const float sj[4] = {s4.x, s4.y, s4.z, s4.w};
+      const int typ = (16 * mt + n16) / G;
       uint32_t bits[4];
       float rs = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool inc = sj[j] != kNegInf;
-        const float pv = inc ? fast_exp(sj[j] - mh) : 0.f;
-        // subtraction terms only for tokens the state holds (complete blocks)
-        const float wv = (inc && x.t0 + 4 * q4 + j < Ts) ? 1.f + sj[j] : 0.f;
-        float val = typ < 2 ? pv : wv;
+        float val = typ < 2 ? pv[j] : wv[j];
         val = typ < 4 ? val : 0.f;
         rs += val;
         const uint32_t hi = bf16_bits_rne(val);
         const uint32_t lo = bf16_bits_rne(val - __uint_as_float(hi << 16));
         bits[j] = (typ & 1) ? lo : hi;
       }
-      l_acc[mt] = fmaf(l_acc[mt], typ < 2 ? ch : 1.f, rs);
+      l_acc[mt] += rs;
       av[mt] = __builtin_bit_cast(s16x4_t, make_uint2(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)));
     }
     // ---- values: tile t takes channel t of each lane's V rows; rows past
-    // the end of the sequence may hold anything and enter as zero
-    bool vrow[4];
+    // the end of the sequence may hold anything and enter as zero (uniform
+    // branch: only a sequence's last slice, or a dead one, has such rows)
+    if (x.t0 + SL > T) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vrow[j] = x.t0 + 4 * q4 + j < T;
+      for (int j = 0; j < 4; ++j)
+        if (tb + j >= T) x.v[j].clear();
+    }
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
-      const uint32_t sel = (tt & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t selw = (tt & 1) ? 0x07060302u : 0x05040100u;
       uint32_t vw[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) vw[j] = vrow[j] ? x.v[j].word(tt / 2) : 0u;
-      const uint32_t lo = __builtin_amdgcn_perm(vw[1], vw[0], sel);
-      const uint32_t hi = __builtin_amdgcn_perm(vw[3], vw[2], sel);
+      for (int j = 0; j < 4; ++j) vw[j] = x.v[j].word(tt / 2);
+      const uint32_t lo = __builtin_amdgcn_perm(vw[1], vw[0], selw);
+      const uint32_t hi = __builtin_amdgcn_perm(vw[3], vw[2], selw);
       const s16x4_t bv = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -2191,7 +2210,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
       if (typ == 2) wst[wave][r % G][2] = v;
     }
   }
-  if (lane < G) wst[wave][lane][0] = m_pub[wave][lane];
+  if (lane < G) wst[wave][lane][0] = m_ref;   // lane h < G scores head h
   __syncthreads();
 
   float* outp = P.part + (static_cast<size_t>(pair) * P.max_split + split) * G * P.pstride;
@@ -2242,7 +2261,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     if (tid == 0)
       is_last = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == writers - 1;
     __syncthreads();
-    if (is_last) merge_pair<D, G>(P, pair, b, g, writers, T);
+    if (is_last) {
+      // the reader's side of the hand-off: drop any non-coherent cached
+      // copy before the partial loads (an invalidate, no L2 writeback)
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      merge_pair<D, G>(P, pair, b, g, writers, T);
+    }
   }
 }
 
@@ -2715,8 +2739,8 @@ __global__ __launch_bounds__(kThreads) void k_token_attend(DecodeParams P) {
       heads[u] = nxt[u].x >> 20;
       const size_t off = (((static_cast<size_t>(nxt[u].y) * P.Hkv + g) * P.B + tok[u] % P.B) * D + lig * 8) *
                          KV::kBytes;
-      kr[u].load(kp + off);
-      vr[u].load(vp + off);
+      kr[u].load_nt(kp + off);
+      vr[u].load_nt(vp + off);
     }
     if (it + 1 < niter) fetch_list(it + 1, nxt);
 #pragma unroll
