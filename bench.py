@@ -52,7 +52,9 @@ def parse(argv=None):
     ap.add_argument("--replicas", type=int, default=0,
                     help="independent caches the steps rotate over; 0: enough that the statistics and states\n                    they re-read span twice the 256 MB Infinity Cache")
     ap.add_argument("--deterministic", action="store_true",
-                    help="fixed split of the attention work (bitwise reproducible) instead of the dynamic one")
+                    help="ask for the fixed split of the attention work (bitwise reproducible; also the default)")
+    ap.add_argument("--dynamic-split", action="store_true",
+                    help="the dynamic split of the attention work (workgroups claim a pair's blocks as they go)")
     ap.add_argument("--grouped", action="store_true",
                     help="the grouped-selection variant (one block selection per kv head)")
     ap.add_argument("--chunk", type=int, default=0,
@@ -77,12 +79,22 @@ def parse(argv=None):
                     help="rocprofv3 --pmc counter files of --traffic-run passes -> markdown table per decode kernel")
     ap.add_argument("--no-secondary", action="store_true",
                     help="measure only --workload (the default run adds needle_128k beside llama8b_32k)")
+    ap.add_argument("--phases", action="store_true",
+                    help="per-phase timestamps of the decode kernels (libhsla_phases.so, a diagnostic build) over "
+                         "PHASE_STEPS steps of --workload: a markdown table")
     ap.add_argument("--separate-append", action="store_true",
                     help="step = hsla_append_token + hsla_decode instead of one hsla_append_decode call")
     return ap.parse_args(argv)
 
 
 MALL_BYTES = 256 << 20
+
+
+def split_of(a):
+    """hsla_config.deterministic: 2 (dynamic split) on request, 1 when the
+    fixed split is asked for explicitly, else 0 (the library's default, the
+    fixed split)."""
+    return 2 if a.dynamic_split else (1 if a.deterministic else 0)
 
 
 def replicas_for(a):
@@ -237,6 +249,84 @@ def traffic_run(args):
 
 
 BUILD_RUNS = 4
+PHASE_STEPS = 12
+PHASE_ATTEND, PHASE_SLOTS, PHASE_SCORE, PHASE_MERGE = 4096, 16, 16384, 8192   # include/hsla.h
+
+
+def phase_stats(buf):
+    """Phase times (us) of one step from the stamps of hsla_phase_timestamps,
+    relative to the first scoring workgroup's entry (100 MHz clock)."""
+    na = PHASE_ATTEND * PHASE_SLOTS
+    a = buf[:na].reshape(PHASE_ATTEND, PHASE_SLOTS).astype(np.int64)
+    sc = buf[na:na + 2 * PHASE_SCORE].reshape(PHASE_SCORE, 2).astype(np.int64)
+    m = buf[na + 2 * PHASE_SCORE:].reshape(PHASE_MERGE, 2).astype(np.int64)
+    a, sc, m = a[a[:, 0] > 0], sc[sc[:, 0] > 0], m[m[:, 0] > 0]
+    t0 = sc[:, 0].min()
+    us = lambda x: (x - t0) / 100.0
+    rel = lambda x: float(np.median(x)) / 100.0
+    sel_done = a[:, 2:6].max(1)
+    r = {
+        "scoring: last workgroup entered": us(sc[:, 0].max()),
+        "scoring: workgroup span (median)": rel(sc[:, 1] - sc[:, 0]),
+        "scoring: end": us(sc[:, 1].max()),
+        "attention: first workgroup entered": us(a[:, 0].min()),
+        "attention: last workgroup entered": us(a[:, 0].max()),
+        "prologue: loads staged (median, from entry)": rel(a[:, 1] - a[:, 0]),
+        "prologue: selection done (median, from entry)": rel(sel_done - a[:, 0]),
+        "prologue: union built (median, from entry)": rel(a[:, 6] - a[:, 0]),
+        "prologue: union built (max, from entry)": float((a[:, 6] - a[:, 0]).max()) / 100.0,
+        "attention: prologue done (median)": float(np.median(us(a[:, 6]))),
+        "attention: first wavefront loop done": us(a[:, 7:11].min()),
+        "attention: wavefront loop done (median)": float(np.median(us(a[:, 7:11]))),
+        "attention: last wavefront loop done": us(a[:, 7:11].max()),
+        "attention: partials written (last)": us(a[:, 11].max()),
+        "attention: end": us(a[:, 12].max()),
+    }
+    if len(m):
+        r["merge: first workgroup entered"] = us(m[:, 0].min())
+        r["merge: end"] = us(m[:, 1].max())
+    return r
+
+
+def phases_main(args):
+    """The phase table of --workload: PHASE_STEPS append + decode steps with
+    libhsla_phases.so, each read back after it ran."""
+    import torch
+
+    import hybrid_sparse_linear_block_amd as H
+    lib = H.use_library(H.PHASES_LIB_PATH)
+    nbytes = int(lib.hsla_phase_timestamp_bytes())
+    assert nbytes == 8 * (PHASE_ATTEND * PHASE_SLOTS + 2 * PHASE_SCORE + 2 * PHASE_MERGE), nbytes
+    env = setup(args, PHASE_STEPS)
+    wl, preps, caches, R = env["wl"], env["preps"], env["caches"], env["R"]
+    for i in range(args.warmup):
+        preps[i % R]()
+    torch.cuda.synchronize()
+    buf = np.zeros(nbytes // 8, np.uint64)
+    assert lib.hsla_phase_timestamps(buf.ctypes.data, nbytes, 1) == 0
+    rows, att_bytes = [], []
+    for i in range(PHASE_STEPS):
+        r = (args.warmup + i) % R
+        preps[r]()
+        torch.cuda.synchronize()
+        assert lib.hsla_phase_timestamps(buf.ctypes.data, nbytes, 1) == 0
+        rows.append(phase_stats(buf))
+        att_bytes.append(step_bytes(wl, caches[r].host_lens, preps[r].keep[4].cpu().numpy())["attend"])
+    keys = list(rows[0].keys())
+    med = {k: float(np.median([x[k] for x in rows if k in x])) for k in keys}
+    stream_us = med["attention: wavefront loop done (median)"] - med["attention: prologue done (median)"]
+    lines = [f"Phases of one `hsla_append_decode` step, {wl.name} ({args.warmup} warmup steps, then the median "
+             f"over {PHASE_STEPS} steps, each read back after it ran; us from the first scoring workgroup's entry, "
+             "or from a workgroup's own entry where stated):", "",
+             "| phase | us (median over steps) | min | max |", "|---|---:|---:|---:|"]
+    for k in keys:
+        v = [x[k] for x in rows if k in x]
+        lines.append(f"| {k} | {np.median(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} |")
+    lines += ["", f"Union K/V of the attention kernel: {np.mean(att_bytes) / 1e6:.1f} MB per step; between the median "
+              f"prologue end and the median wavefront loop end ({stream_us:.2f} us) that is "
+              f"{np.mean(att_bytes) / (stream_us * 1e-6) / 1e12:.2f} TB/s (an upper estimate of the streaming rate: "
+              "the window slices prefetched during the prologue are counted in it)."]
+    print("\n".join(lines))
 
 
 def build_run(args):
@@ -387,23 +477,28 @@ def profile_summary(stats_csv, command):
         # this order, one record after the other).
         import shlex
         a = parse(shlex.split(command.split(" -- ", 1)[1])[2:]) if " -- " in command else parse([])
-        K, Wm, R = a.steps, a.warmup, replicas_for(a)
+        import copy
+        K, Wm = a.steps, a.warmup
         records = [a.workload]
         if a.workload == "llama8b_32k" and not (a.grouped or a.tokens or a.no_secondary):
             records.append("needle_128k")
-        phases = [("spot check", 1), ("warmup steps", Wm), ("timed steps", K), ("event-timed steps", K),
-                  ("selection reads", R), ("warm decode-only loop", K)]
-        per_rec = sum(n for _, n in phases)
+
+        def phases_of(rec):   # each record rotates over its own number of caches
+            ar = copy.copy(a)
+            ar.workload = rec
+            return [("spot check", 1), ("warmup steps", Wm), ("timed steps", K), ("event-timed steps", K),
+                    ("selection reads", replicas_for(ar)), ("warm decode-only loop", K)]
+        total = sum(n for rec in records for _, n in phases_of(rec))
         rows = sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"]))
         for kern in ("k_score_readout", "k_attend", "k_merge"):
             us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows if kern in r["Kernel_Name"]]
-            if len(us) != per_rec * len(records):
+            if len(us) != total:
                 continue
             lines += ["", f"`{kern}` dispatches by record and phase (kernel trace of the same run):", "",
                       "| record | phase | calls | avg us | median us |", "|---|---|---:|---:|---:|"]
             at = 0
             for rec in records:
-                for name, n in phases:
+                for name, n in phases_of(rec):
                     seg = us[at:at + n]
                     at += n
                     lines.append(f"| {rec} | {name} | {n} | {np.mean(seg):.2f} | {np.median(seg):.2f} |")
@@ -529,7 +624,7 @@ def setup(args, extra_steps):
     print(f"[bench] {wl.name}: inputs generated in {t_gen:.1f}s", file=sys.stderr, flush=True)
     cfg = config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
                      wl.window, wl.linear_tail, wl.kv_dtype, grouped=wl.grouped, tokens=wl.tokens,
-                     deterministic=int(args.deterministic))
+                     deterministic=split_of(args))
     cap = max(wl.seq_lens) + appends_per_replica + 1
     hip = Hip()
     stream = torch.cuda.current_stream().cuda_stream
@@ -610,7 +705,7 @@ def chunk_main(args):
     inp = W.make_inputs(wl, keep_pairs=False)
     cfg = config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k, wl.num_sink,
                      wl.window, wl.linear_tail, wl.kv_dtype, grouped=wl.grouped,
-                     deterministic=int(args.deterministic))
+                     deterministic=split_of(args))
     cap = max(wl.seq_lens) + room + 1
     caches = []
     for r in range(R):
@@ -686,7 +781,7 @@ def hybrid_main(args):
             inp = f.result()
             cfg = config_for(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.top_k,
                              wl.num_sink, wl.window, wl.linear_tail, wl.kv_dtype,
-                             deterministic=int(args.deterministic))
+                             deterministic=split_of(args))
             dc = DeviceCache(cfg, inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"],
                              capacity_len=cap)
             if not dcs:   # the first launch of the build loads its code; untimed
@@ -787,7 +882,7 @@ def hybrid_main(args):
         "config": {"workload": "hybrid32_32k", "layers": len(layers), "batch": 1, "ctx": int(max(layers[0].seq_lens)),
                    "q_heads": 32, "kv_heads": 8, "head_dim": 128, "block": 64,
                    "top_k": [wl.top_k for wl in layers], "linear_tail": [wl.linear_tail for wl in layers],
-                   "sinks": 4, "window": 512, "attention_split": "fixed" if args.deterministic else "dynamic",
+                   "sinks": 4, "window": 512, "attention_split": "dynamic" if args.dynamic_split else "fixed",
                    "step": (STEP_SEPARATE if args.separate_append else STEP_FUSED) + " per layer",
                    "launch": "eager"},
         "us_per_step": round(eager_s * 1e6, 2),
@@ -934,7 +1029,7 @@ def measure(args, name, primary):
                    "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block": wl.block_size,
                    "top_k": wl.top_k, "sinks": wl.num_sink, "window": wl.window, "replicas": R,
                    "selection": "tokens" if wl.tokens else ("grouped" if wl.grouped else "per_head"),
-                   "attention_split": "fixed" if args.deterministic else "dynamic",
+                   "attention_split": "dynamic" if args.dynamic_split else "fixed",
                    "step": STEP_SEPARATE if args.separate_append else STEP_FUSED},
         "us_per_step": round(us_per_step, 2),
         "gpu_us_per_step": round(gpu_step_us, 2),
@@ -991,6 +1086,9 @@ def main():
         return
     if args.chunk:
         chunk_main(args)
+        return
+    if args.phases:
+        phases_main(args)
         return
     if args.traffic_run:
         traffic_run(args)

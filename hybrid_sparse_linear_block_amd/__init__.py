@@ -19,6 +19,9 @@ LIB_PATH = os.path.join(HERE, "libhsla.so")
 # the same library with every entry point checking lengths and block tables
 # before it launches (HSLA_DEBUG_CHECKS); open it with open_library()
 DEBUG_LIB_PATH = os.path.join(HERE, "libhsla_debug.so")
+# the same library with per-workgroup phase timestamps of the decode kernels
+# (HSLA_PHASE_TIMESTAMPS; a diagnostic build, read by hsla_phase_timestamps)
+PHASES_LIB_PATH = os.path.join(HERE, "libhsla_phases.so")
 
 HSLA_OK = 0
 HSLA_ERR_INVALID_ARG = -1
@@ -30,12 +33,16 @@ HSLA_BF16 = 1
 HSLA_SEL_PER_HEAD = 0
 HSLA_SEL_GROUPED = 1
 HSLA_SEL_TOKEN = 2
+HSLA_SPLIT_DEFAULT = 0
+HSLA_SPLIT_FIXED = 1
+HSLA_SPLIT_DYNAMIC = 2
 HSLA_MAX_PROFILE_EVENTS = 8
 
 EXPORTED = ("hsla_status_string", "hsla_version", "hsla_build_workspace_size", "hsla_build_state",
             "hsla_append_token", "hsla_decode_workspace_size", "hsla_decode", "hsla_append_decode",
             "hsla_prefill_chunk_workspace_size", "hsla_prefill_chunk", "hsla_noalloc_scratch_bytes",
-            "hsla_append_decode_noalloc", "hsla_check_tables", "hsla_check_tables_host")
+            "hsla_append_decode_noalloc", "hsla_check_tables", "hsla_check_tables_host",
+            "hsla_phase_timestamp_bytes", "hsla_phase_timestamps")
 
 
 class hsla_config(ctypes.Structure):
@@ -87,6 +94,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     return _lib
 
 
+def use_library(path: str) -> ctypes.CDLL:
+    """Make the build at `path` (the debug or the phase-timestamp library)
+    the one every binding function calls from now on."""
+    global _lib
+    _lib = open_library(path)
+    return _lib
+
+
 def open_library(path: str) -> ctypes.CDLL:
     """A libhsla build at `path` with every entry point's argument types
     set, independent of the one load() keeps (the debug library, say)."""
@@ -127,6 +142,10 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.hsla_append_decode_noalloc.argtypes = [P(hsla_config), P(hsla_kv_pool), P(hsla_state), vp, vp, vp, vp, vp,
                                                i32, i32, vp, vp, vp]
     lib.hsla_append_decode_noalloc.restype = ctypes.c_int
+    lib.hsla_phase_timestamp_bytes.argtypes = []
+    lib.hsla_phase_timestamp_bytes.restype = sz
+    lib.hsla_phase_timestamps.argtypes = [vp, sz, i32]
+    lib.hsla_phase_timestamps.restype = ctypes.c_int
     lib.hsla_check_tables.argtypes = [P(hsla_config), P(hsla_kv_pool), vp, i32, i32, i32, vp, vp]
     lib.hsla_check_tables.restype = ctypes.c_int
     lib.hsla_check_tables_host.argtypes = [P(hsla_config), i32, i32, vp, vp, i32, i32, i32, vp]

@@ -1,7 +1,9 @@
-"""Build libhsla.so and libhsla_debug.so for gfx950 with hipcc (in-tree,
-next to this file).  The debug library is the same code with
+"""Build libhsla.so, libhsla_debug.so and libhsla_phases.so for gfx950 with
+hipcc (in-tree, next to this file).  The debug library is the same code with
 HSLA_DEBUG_CHECKS defined in the C ABI layer: every entry point checks the
-lengths and block tables its kernels will use before it launches them.
+lengths and block tables its kernels will use before it launches them.  The
+phases library compiles the decode kernels with HSLA_PHASE_TIMESTAMPS: every
+workgroup stamps its phases (a diagnostic build, read by bench.py --phases).
 
     python hybrid_sparse_linear_block_amd/build.py
 
@@ -22,8 +24,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhsla.so")
 DEBUG_LIB = os.path.join(HERE, "libhsla_debug.so")
+PHASES_LIB = os.path.join(HERE, "libhsla_phases.so")
 SOURCES = ["hsla_api.cpp", "decode.hip", "build.hip", "append.hip", "check.hip"]
 DEBUG_DEFINES = ["-DHSLA_DEBUG_CHECKS=1"]
+PHASES_DEFINES = ["-DHSLA_PHASE_TIMESTAMPS=1"]
 ARCH = os.environ.get("HSLA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -40,9 +44,10 @@ CFLAGS = [
 
 
 def _compile(job) -> str:
-    src, debug = job
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ("_debug" if debug else "") + ".o")
-    cmd = [HIPCC, *CFLAGS, *(DEBUG_DEFINES if debug else []), "-c", os.path.join(CSRC, src), "-o", obj]
+    src, variant = job   # variant: "", "debug" or "phases"
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + (f"_{variant}" if variant else "") + ".o")
+    defines = {"": [], "debug": DEBUG_DEFINES, "phases": PHASES_DEFINES}[variant]
+    cmd = [HIPCC, *CFLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -63,17 +68,20 @@ def _link(objs, lib: str) -> None:
 
 
 def build(verbose: bool = True) -> str:
-    """Both libraries: the kernels are compiled once; only the C ABI layer
-    differs (HSLA_DEBUG_CHECKS)."""
+    """The three libraries: the release objects are compiled once; the debug
+    library differs in its C ABI layer (HSLA_DEBUG_CHECKS), the phases
+    library in its decode kernels (HSLA_PHASE_TIMESTAMPS)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = [(s, False) for s in SOURCES] + [("hsla_api.cpp", True)]
+    jobs = [(s, "") for s in SOURCES] + [("hsla_api.cpp", "debug"), ("decode.hip", "phases")]
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         objs = list(ex.map(_compile, jobs))
-    release, api_debug = objs[:len(SOURCES)], objs[len(SOURCES)]
+    release, api_debug, decode_phases = objs[:len(SOURCES)], objs[len(SOURCES)], objs[len(SOURCES) + 1]
+    assert SOURCES[0] == "hsla_api.cpp" and SOURCES[1] == "decode.hip"
     _link(release, LIB)
     _link([api_debug] + release[1:], DEBUG_LIB)
+    _link([release[0], decode_phases] + release[2:], PHASES_LIB)
     if verbose:
-        print(f"built {LIB} and {DEBUG_LIB}")
+        print(f"built {LIB}, {DEBUG_LIB} and {PHASES_LIB}")
     return LIB
 
 

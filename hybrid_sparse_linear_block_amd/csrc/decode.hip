@@ -39,6 +39,45 @@
 
 namespace hsla {
 
+// Diagnostic build (HSLA_PHASE_TIMESTAMPS, libhsla_phases.so): thread 0 of
+// every workgroup stamps the phases of the last launch of each decode kernel
+// with s_memrealtime (a 100 MHz clock shared by the whole device).  Attention
+// workgroups: 0 entry, 1 prologue loads staged, 2 + w selection done by
+// wavefront w, 6 prologue done, 7 + w loop done by wavefront w, 11 partials
+// written, 12 exit; scoring and merge workgroups: entry and exit.  The
+// release build compiles none of it.
+#ifdef HSLA_PHASE_TIMESTAMPS
+__device__ uint64_t g_phase_attend[kPhaseAttendWgs][kPhaseSlots];
+__device__ uint64_t g_phase_score[kPhaseScoreWgs][2];
+__device__ uint64_t g_phase_merge[kPhaseMergeWgs][2];
+#define HSLA_STAMP(slot)                                                         \
+  do {                                                                           \
+    if (threadIdx.x == 0 && blockIdx.x < kPhaseAttendWgs)                        \
+      g_phase_attend[blockIdx.x][slot] = __builtin_amdgcn_s_memrealtime();       \
+  } while (0)
+#define HSLA_STAMP_WAVE(slot)                                                    \
+  do {                                                                           \
+    const uint64_t t_ = __builtin_amdgcn_s_memrealtime();                        \
+    if (threadIdx.x % kWave == 0 && blockIdx.x < kPhaseAttendWgs)                \
+      g_phase_attend[blockIdx.x][(slot) + threadIdx.x / kWave] = t_;             \
+  } while (0)
+// entry now, exit when the kernel returns
+struct PhaseSpan {
+  uint64_t (*arr)[2];
+  size_t idx;
+  __device__ PhaseSpan(uint64_t (*a)[2], size_t n, size_t i) : arr(a), idx(i < n ? i : n) {
+    if (threadIdx.x == 0 && idx < n) arr[idx][0] = __builtin_amdgcn_s_memrealtime();
+    if (idx >= n) arr = nullptr;
+  }
+  __device__ ~PhaseSpan() {
+    if (threadIdx.x == 0 && arr) arr[idx][1] = __builtin_amdgcn_s_memrealtime();
+  }
+};
+#else
+#define HSLA_STAMP(slot) do {} while (0)
+#define HSLA_STAMP_WAVE(slot) do {} while (0)
+#endif
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -648,6 +687,9 @@ __device__ __forceinline__ void readout_part(const DecodeParams& P, int b, int g
 
 template <typename KV, int D, int G>
 __global__ __launch_bounds__(kThreads) void k_score_readout(DecodeParams P) {
+#ifdef HSLA_PHASE_TIMESTAMPS
+  const PhaseSpan span(g_phase_score, kPhaseScoreWgs, static_cast<size_t>(blockIdx.y) * gridDim.x + blockIdx.x);
+#endif
   const int pair = blockIdx.y;
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
@@ -1258,6 +1300,7 @@ __device__ __forceinline__ SplitShare union_share(const DecodeParams& P, char* s
         if (base + tid + u * kThreads < nbt) btrow[base + tid + u * kThreads] = w[u];
     }
   }
+  HSLA_STAMP(1);
   if constexpr (FULL) {
     // The blocks past the candidates (window blocks) are in the union
     // whatever the selection: the caller may start loading them now, so that
@@ -1282,6 +1325,7 @@ __device__ __forceinline__ SplitShare union_share(const DecodeParams& P, char* s
         }
       }
     }
+    HSLA_STAMP_WAVE(2);
   } else if (nc > 0) {
     // grouped selection, as k_select_grouped computes it: each wavefront
     // turns its heads' scores into shares of the head's candidate mass (a
@@ -1887,6 +1931,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   __shared__ float wst[NW][G][3];       // per-wavefront m, sum p, sum w
   __shared__ uint4 q_lds[16][D / 8 + 1];
 
+  HSLA_STAMP(0);
+#ifdef HSLA_PHASE_TIMESTAMPS
+  struct ExitStamp { __device__ ~ExitStamp() { HSLA_STAMP(12); } } exit_stamp;
+#endif
   const int pair = blockIdx.x / P.max_split;
   const int split = blockIdx.x % P.max_split;
   const int tid = threadIdx.x;
@@ -1962,6 +2010,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   extern __shared__ uint64_t dyn_lds[];
   const SplitShare share =
       union_share<G, DYN, FK, GS>(P, reinterpret_cast<char*>(dyn_lds), pair, b, g, split, stage_q, early);
+  HSLA_STAMP(6);
   const int T = share.T;
   const int Ts = state_tokens(P, T, b);           // tokens the linear state holds
   const int win0 = T - P.W;
@@ -2168,6 +2217,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
     }
   }
 
+  HSLA_STAMP_WAVE(7);
   // ---- per-wavefront sums: hi + lo rows, then p v / w v per head to LDS
   // Row r of value tile (mt, t) sits in lane group q4 = (r % 16) / 4, entry
   // r % 4, column n16 = channel NT n16 + t.
@@ -2250,6 +2300,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
       }
     }
   }
+  HSLA_STAMP(11);
   if (P.fused_merge) {
     // The pair's last workgroup to finish merges: every thread's partial
     // stores complete first, then one thread counts the workgroup done.
@@ -2284,6 +2335,9 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
   constexpr int RO = D / kRoRows;   // readout partials per head
   constexpr int NPC = 8;            // splits per lane whose loads are issued together
   __shared__ float part_m[NP][D], part_num[NP][D], part_den[NP][D], part_lnum[NP][D], part_lden[NP][D];
+#ifdef HSLA_PHASE_TIMESTAMPS
+  const PhaseSpan span(g_phase_merge, kPhaseMergeWgs, blockIdx.x);
+#endif
   const int bh = blockIdx.x;
   const int b = bh / P.Hq;
   const int h = bh % P.Hq;
@@ -3012,7 +3066,8 @@ DecodeLayout decode_layout(const Problem& p) {
   // with the selection fused, the scoring kernel zeroes the work counters,
   // so the dynamic split needs that launch
   const bool scores_launched = (p.nc_max > 0) || p.linear_tail;
-  L.dyn = (p.bf16 && !p.tokens && !p.deterministic && L.umax <= kMaxDynList && (!L.fused_sel || scores_launched))
+  L.dyn = (p.bf16 && !p.tokens && p.deterministic == HSLA_SPLIT_DYNAMIC && L.umax <= kMaxDynList &&
+           (!L.fused_sel || scores_launched))
               ? 1 : 0;
   {
     const int want = std::max(1, (kAttendWgsTarget + pairs / 2) / pairs);
@@ -3135,6 +3190,40 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   }
   return p.D == 64 ? dispatch_g<KvF32, 64>(p, L, P, stream, rec, ctx)
                    : dispatch_g<KvF32, 128>(p, L, P, stream, rec, ctx);
+}
+
+size_t phase_bytes() {
+#ifdef HSLA_PHASE_TIMESTAMPS
+  return sizeof(g_phase_attend) + sizeof(g_phase_score) + sizeof(g_phase_merge);
+#else
+  return 0;
+#endif
+}
+
+hipError_t phase_copy(void* host, bool clear) {
+#ifdef HSLA_PHASE_TIMESTAMPS
+  char* h = static_cast<char*>(host);
+  hipError_t e = hipMemcpyFromSymbol(h, HIP_SYMBOL(g_phase_attend), sizeof(g_phase_attend));
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(h + sizeof(g_phase_attend), HIP_SYMBOL(g_phase_score), sizeof(g_phase_score));
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbol(h + sizeof(g_phase_attend) + sizeof(g_phase_score), HIP_SYMBOL(g_phase_merge),
+                            sizeof(g_phase_merge));
+  if (e == hipSuccess && clear) {
+    void* a = nullptr;
+    for (const void* sym : {reinterpret_cast<const void*>(&g_phase_attend), reinterpret_cast<const void*>(&g_phase_score),
+                            reinterpret_cast<const void*>(&g_phase_merge)}) {
+      size_t n = 0;
+      if (e == hipSuccess) e = hipGetSymbolAddress(&a, sym);
+      if (e == hipSuccess) e = hipGetSymbolSize(&n, sym);
+      if (e == hipSuccess) e = hipMemset(a, 0, n);
+    }
+  }
+  return e;
+#else
+  (void)host;
+  (void)clear;
+  return hipErrorNotSupported;
+#endif
 }
 
 }  // namespace hsla

@@ -25,7 +25,7 @@ hsla_status resolve(const hsla_config* cfg, int32_t batch, int32_t max_seq_len,
   if (cfg->linear_tail != 0 && cfg->linear_tail != 1) return HSLA_ERR_INVALID_ARG;
   if (cfg->selection != HSLA_SEL_PER_HEAD && cfg->selection != HSLA_SEL_GROUPED && cfg->selection != HSLA_SEL_TOKEN)
     return HSLA_ERR_INVALID_ARG;
-  if (cfg->deterministic != 0 && cfg->deterministic != 1) return HSLA_ERR_INVALID_ARG;
+  if (cfg->deterministic < HSLA_SPLIT_DEFAULT || cfg->deterministic > HSLA_SPLIT_DYNAMIC) return HSLA_ERR_INVALID_ARG;
   if (!(cfg->scale >= 0.0f) || !isfinite(cfg->scale)) return HSLA_ERR_INVALID_ARG;
   if (batch < 1 || max_seq_len < 1) return HSLA_ERR_INVALID_ARG;
   const int G = cfg->num_q_heads / cfg->num_kv_heads;
@@ -528,6 +528,15 @@ hsla_status hsla_append_decode_noalloc(const hsla_config* cfg, const hsla_kv_poo
   if (!ws) return HSLA_ERR_HIP;
   return hsla_append_decode(cfg, pool, state, k_new, v_new, seq_lens_before, seq_lens_after, q, batch, max_seq_len,
                             out, sel_idx, ws, kNoAllocScratchBytes, stream, nullptr);
+}
+
+size_t hsla_phase_timestamp_bytes(void) { return hsla::phase_bytes(); }
+
+hsla_status hsla_phase_timestamps(void* host, size_t bytes, int32_t clear) {
+  const size_t need = hsla::phase_bytes();
+  if (need == 0) return HSLA_ERR_UNSUPPORTED;
+  if (!host || bytes < need) return HSLA_ERR_INVALID_ARG;
+  return hsla::phase_copy(host, clear != 0) == hipSuccess ? HSLA_OK : HSLA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -22,7 +22,7 @@ inline hipError_t launch_status(const char* what) {
 struct Problem {
   int Hq, Hkv, G, D, B, top_k, ns, W, linear_tail, bf16;
   int grouped;     // one selection per kv head (HSLA_SEL_GROUPED)
-  int deterministic;  // static split-K attention (bitwise reproducible)
+  int deterministic;  // HSLA_SPLIT_*: only HSLA_SPLIT_DYNAMIC selects the dynamic split-K attention
   int tokens;      // token-level variant (HSLA_SEL_TOKEN): candidates are single tokens
   int qrows;       // query rows per sequence: 1, or the chunk length of the multi-query form
                    // (then batch counts query rows: sequences x qrows)
@@ -66,6 +66,17 @@ struct DecodeLayout {
   size_t off_scores, off_ro, off_roz, off_bits, off_ucount, off_ctr, off_part, off_tlist, total;
 };
 DecodeLayout decode_layout(const Problem& p);
+
+// Diagnostic build (HSLA_PHASE_TIMESTAMPS): the per-workgroup phase stamps
+// of the last decode launches, attention [kPhaseAttendWgs][kPhaseSlots]
+// then scoring [kPhaseScoreWgs][2] then merge [kPhaseMergeWgs][2] (uint64);
+// phase_bytes() is 0 in the release build.
+constexpr int kPhaseAttendWgs = 4096;
+constexpr int kPhaseSlots = 16;
+constexpr int kPhaseScoreWgs = 16384;
+constexpr int kPhaseMergeWgs = 8192;
+size_t phase_bytes();
+hipError_t phase_copy(void* host, bool clear);
 
 // ---------------------------------------------------------------- append
 struct AppendArgs {

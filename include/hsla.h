@@ -119,12 +119,18 @@ typedef enum hsla_selection {
  * kv_dtype: hsla_dtype of keys, values, queries and appended tokens.
  * scale: sigma; 0 selects 1/sqrt(head_dim).
  * selection: hsla_selection (0 = per head).
- * deterministic: 1 = bitwise reproducible results: every attention
- *   workgroup of a (sequence, kv head) takes a fixed share of its exact
- *   blocks.  0 = those workgroups claim the blocks from a shared counter as
- *   they go, so that workgroups on faster XCDs take more; the summation
- *   order, and so the last bits of the output, then vary from run to run
- *   (selections do not).  fp32 keys/values always run the fixed split. */
+ * deterministic: how the attention workgroups of a (sequence, kv head)
+ *   share its exact blocks.  HSLA_SPLIT_FIXED (1): each takes a fixed share;
+ *   results are bitwise reproducible.  HSLA_SPLIT_DYNAMIC (2): they claim
+ *   the blocks from a shared counter as they go, so that workgroups on
+ *   faster XCDs take more; the summation order, and so the last bits of
+ *   the output, then vary from run to run (selections do not).
+ *   HSLA_SPLIT_DEFAULT (0): the library's choice, the fixed split (it
+ *   measured as fast or faster at every workload here).  fp32 keys/values
+ *   always run the fixed split.  Other values: HSLA_ERR_INVALID_ARG. */
+#define HSLA_SPLIT_DEFAULT 0
+#define HSLA_SPLIT_FIXED 1
+#define HSLA_SPLIT_DYNAMIC 2
 typedef struct hsla_config {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -322,6 +328,25 @@ hsla_status hsla_append_decode_noalloc(const hsla_config* cfg, const hsla_kv_poo
                                        const void* k_new, const void* v_new, const int32_t* seq_lens_before,
                                        int32_t* seq_lens_after, const void* q, int32_t batch, int32_t max_seq_len,
                                        float* out, int32_t* sel_idx, hipStream_t stream);
+
+/* Diagnostics: per-workgroup phase timestamps of the decode kernels (not
+ * part of the method; for measuring where a step's time goes).  Only a
+ * library built with HSLA_PHASE_TIMESTAMPS (libhsla_phases.so) records
+ * them; there every workgroup of the last launch of each decode kernel
+ * stamps its phases with the device's 100 MHz real-time counter (uint64):
+ * attention workgroups [4096][16] (slots: 0 entry, 1 prologue loads staged,
+ * 2..5 selection done per wavefront, 6 prologue done, 7..10 loop done per
+ * wavefront, 11 partials written, 12 exit; row = workgroup index), then
+ * scoring workgroups [16384][2] (entry, exit; row = pair x scoring grid +
+ * workgroup), then merge workgroups [8192][2]; unused rows are 0.
+ * hsla_phase_timestamp_bytes: the size of that host buffer; 0 in other
+ * builds.  Pure host function.
+ * hsla_phase_timestamps: copies the stamps into `host` (a host pointer of
+ * at least that many bytes) and, when clear != 0, zeroes them on the device.
+ * Synchronous on the null stream.  HSLA_ERR_UNSUPPORTED in other builds,
+ * HSLA_ERR_INVALID_ARG for a missing or short buffer. */
+size_t hsla_phase_timestamp_bytes(void);
+hsla_status hsla_phase_timestamps(void* host, size_t bytes, int32_t clear);
 
 /* Bytes of workspace hsla_prefill_chunk needs (0 on invalid arguments or
  * an unsupported chunk).  Pure host function. */

@@ -218,7 +218,7 @@ def test_prefill_from_empty_in_chunks(kv):
     print(f"  worst row error over {n_chunks} chunks {worst_all:.3e}")
 
 
-@pytest.mark.parametrize("deterministic", [1, 0])
+@pytest.mark.parametrize("deterministic", [1, 2])
 def test_chunk_graph_replays_match_eager_chunks(deterministic):
     # two chunks per captured graph (the ping-ponged length buffers return),
     # replayed three times with eager torch work and synchronisation in
@@ -278,7 +278,7 @@ def test_chunk_graph_replays_match_eager_chunks(deterministic):
         torch.cuda.synchronize()
         wo, wsel = want[r]
         assert np.array_equal(gsel, wsel), r
-        if deterministic:
+        if deterministic == 1:
             assert np.array_equal(go, wo), r
         else:
             err = np.abs(go - wo).max(axis=-1) / np.abs(wo).max(axis=-1)

@@ -88,10 +88,11 @@ def test_full_size_workload(name):
                     assert blk in sel[b, h].tolist(), (b, g, blk, h)
 
 
-@pytest.mark.parametrize("name", ["llama8b_32k", "needle_128k"])
-def test_full_size_append_decode(name):
+@pytest.mark.parametrize("name,split", [("llama8b_32k", 0), ("needle_128k", 0), ("llama8b_32k", 2)])
+def test_full_size_append_decode(name, split):
     """The call the benchmark times: one hsla_append_decode with the
-    default (dynamic) split at full size -- the token's page write, the fold
+    default (fixed) split at full size (and once with the dynamic split,
+    split = 2) -- the token's page write, the fold
     of a block it completes with that block's statistics, and the decode at
     T + 1 -- checked against the oracle at T + 1 on sampled pairs.  The
     first sequence is one token shorter, so that its appended token
@@ -99,9 +100,9 @@ def test_full_size_append_decode(name):
     base = FULL[name]()
     lens = list(base.seq_lens)
     lens[0] -= 1
-    wl = W.dataclasses.replace(base, seq_lens=tuple(lens))
+    wl = W.dataclasses.replace(base, seq_lens=tuple(lens), deterministic=split)
     assert (wl.seq_lens[0] + 1) % wl.block_size == 0
-    _announce(wl, "full size, hsla_append_decode, sampled pairs at T + 1")
+    _announce(wl, f"full size, hsla_append_decode (split {split}), sampled pairs at T + 1")
     inp = W.make_inputs(wl, keep_pairs=False)
     dc = DeviceCache(cfg_of(wl), inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"],
                      capacity_len=int(max(wl.seq_lens)) + 1)

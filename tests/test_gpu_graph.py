@@ -47,7 +47,7 @@ def _snapshot(preps):
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "append_decode"])
-@pytest.mark.parametrize("deterministic", [1, 0])
+@pytest.mark.parametrize("deterministic", [1, 2])
 def test_graph_replays_match_eager_steps(deterministic, fused):
     # 4157 tokens: the third step's token completes block 64, so the replays
     # also fold a block into the state and write its statistics
@@ -91,7 +91,7 @@ def test_graph_replays_match_eager_steps(deterministic, fused):
         torch.cuda.synchronize()
         for li, ((go, gsel), (wo, wsel)) in enumerate(zip(got, want[r])):
             assert np.array_equal(gsel, wsel), (r, li)
-            if deterministic:
+            if deterministic == 1:
                 assert np.array_equal(go, wo), (r, li)
             else:
                 for b in range(go.shape[0]):

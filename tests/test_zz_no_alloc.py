@@ -37,7 +37,7 @@ def _noalloc_step(dc, k, v, q, out, sel):
     dc.host_lens += 1
 
 
-@pytest.mark.parametrize("deterministic", [1, 0])
+@pytest.mark.parametrize("deterministic", [1, 2])
 def test_noalloc_matches_workspace_entry_point(deterministic):
     assert H.hsla_noalloc_scratch_bytes() == 16 << 20
     for i, shape in enumerate(CALLS):
@@ -57,7 +57,7 @@ def test_noalloc_matches_workspace_entry_point(deterministic):
         _noalloc_step(got, k, v, q, o_got, s_got)
         torch.cuda.synchronize()
         assert torch.equal(s_got, s_ref)
-        if deterministic:
+        if deterministic == 1:
             assert torch.equal(o_got, o_ref)
         else:
             a, b = o_got.cpu().numpy(), o_ref.cpu().numpy()

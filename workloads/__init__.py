@@ -59,7 +59,7 @@ class Workload:
     scale: float = 0.0            # 0 means 1/sqrt(head_dim)
     layer: int = 0
     grouped: int = 0              # one block selection per kv head
-    deterministic: int = 0        # fixed split of the attention work (bitwise reproducible)
+    deterministic: int = 0        # attention split: 0 the library's default, 1 fixed (bitwise reproducible), 2 dynamic
     tokens: int = 0               # token-level variant: top_k counts single tokens
 
     @property
