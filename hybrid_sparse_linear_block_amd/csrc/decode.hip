@@ -1838,6 +1838,7 @@ template <>
 struct VSlice<8> {   // D = 128: 8 channels of a row per lane
   u32x4 r;
   __device__ __forceinline__ void load(const char* p) { r = ld_global_nt<u32x4>(p); }
+  __device__ __forceinline__ void load_cached(const char* p) { r = ld_global<u32x4>(p); }
   __device__ __forceinline__ void clear() { r = u32x4{0u, 0u, 0u, 0u}; }
   __device__ __forceinline__ uint32_t word(int i) const { return r[i]; }
 };
@@ -1845,6 +1846,7 @@ template <>
 struct VSlice<4> {   // D = 64: 4 channels of a row per lane
   u32x2 r;
   __device__ __forceinline__ void load(const char* p) { r = ld_global_nt<u32x2>(p); }
+  __device__ __forceinline__ void load_cached(const char* p) { r = ld_global<u32x2>(p); }
   __device__ __forceinline__ void clear() { r = u32x2{0u, 0u}; }
   __device__ __forceinline__ uint32_t word(int i) const { return r[i]; }
 };
@@ -1918,7 +1920,10 @@ __device__ __forceinline__ void merge_pair(const DecodeParams& P, int pair, int 
   }
 }
 
-template <int D, int G, bool DYN, int FK, bool GS>
+// NTL: the K/V loads are non-temporal (decode: each page is read once per
+// step); the multi-query form, whose query rows of one sequence re-read the
+// same pages from L2, loads them normally.
+template <int D, int G, bool DYN, int FK, bool GS, bool NTL = true>
 __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   constexpr int NW = kThreads / kWave;
   constexpr int KS = D / 32;            // score MFMAs per slice (32 channels each)
@@ -1978,9 +1983,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
   auto load_slice = [&](int ent, int pg, int sub, bool live, Slice& x) __attribute__((always_inline)) {
     const size_t base = ((static_cast<size_t>(max(pg, 0)) * P.Hkv + g) * B + sub * SL) * D * 2;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) x.k[s] = ld_global_nt<u32x4>(kp + base + k_lane + 64 * s);
+    for (int s = 0; s < KS; ++s)
+      x.k[s] = NTL ? ld_global_nt<u32x4>(kp + base + k_lane + 64 * s) : ld_global<u32x4>(kp + base + k_lane + 64 * s);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x.v[j].load(vp + base + v_lane + static_cast<size_t>(j) * D * 2);
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (NTL) x.v[j].load(vp + base + v_lane + static_cast<size_t>(j) * D * 2);
+      else x.v[j].load_cached(vp + base + v_lane + static_cast<size_t>(j) * D * 2);
+    }
     x.t0 = (live && pg >= 0) ? (ent & 0xFFFFF) * B + sub * SL : kDeadT0;
     x.fm = (ent >> 20) & kAll;
     // keep the loads ahead of the previous slice's arithmetic
@@ -2995,7 +3004,14 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
     if constexpr (KV::kBytes == 2) {
       // keys per lane of the fused selection: 8 up to 512 candidates
       const bool fk8 = p.nc_max <= 8 * kWave;
-      if (L.fused_sel && p.grouped && P.dyn)   // fused grouped selection: up to 512 candidates
+      const bool rows = p.qrows > 1;   // multi-query form: cached K/V loads
+      if (rows && !P.dyn && L.fused_sel && p.grouped)
+        hipLaunchKernelGGL((k_attend_mfma<D, G, false, 8, true, false>), grid, dim3(kThreads), lds, stream, P);
+      else if (rows && !P.dyn && !(L.fused_sel && p.grouped) && fk8)
+        hipLaunchKernelGGL((k_attend_mfma<D, G, false, 8, false, false>), grid, dim3(kThreads), lds, stream, P);
+      else if (rows && !P.dyn && !(L.fused_sel && p.grouped))
+        hipLaunchKernelGGL((k_attend_mfma<D, G, false, 16, false, false>), grid, dim3(kThreads), lds, stream, P);
+      else if (L.fused_sel && p.grouped && P.dyn)   // fused grouped selection: up to 512 candidates
         hipLaunchKernelGGL((k_attend_mfma<D, G, true, 8, true>), grid, dim3(kThreads), lds, stream, P);
       else if (L.fused_sel && p.grouped)
         hipLaunchKernelGGL((k_attend_mfma<D, G, false, 8, true>), grid, dim3(kThreads), lds, stream, P);
