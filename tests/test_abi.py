@@ -64,6 +64,8 @@ BAD_CONFIGS = [
     (dict(kv_dtype=7), H.HSLA_ERR_UNSUPPORTED),
     (dict(scale=float("nan")), H.HSLA_ERR_INVALID_ARG),
     (dict(scale=-1.0), H.HSLA_ERR_INVALID_ARG),
+    (dict(deterministic=3), H.HSLA_ERR_INVALID_ARG),
+    (dict(deterministic=-1), H.HSLA_ERR_INVALID_ARG),
 ]
 
 FAKE = 1 << 20   # an aligned non-null address; never dereferenced because validation fails first
@@ -249,3 +251,27 @@ def test_noalloc_rejects_a_shape_beyond_its_scratch():
     st = lib.hsla_append_decode_noalloc(ctypes.byref(cfg(head_dim=96).c()), ctypes.byref(pool), ctypes.byref(state),
                                         fake, fake, fake, fake + 4096, fake, 1, 1024, fake, None, None)
     assert st == H.HSLA_ERR_UNSUPPORTED
+
+
+def test_split_choices_are_accepted():
+    """deterministic: 0 (the library's default), 1 (fixed) and 2 (dynamic)
+    all give a workspace size."""
+    for split in (H.HSLA_SPLIT_DEFAULT, H.HSLA_SPLIT_FIXED, H.HSLA_SPLIT_DYNAMIC):
+        c = cfg(deterministic=split)
+        assert H.hsla_decode_workspace_size(c, 8, 32768) > 0, split
+
+
+def test_phase_timestamps_only_in_the_diagnostic_build():
+    """The release library records no phase stamps; libhsla_phases.so
+    reports the documented buffer size and rejects a short buffer (host-side
+    checks, no GPU)."""
+    lib = H.load()
+    assert lib.hsla_phase_timestamp_bytes() == 0
+    buf = (ctypes.c_uint64 * 4)()
+    assert lib.hsla_phase_timestamps(ctypes.addressof(buf), 32, 0) == H.HSLA_ERR_UNSUPPORTED
+    if not os.path.exists(H.PHASES_LIB_PATH):
+        pytest.skip("libhsla_phases.so not built")
+    ph = H.open_library(H.PHASES_LIB_PATH)
+    assert ph.hsla_phase_timestamp_bytes() == 8 * (4096 * 16 + 16384 * 2 + 8192 * 2)
+    assert ph.hsla_phase_timestamps(ctypes.addressof(buf), 32, 0) == H.HSLA_ERR_INVALID_ARG
+    assert ph.hsla_phase_timestamps(None, 1 << 30, 0) == H.HSLA_ERR_INVALID_ARG
