@@ -2335,14 +2335,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_attend_mfma(DecodeParams P) {
 // ---------------------------------------------------------------------------
 // One workgroup per (sequence, query head); NP = 256 / D lanes share a
 // channel and walk the splits with a running maximum, then combine.  Every
-// load of the usual case -- the first NP * 8 splits' partials, the readout
+// load of the usual case -- the first NP * NPC splits' partials, the readout
 // partials, sv, the union size and the sequence length -- goes out in one
 // round trip: partials of splits past the union size are loaded and ignored.
-template <int D, int G>
+// NPC (splits per lane loaded together) is the launch's splits per lane,
+// rounded up to 2, 4, 8 or 16, so that up to 16 NP splits take one round
+// trip and few splits issue no surplus loads.
+template <int D, int G, int NPC>
 __global__ __launch_bounds__(kThreads) void k_merge(DecodeParams P) {
   constexpr int NP = kThreads / D;
   constexpr int RO = D / kRoRows;   // readout partials per head
-  constexpr int NPC = 8;            // splits per lane whose loads are issued together
   __shared__ float part_m[NP][D], part_num[NP][D], part_den[NP][D], part_lnum[NP][D], part_lden[NP][D];
 #ifdef HSLA_PHASE_TIMESTAMPS
   const PhaseSpan span(g_phase_merge, kPhaseMergeWgs, blockIdx.x);
@@ -2903,6 +2905,22 @@ __global__ __launch_bounds__(kThreads) void k_token_attend(DecodeParams P) {
 // The token-level variant after the scoring launch: per-head selection over
 // the candidate tokens, the pairs' exact token lists, attention over them,
 // merge.
+// The merge kernel with NPC matched to the splits each of its lanes walks.
+template <int D, int G>
+hipError_t launch_merge(const Problem& p, const DecodeLayout& L, const DecodeParams& P, hipStream_t stream) {
+  const int per_lane = ceil_div(L.max_split, kThreads / D);
+  const dim3 grid(p.batch * p.Hq);
+  if (per_lane <= 2)
+    hipLaunchKernelGGL((k_merge<D, G, 2>), grid, dim3(kThreads), 0, stream, P);
+  else if (per_lane <= 4)
+    hipLaunchKernelGGL((k_merge<D, G, 4>), grid, dim3(kThreads), 0, stream, P);
+  else if (per_lane <= 8)
+    hipLaunchKernelGGL((k_merge<D, G, 8>), grid, dim3(kThreads), 0, stream, P);
+  else
+    hipLaunchKernelGGL((k_merge<D, G, 16>), grid, dim3(kThreads), 0, stream, P);
+  return launch_status("k_merge");
+}
+
 template <typename KV, int D, int G>
 hipError_t launch_tokens(const Problem& p, const DecodeLayout& L, const DecodeParams& P, hipStream_t stream,
                          RecordFn rec, void* ctx, int ev) {
@@ -2938,8 +2956,7 @@ hipError_t launch_tokens(const Problem& p, const DecodeLayout& L, const DecodePa
   e = launch_status("k_token_attend");
   if (e != hipSuccess) return e;
   if (rec) rec(ctx, ev++, "merge");
-  hipLaunchKernelGGL((k_merge<D, G>), dim3(p.batch * p.Hq), dim3(kThreads), 0, stream, P);
-  e = launch_status("k_merge");
+  e = launch_merge<D, G>(p, L, P, stream);
   if (e != hipSuccess) return e;
   if (rec) rec(ctx, ev, nullptr);
   return hipSuccess;
@@ -3033,8 +3050,7 @@ hipError_t launch_typed(const Problem& p, const DecodeLayout& L, const DecodePar
   }
   if (!P.fused_merge) {   // else the last attention workgroup of each pair merged it
     if (rec) rec(ctx, ev++, "merge");
-    hipLaunchKernelGGL((k_merge<D, G>), dim3(p.batch * p.Hq), dim3(kThreads), 0, stream, P);
-    hipError_t e = launch_status("k_merge");
+    hipError_t e = launch_merge<D, G>(p, L, P, stream);
     if (e != hipSuccess) return e;
   }
   if (rec) rec(ctx, ev, nullptr);
