@@ -326,8 +326,8 @@ def phases_main(args):
         lines.append(f"| {k} | {np.median(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} |")
     lines += ["", f"Union K/V of the attention kernel: {np.mean(att_bytes) / 1e6:.1f} MB per step; between the median "
               f"prologue end and the median wavefront loop end ({stream_us:.2f} us) that is "
-              f"{np.mean(att_bytes) / (stream_us * 1e-6) / 1e12:.2f} TB/s (an upper estimate of the streaming rate: "
-              "the window slices prefetched during the prologue are counted in it)."]
+              f"{np.mean(att_bytes) / (stream_us * 1e-6) / 1e12:.2f} TB/s (with the dynamic split an upper estimate of "
+              "the streaming rate: its window slices prefetched during the prologue are counted in it)."]
     print("\n".join(lines))
 
 
