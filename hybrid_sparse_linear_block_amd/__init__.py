@@ -33,6 +33,8 @@ HSLA_BF16 = 1
 HSLA_SEL_PER_HEAD = 0
 HSLA_SEL_GROUPED = 1
 HSLA_SEL_TOKEN = 2
+HSLA_STATE_BLOCKS = 0
+HSLA_STATE_TOKENS = 1
 HSLA_SPLIT_DEFAULT = 0
 HSLA_SPLIT_FIXED = 1
 HSLA_SPLIT_DYNAMIC = 2
@@ -51,7 +53,8 @@ class hsla_config(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("num_sink", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("linear_tail", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("selection", ctypes.c_int32), ("deterministic", ctypes.c_int32)]
+                ("selection", ctypes.c_int32), ("deterministic", ctypes.c_int32),
+                ("state_span", ctypes.c_int32)]
 
 
 class hsla_kv_pool(ctypes.Structure):
@@ -179,11 +182,12 @@ class Config:
     scale: float = 0.0
     selection: int = HSLA_SEL_PER_HEAD
     deterministic: int = 0
+    state_span: int = HSLA_STATE_BLOCKS
 
     def c(self) -> hsla_config:
         return hsla_config(self.num_q_heads, self.num_kv_heads, self.head_dim, self.block_size, self.top_k,
                            self.num_sink, self.window, self.linear_tail, self.kv_dtype, self.scale,
-                           self.selection, self.deterministic)
+                           self.selection, self.deterministic, self.state_span)
 
 
 def _ptr(t) -> Optional[int]:

@@ -39,6 +39,7 @@ struct BuildParams {
   const int32_t* seq_lens;
   float* ws;
   int Hkv, B, max_blocks, max_seq_len, chunk, nchunk;
+  int state_all;   // the state takes every token, not only those of complete blocks
   size_t part_stride;
 };
 
@@ -46,6 +47,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ int clamp_len(int T, int max_len) { return min(max(T, 0), max_len); }
 __device__ __forceinline__ int full_blocks_len(int T, int B) { return T - T % B; }
+// Tokens the state is built over: those of complete blocks, or all of them.
+__device__ __forceinline__ int state_len(const BuildParams& P, int b) {
+  const int T = clamp_len(P.seq_lens[b], P.max_seq_len);
+  return P.state_all ? T : full_blocks_len(T, P.B);
+}
 
 // ---------------------------------------------------------------------------
 // bf16: MFMA
@@ -89,9 +95,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_build_bf16(BuildParams P) {
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
   const int chunk = blockIdx.x;
-  // the state holds the tokens of complete blocks; the incomplete last
-  // block's tokens lie inside the window and are attended exactly
-  const int T = full_blocks_len(clamp_len(P.seq_lens[b], P.max_seq_len), P.B);
+  // the state holds the tokens of complete blocks (the incomplete last
+  // block's tokens lie inside the window and are attended exactly), or
+  // every token when the caller keeps a per-token state
+  const int T = state_len(P, b);
   const int c_begin = chunk * P.chunk;
   const int c_end = min(c_begin + P.chunk, T);
   if (c_begin >= c_end) {
@@ -313,9 +320,10 @@ __global__ __launch_bounds__(kThreads) void k_build_f32(BuildParams P) {
   const int b = pair / P.Hkv;
   const int g = pair % P.Hkv;
   const int chunk = blockIdx.x;
-  // the state holds the tokens of complete blocks; the incomplete last
-  // block's tokens lie inside the window and are attended exactly
-  const int T = full_blocks_len(clamp_len(P.seq_lens[b], P.max_seq_len), P.B);
+  // the state holds the tokens of complete blocks (the incomplete last
+  // block's tokens lie inside the window and are attended exactly), or
+  // every token when the caller keeps a per-token state
+  const int T = state_len(P, b);
   const int c_begin = chunk * P.chunk;
   const int c_end = min(c_begin + P.chunk, T);
   const int tid = threadIdx.x;
@@ -501,6 +509,7 @@ hipError_t launch_build(const Problem& p, const BuildLayout& L, const BuildArgs&
   P.max_seq_len = p.max_seq_len;
   P.chunk = L.chunk;
   P.nchunk = L.nchunk;
+  P.state_all = p.state_all;
   P.part_stride = L.part_stride;
   return p.D == 64 ? launch_d<64>(p, L, P, s) : launch_d<128>(p, L, P, s);
 }

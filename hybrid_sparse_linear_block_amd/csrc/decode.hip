@@ -155,6 +155,7 @@ struct DecodeParams {
   int tokens;       // token-level variant: candidates are single tokens, scored by their keys
   int qrows;        // query rows per sequence: 1, or the chunk length of the multi-query form
   int chunk;        // multi-query form: the state holds the whole blocks before the chunk
+  int state_all;    // the caller's state holds every token (n = T)
   int bsel;         // candidate granularity: the block size, or 1 for the token-level variant
   int32_t* tlist;   // token-level variant: each pair's exact token list [pairs, umax] x (token | heads << 20, page)
   SelLayout sl;
@@ -212,6 +213,7 @@ __device__ __forceinline__ int state_pair(const DecodeParams& P, int pair) {
 // folded in after it.  Every token from there to T is in the row's window
 // (chunk length <= W - B + 1), so the exact part covers it.
 __device__ __forceinline__ int state_tokens(const DecodeParams& P, int T, int b) {
+  if (P.state_all) return T;   // a per-token state (never with the chunk form)
   const int t = P.chunk ? T - 1 - b % P.qrows : T;
   return t - t % P.B;
 }
@@ -3189,6 +3191,7 @@ hipError_t launch_decode(const Problem& p, const DecodeLayout& L, const DecodeAr
   P.tokens = p.tokens;
   P.qrows = p.qrows;
   P.chunk = p.chunk;
+  P.state_all = p.state_all;
   P.bsel = p.tokens ? 1 : p.B;
   P.tlist = reinterpret_cast<int32_t*>(a.ws + L.off_tlist);
   P.part = reinterpret_cast<float*>(a.ws + L.off_part);

@@ -27,6 +27,7 @@ hsla_status resolve(const hsla_config* cfg, int32_t batch, int32_t max_seq_len,
     return HSLA_ERR_INVALID_ARG;
   if (cfg->deterministic < HSLA_SPLIT_DEFAULT || cfg->deterministic > HSLA_SPLIT_DYNAMIC) return HSLA_ERR_INVALID_ARG;
   if (!(cfg->scale >= 0.0f) || !isfinite(cfg->scale)) return HSLA_ERR_INVALID_ARG;
+  if (cfg->state_span != HSLA_STATE_BLOCKS && cfg->state_span != HSLA_STATE_TOKENS) return HSLA_ERR_INVALID_ARG;
   if (batch < 1 || max_seq_len < 1) return HSLA_ERR_INVALID_ARG;
   const int G = cfg->num_q_heads / cfg->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return HSLA_ERR_UNSUPPORTED;
@@ -52,6 +53,7 @@ hsla_status resolve(const hsla_config* cfg, int32_t batch, int32_t max_seq_len,
   p.tokens = cfg->selection == HSLA_SEL_TOKEN ? 1 : 0;
   p.qrows = 1;
   p.deterministic = cfg->deterministic;
+  p.state_all = cfg->state_span == HSLA_STATE_TOKENS ? 1 : 0;
   p.bf16 = cfg->kv_dtype == HSLA_BF16;
   p.sigma = cfg->scale > 0.0f ? cfg->scale : 1.0f / sqrtf(static_cast<float>(cfg->head_dim));
   p.batch = batch;
@@ -230,6 +232,7 @@ hsla_status hsla_append_token(const hsla_config* cfg, const hsla_kv_pool* pool, 
   Problem p;
   hsla_status st = resolve(cfg, batch, max_seq_len, pool ? pool->max_blocks_per_seq : 0, &p);
   if (st != HSLA_OK) return st;
+  if (p.state_all) return HSLA_ERR_UNSUPPORTED;   // the library updates a state of whole blocks only
   if ((st = check_pool(pool, true)) != HSLA_OK) return st;
   if ((st = check_state(state)) != HSLA_OK) return st;
   if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return HSLA_ERR_INVALID_ARG;
@@ -304,6 +307,7 @@ hsla_status decode_impl(const hsla_config* cfg, const hsla_kv_pool* pool, const 
   Problem p;
   hsla_status st = resolve(cfg, batch, max_seq_len, pool ? pool->max_blocks_per_seq : 0, &p);
   if (st != HSLA_OK) return st;
+  if (app && p.state_all) return HSLA_ERR_UNSUPPORTED;   // the fused append folds whole blocks
   if ((st = check_pool(pool, true)) != HSLA_OK) return st;
   if ((p.linear_tail || app) && (st = check_state(state)) != HSLA_OK) return st;
   if (!q || !aligned(q, 16) || !out || !aligned(out, 16)) return HSLA_ERR_INVALID_ARG;
@@ -417,7 +421,7 @@ hsla_status resolve_chunk(const hsla_config* cfg, int32_t batch, int32_t q_len, 
                           int32_t max_blocks, Problem* seq, Problem* rows, size_t* ws_rows, size_t* ws_total) {
   hsla_status st = resolve(cfg, batch, max_seq_len, max_blocks, seq);
   if (st != HSLA_OK) return st;
-  if (seq->tokens) return HSLA_ERR_UNSUPPORTED;
+  if (seq->tokens || seq->state_all) return HSLA_ERR_UNSUPPORTED;
   if (q_len < 1 || q_len > seq->B || q_len > seq->W - seq->B + 1 || q_len > max_seq_len) return HSLA_ERR_INVALID_ARG;
   if (static_cast<long>(batch) * q_len > (1L << 24)) return HSLA_ERR_INVALID_ARG;
   if ((st = resolve(cfg, batch * q_len, max_seq_len, max_blocks, rows)) != HSLA_OK) return st;

@@ -27,6 +27,7 @@ struct Problem {
   int qrows;       // query rows per sequence: 1, or the chunk length of the multi-query form
                    // (then batch counts query rows: sequences x qrows)
   int chunk;       // multi-query form: the state holds the whole blocks before the chunk
+  int state_all;   // HSLA_STATE_TOKENS: the state holds all T tokens (n = T)
   float sigma;
   int batch, max_seq_len;
   int max_blocks;  // block table row stride

@@ -141,10 +141,10 @@ class DeviceCache:
 
 def config_for(num_q_heads, num_kv_heads, head_dim, block_size, top_k, num_sink, window, linear_tail,
                kv_dtype: str, scale: float = 0.0, grouped: int = 0, deterministic: int = 0,
-               tokens: int = 0) -> Config:
+               tokens: int = 0, state_span: int = 0) -> Config:
     sel = HSLA_SEL_TOKEN if tokens else (HSLA_SEL_GROUPED if grouped else HSLA_SEL_PER_HEAD)
     return Config(num_q_heads, num_kv_heads, head_dim, block_size, top_k, num_sink, window, linear_tail,
-                  HSLA_BF16 if kv_dtype == "bf16" else HSLA_F32, scale, sel, int(deterministic))
+                  HSLA_BF16 if kv_dtype == "bf16" else HSLA_F32, scale, sel, int(deterministic), int(state_span))
 
 
 class PreparedDecodeStep:

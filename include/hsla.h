@@ -131,6 +131,21 @@ typedef enum hsla_selection {
 #define HSLA_SPLIT_DEFAULT 0
 #define HSLA_SPLIT_FIXED 1
 #define HSLA_SPLIT_DYNAMIC 2
+/* state_span: which tokens the global linear state (hsla_state) holds
+ *   [SPLA, "Residual Linear Attention (RLA)", "Recurrence"].
+ *   HSLA_STATE_BLOCKS (0): the tokens of complete blocks, n = T - T % B.
+ *     The library keeps it so: hsla_build_state builds it, and the appends
+ *     fold a block in when it completes.
+ *   HSLA_STATE_TOKENS (1): every token, n = T, as a state updated at every
+ *     token holds it.  hsla_build_state builds it over all T tokens and
+ *     hsla_decode subtracts every exact token from it; the caller updates
+ *     it per token.  hsla_append_token, hsla_append_decode(_noalloc) and
+ *     hsla_prefill_chunk update only a state of whole blocks and return
+ *     HSLA_ERR_UNSUPPORTED.  Both spans give the same residual, up to
+ *     rounding, since the tokens of the incomplete block are in the window.
+ *   Other values: HSLA_ERR_INVALID_ARG. */
+#define HSLA_STATE_BLOCKS 0
+#define HSLA_STATE_TOKENS 1
 typedef struct hsla_config {
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -144,6 +159,7 @@ typedef struct hsla_config {
   float scale;
   int32_t selection;
   int32_t deterministic;
+  int32_t state_span;
 } hsla_config;
 
 /* Paged KV cache [SPLA, "Page Attention and Selection"].
@@ -170,7 +186,8 @@ typedef struct hsla_kv_pool {
 /* Global linear state per (sequence, kv head) [SPLA, "Residual Linear
  * Attention (RLA)", "Recurrence"]: S [batch, Hkv, d, d], z and sv
  * [batch, Hkv, d], all float32, over the tokens of the sequence's complete
- * blocks; n = T - T % B follows from the length. */
+ * blocks (n = T - T % B follows from the length), or over all T tokens
+ * (n = T) with state_span = HSLA_STATE_TOKENS. */
 typedef struct hsla_state {
   float* S;
   float* z;

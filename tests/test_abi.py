@@ -66,6 +66,8 @@ BAD_CONFIGS = [
     (dict(scale=-1.0), H.HSLA_ERR_INVALID_ARG),
     (dict(deterministic=3), H.HSLA_ERR_INVALID_ARG),
     (dict(deterministic=-1), H.HSLA_ERR_INVALID_ARG),
+    (dict(state_span=2), H.HSLA_ERR_INVALID_ARG),
+    (dict(state_span=-1), H.HSLA_ERR_INVALID_ARG),
 ]
 
 FAKE = 1 << 20   # an aligned non-null address; never dereferenced because validation fails first
@@ -275,3 +277,18 @@ def test_phase_timestamps_only_in_the_diagnostic_build():
     assert ph.hsla_phase_timestamp_bytes() == 8 * (4096 * 16 + 16384 * 2 + 8192 * 2)
     assert ph.hsla_phase_timestamps(ctypes.addressof(buf), 32, 0) == H.HSLA_ERR_INVALID_ARG
     assert ph.hsla_phase_timestamps(None, 1 << 30, 0) == H.HSLA_ERR_INVALID_ARG
+
+
+def test_per_token_state_only_where_the_caller_updates_it():
+    """state_span = HSLA_STATE_TOKENS: build and decode accept it; every entry
+    point that updates the state itself (whole blocks) refuses it on the host."""
+    c = cfg(state_span=H.HSLA_STATE_TOKENS)
+    assert H.hsla_decode_workspace_size(c, 8, 32768) == H.hsla_decode_workspace_size(cfg(), 8, 32768) > 0
+    assert H.hsla_build_workspace_size(c, 8, 32768) > 0
+    lib = H.load()
+    U = H.HSLA_ERR_UNSUPPORTED
+    assert lib.hsla_append_token(ctypes.byref(c.c()), ctypes.byref(pool()), ctypes.byref(state()), FAKE, FAKE,
+                                 FAKE, FAKE + 256, 8, 32768, None) == U
+    assert call_append_decode(c) == U
+    assert call_prefill_chunk(c) == U
+    assert H.hsla_prefill_chunk_workspace_size(c, 8, 16, 32768) == 0
