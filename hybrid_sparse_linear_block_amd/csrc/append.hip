@@ -47,6 +47,7 @@ struct AppendParams {
   int Hkv, B, max_blocks, max_seq_len;
   int count;           // tokens per sequence: 1, or the chunk length
   int mode;            // kWriteRows | kFold
+  int state_all;       // a per-token state: every appended token enters S, z and sv at once
 };
 constexpr int kWriteRows = kAppendWriteRows;
 constexpr int kFold = kAppendFold;
@@ -84,6 +85,30 @@ __global__ __launch_bounds__(kThreads) void k_append(AppendParams P) {
     if ((P.mode & kFold) && g == 0 && tid == 0 && P.seq_lens_after) P.seq_lens_after[b] = T0 + Q;
   }
   if (!(P.mode & kFold)) return;
+  if (P.state_all && rc < D / kFoldRows) {
+    // A per-token state (one token per call: the chunk form refuses this
+    // state): row chunk rc adds k_r v^T to its rows of S, k_r to z, and
+    // chunk 0 adds v to sv.  No block is folded later.
+    const int col4 = tid % C4;
+    const int r_first = rc * kFoldRows + tid / C4;
+    float* Sp = P.S + static_cast<size_t>(pair) * D * D;
+    const float4 vv = kv_load4<KV>(P.v_new, new_row(0) + col4 * 4);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int r = r_first + i * RG;
+      const float kr = kv_elem<KV>(P.k_new, new_row(0) + r);
+      float4* sp = reinterpret_cast<float4*>(Sp + static_cast<size_t>(r) * D + col4 * 4);
+      float4 s = *sp;
+      s.x = fmaf(kr, vv.x, s.x);
+      s.y = fmaf(kr, vv.y, s.y);
+      s.z = fmaf(kr, vv.z, s.z);
+      s.w = fmaf(kr, vv.w, s.w);
+      *sp = s;
+    }
+    if (tid < kFoldRows) P.z[nbase + rc * kFoldRows + tid] += kv_elem<KV>(P.k_new, new_row(0) + rc * kFoldRows + tid);
+    if (rc == 0 && tid < D) P.sv[nbase + tid] += kv_elem<KV>(P.v_new, new_row(0) + tid);
+    return;
+  }
   const int ic = B - 1 - T0 % B;   // the new token that completes a block, if ic < Q
   if (ic >= Q) return;              // uniform: no block completes
   const int T = T0 + ic;
@@ -147,6 +172,7 @@ hipError_t launch_append(const Problem& p, const AppendArgs& a, hipStream_t s, i
   P.B = p.B;
   P.max_blocks = p.max_blocks;
   P.max_seq_len = p.max_seq_len;
+  P.state_all = p.state_all;
   if (p.bf16) return p.D == 64 ? launch_t<KvBf16, 64>(p, P, s) : launch_t<KvBf16, 128>(p, P, s);
   return p.D == 64 ? launch_t<KvF32, 64>(p, P, s) : launch_t<KvF32, 128>(p, P, s);
 }

@@ -232,7 +232,6 @@ hsla_status hsla_append_token(const hsla_config* cfg, const hsla_kv_pool* pool, 
   Problem p;
   hsla_status st = resolve(cfg, batch, max_seq_len, pool ? pool->max_blocks_per_seq : 0, &p);
   if (st != HSLA_OK) return st;
-  if (p.state_all) return HSLA_ERR_UNSUPPORTED;   // the library updates a state of whole blocks only
   if ((st = check_pool(pool, true)) != HSLA_OK) return st;
   if ((st = check_state(state)) != HSLA_OK) return st;
   if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return HSLA_ERR_INVALID_ARG;

@@ -82,3 +82,51 @@ def test_per_token_state_decodes_like_the_oracle(name):
     for b in range(wl.batch):
         for h in range(wl.num_q_heads):
             assert row_rel_err(outs[H.HSLA_STATE_TOKENS][b, h], outs[H.HSLA_STATE_BLOCKS][b, h]) <= 2 * tol
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_per_token_state_through_appends(dtype):
+    """Build at T - N, then N hsla_append_token calls crossing block
+    boundaries (each adds its token to S, z and sv), then a decode: the state
+    holds all T tokens, the completed blocks have their statistics, and every
+    head's selection and output match the oracle on the full sequence."""
+    N = 70
+    full = W.Workload("span_append", 64, batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=64,
+                      top_k=6, num_sink=4, window=256, linear_tail=1, kv_dtype=dtype, seq_lens=(1400, 1250),
+                      shuffle_pages=True, spare_pages=2, append_room=3)
+    start = tuple(t - N for t in full.seq_lens)
+    print(f"[case] {full.name} cid={full.cid} {dtype} T={list(full.seq_lens)} N={N}", flush=True)
+    sys.stdout.flush()
+    inp = W.make_inputs(full)
+    table = inp["block_table"]
+    kp, vp = W.empty_pool(full), W.empty_pool(full)
+    for (b, g), (K, V) in inp["pairs"].items():
+        W.scatter_pairs(full, table, kp, b, g, K[:start[b]])
+        W.scatter_pairs(full, table, vp, b, g, V[:start[b]])
+    dc = DeviceCache(_cfg(full, H.HSLA_STATE_TOKENS), kp, vp, table, np.asarray(start, np.int32),
+                     capacity_len=max(full.seq_lens))
+    dc.build()
+    for i in range(N):
+        kn = np.stack([np.stack([inp["pairs"][(b, g)][0][start[b] + i] for g in range(full.num_kv_heads)])
+                       for b in range(full.batch)])
+        vn = np.stack([np.stack([inp["pairs"][(b, g)][1][start[b] + i] for g in range(full.num_kv_heads)])
+                       for b in range(full.batch)])
+        dc.append(to_device(kn), to_device(vn))
+    out, sel = dc.decode(to_device(inp["q"]))
+    torch.cuda.synchronize()
+    assert dc.seq_lens.cpu().numpy().tolist() == list(full.seq_lens)
+    # statistics of every complete block and the state over all T tokens
+    check_case(full, inp, dc, out.cpu().numpy(), sel.cpu().numpy(), check_build=False)
+    mean_g, var_g = dc.blk_mean.cpu().numpy(), dc.blk_var.cpu().numpy()
+    S_g, z_g, sv_g = dc.S.cpu().numpy(), dc.z.cpu().numpy(), dc.sv.cpu().numpy()
+    from parity import assert_stats_close
+    for (b, g), (K, V) in inp["pairs"].items():
+        Kf, Vf = O.to_f64(K, dtype), O.to_f64(V, dtype)
+        T = Kf.shape[0]
+        nb = T // full.block_size
+        st = O.block_statistics(Kf, full.block_size)
+        pages = table[b, :nb]
+        assert_stats_close(mean_g[pages, g], var_g[pages, g], st[0], st[1], Kf, full.block_size, f"pair {(b, g)}")
+        gs = O.LinearState(S_g[b, g].astype(np.float64), z_g[b, g].astype(np.float64),
+                           sv_g[b, g].astype(np.float64), T)
+        assert_state_close(gs, O.global_state(Kf, Vf), Kf, Vf, _state_depth(T) + N, f"pair {(b, g)}")
