@@ -603,15 +603,36 @@ __device__ __forceinline__ void readout_finish(const DecodeParams& P, int b, int
     }
     if (g == 0 && tid == 0 && P.app.lens_after) P.app.lens_after[b] = T + 1;
   }
+  // a per-token state takes the new token now (never with the chunk form)
+  const bool tok = app && P.state_all;
   if (!lin) {
-    if (!completes) return;
+    if (!completes && !tok) return;
     const float* Sp = P.app.S + static_cast<size_t>(pair) * D * D;
 #pragma unroll
     for (int i = 0; i < NR; ++i)
       R.srow[i] = *reinterpret_cast<const float4*>(Sp + static_cast<size_t>(r0 + rg + i * RG) * D + col4 * 4);
     if (tid < kRoRows) R.zr = P.app.z[nbase + r0 + tid];
   }
-  if (completes) {
+  if (tok) {
+    // S += k v^T on the chunk's rows, z += k, and chunk 0 sv += v: the same
+    // arithmetic as the stand-alone append, before the readout reads them
+    const float4 vv = kv_load4<KV>(P.app.v_new, nbase + col4 * 4);
+    float* Sw = P.app.S + static_cast<size_t>(pair) * D * D;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const float kr = kv_elem<KV>(P.app.k_new, nbase + r0 + rg + i * RG);
+      R.srow[i].x = fmaf(kr, vv.x, R.srow[i].x);
+      R.srow[i].y = fmaf(kr, vv.y, R.srow[i].y);
+      R.srow[i].z = fmaf(kr, vv.z, R.srow[i].z);
+      R.srow[i].w = fmaf(kr, vv.w, R.srow[i].w);
+      *reinterpret_cast<float4*>(Sw + static_cast<size_t>(r0 + rg + i * RG) * D + col4 * 4) = R.srow[i];
+    }
+    if (tid < kRoRows) {
+      R.zr += kv_elem<KV>(P.app.k_new, nbase + r0 + tid);
+      P.app.z[nbase + r0 + tid] = R.zr;
+    }
+    if (rc == 0 && tid < D) P.app.sv[nbase + tid] += kv_elem<KV>(P.app.v_new, nbase + tid);
+  } else if (completes) {
     const CompletedBlock cb{P.app.k_pages, P.app.v_pages, P.app.k_new, P.app.v_new, row0, nbase, T % P.B, P.B};
     const int zrow = tid < kRoRows ? r0 + tid : -1;
     const int svcol = rc == 0 && tid < D ? tid : -1;

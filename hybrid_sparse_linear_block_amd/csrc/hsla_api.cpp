@@ -306,7 +306,6 @@ hsla_status decode_impl(const hsla_config* cfg, const hsla_kv_pool* pool, const 
   Problem p;
   hsla_status st = resolve(cfg, batch, max_seq_len, pool ? pool->max_blocks_per_seq : 0, &p);
   if (st != HSLA_OK) return st;
-  if (app && p.state_all) return HSLA_ERR_UNSUPPORTED;   // the fused append folds whole blocks
   if ((st = check_pool(pool, true)) != HSLA_OK) return st;
   if ((p.linear_tail || app) && (st = check_state(state)) != HSLA_OK) return st;
   if (!q || !aligned(q, 16) || !out || !aligned(out, 16)) return HSLA_ERR_INVALID_ARG;

@@ -138,13 +138,14 @@ typedef enum hsla_selection {
  *     fold a block in when it completes.
  *   HSLA_STATE_TOKENS (1): every token, n = T, as a state updated at every
  *     token holds it.  hsla_build_state builds it over all T tokens,
- *     hsla_append_token adds each appended token to it (S += k v^T, z += k,
- *     sv += v; a completed block still gets its statistics), and
- *     hsla_decode subtracts every exact token from it.  The fused forms
- *     (hsla_append_decode, its no-alloc variant, hsla_prefill_chunk) update
- *     only a state of whole blocks and return HSLA_ERR_UNSUPPORTED.  Both
- *     spans give the same residual, up to rounding, since the tokens of the
- *     incomplete block are in the window.
+ *     hsla_append_token and hsla_append_decode (and its no-alloc variant)
+ *     add each appended token to it (S += k v^T, z += k, sv += v; a
+ *     completed block still gets its statistics), and the decode subtracts
+ *     every exact token from it.  hsla_prefill_chunk, whose queries read
+ *     the state as it was before the chunk, folds whole blocks only and
+ *     returns HSLA_ERR_UNSUPPORTED.  Both spans give the same residual, up
+ *     to rounding, since the tokens of the incomplete block are in the
+ *     window.
  *   Other values: HSLA_ERR_INVALID_ARG. */
 #define HSLA_STATE_BLOCKS 0
 #define HSLA_STATE_TOKENS 1

@@ -280,14 +280,13 @@ def test_phase_timestamps_only_in_the_diagnostic_build():
 
 
 def test_per_token_state_only_where_the_caller_updates_it():
-    """state_span = HSLA_STATE_TOKENS: build, decode and the per-token append
-    accept it; the fused entry points, which update a state of whole blocks,
-    refuse it on the host."""
+    """state_span = HSLA_STATE_TOKENS: build, decode and the appends accept
+    it; the chunk form, which folds whole blocks after its queries, refuses
+    it on the host."""
     c = cfg(state_span=H.HSLA_STATE_TOKENS)
     assert H.hsla_decode_workspace_size(c, 8, 32768) == H.hsla_decode_workspace_size(cfg(), 8, 32768) > 0
     assert H.hsla_build_workspace_size(c, 8, 32768) > 0
     lib = H.load()
     U = H.HSLA_ERR_UNSUPPORTED
-    assert call_append_decode(c) == U
     assert call_prefill_chunk(c) == U
     assert H.hsla_prefill_chunk_workspace_size(c, 8, 16, 32768) == 0

@@ -20,6 +20,7 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():  # collected on CPU hosts, skipped there
     pytest.skip("needs a GPU", allow_module_level=True)
 
+import hybrid_sparse_linear_block_amd as H  # noqa: E402
 from hybrid_sparse_linear_block_amd.device import DeviceCache, to_device  # noqa: E402
 
 STEPS = 4
@@ -34,6 +35,11 @@ CASES = {
     "block16": dict(block_size=16, window=64, top_k=12, seq_lens=(1471, 1202)),
     "no_candidates": dict(seq_lens=(200, 37)),
     "token_level": dict(tokens=1, top_k=40, seq_lens=(1471, 1203)),
+    # a per-token state (state_span = HSLA_STATE_TOKENS): every append adds
+    # its token to S, z and sv
+    "per_token_state": dict(seq_lens=(1471, 1203)),
+    "per_token_state_f32_d64": dict(kv_dtype=W.F32, head_dim=64, seq_lens=(1471, 1203)),
+    "per_token_state_no_tail": dict(linear_tail=0, seq_lens=(1471, 1203)),
 }
 
 
@@ -53,7 +59,10 @@ def test_append_decode_equals_append_then_decode(name):
     _announce(wl, f"append + decode, {STEPS} steps")
     inp = W.make_inputs(wl, keep_pairs=False)
     cap = int(max(wl.seq_lens)) + STEPS + 1
-    caches = [DeviceCache(cfg_of(wl), inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"],
+    cfg = cfg_of(wl)
+    if name.startswith("per_token_state"):
+        cfg = dataclasses.replace(cfg, state_span=H.HSLA_STATE_TOKENS)
+    caches = [DeviceCache(cfg, inp["k_pages"], inp["v_pages"], inp["block_table"], inp["seq_lens"],
                           capacity_len=cap) for _ in range(2)]
     for dc in caches:
         dc.build()

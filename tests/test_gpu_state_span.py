@@ -84,18 +84,20 @@ def test_per_token_state_decodes_like_the_oracle(name):
             assert row_rel_err(outs[H.HSLA_STATE_TOKENS][b, h], outs[H.HSLA_STATE_BLOCKS][b, h]) <= 2 * tol
 
 
-@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
-def test_per_token_state_through_appends(dtype):
-    """Build at T - N, then N hsla_append_token calls crossing block
-    boundaries (each adds its token to S, z and sv), then a decode: the state
-    holds all T tokens, the completed blocks have their statistics, and every
-    head's selection and output match the oracle on the full sequence."""
+@pytest.mark.parametrize("dtype,fused", [(W.BF16, False), (W.F32, False), (W.BF16, True), (W.F32, True)])
+def test_per_token_state_through_appends(dtype, fused):
+    """Build at T - N, then N appends crossing block boundaries (each adds
+    its token to S, z and sv), then a decode: the state holds all T tokens,
+    the completed blocks have their statistics, and every head's selection
+    and output match the oracle on the full sequence.  `fused`: every append
+    is an hsla_append_decode call, and the last call's output is the decode
+    checked; else hsla_append_token, then hsla_decode."""
     N = 70
     full = W.Workload("span_append", 64, batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=64,
                       top_k=6, num_sink=4, window=256, linear_tail=1, kv_dtype=dtype, seq_lens=(1400, 1250),
                       shuffle_pages=True, spare_pages=2, append_room=3)
     start = tuple(t - N for t in full.seq_lens)
-    print(f"[case] {full.name} cid={full.cid} {dtype} T={list(full.seq_lens)} N={N}", flush=True)
+    print(f"[case] {full.name} cid={full.cid} {dtype} fused={fused} T={list(full.seq_lens)} N={N}", flush=True)
     sys.stdout.flush()
     inp = W.make_inputs(full)
     table = inp["block_table"]
@@ -106,13 +108,18 @@ def test_per_token_state_through_appends(dtype):
     dc = DeviceCache(_cfg(full, H.HSLA_STATE_TOKENS), kp, vp, table, np.asarray(start, np.int32),
                      capacity_len=max(full.seq_lens))
     dc.build()
+    q_dev = to_device(inp["q"])
     for i in range(N):
         kn = np.stack([np.stack([inp["pairs"][(b, g)][0][start[b] + i] for g in range(full.num_kv_heads)])
                        for b in range(full.batch)])
         vn = np.stack([np.stack([inp["pairs"][(b, g)][1][start[b] + i] for g in range(full.num_kv_heads)])
                        for b in range(full.batch)])
-        dc.append(to_device(kn), to_device(vn))
-    out, sel = dc.decode(to_device(inp["q"]))
+        if fused:
+            out, sel = dc.append_decode(to_device(kn), to_device(vn), q_dev)
+        else:
+            dc.append(to_device(kn), to_device(vn))
+    if not fused:
+        out, sel = dc.decode(q_dev)
     torch.cuda.synchronize()
     assert dc.seq_lens.cpu().numpy().tolist() == list(full.seq_lens)
     # statistics of every complete block and the state over all T tokens
